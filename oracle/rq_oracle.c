@@ -1,0 +1,404 @@
+/*
+ * rq_oracle.c -- plain, slow CPU oracle for the ResidualQuant KV-cache path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The product path
+ * (the HIP library and its Python binding) never calls it, and it shares no
+ * code, header, table or helper with the HIP sources.
+ *
+ * What it computes, with the passage each step follows.  "ResidualQuant page"
+ * is the summary page "ResidualQuant: KV Cache Quantization for Looped
+ * Transformers with 2-Bit Residuals" (thelatestinai.com, arXiv 2610.10381).
+ *
+ *   encode (FP32, bit-exact contract):
+ *     - the final loop's KV is the reference and every earlier loop is stored
+ *       as a low-precision residual against it            (Abstract; Fig. 1 step 2)
+ *     - least-square scaling: alpha = <x,y>/<y,y>, residual x - alpha*y
+ *                                                   (Abstract; Fig. 1 step 3; Fig. 2;
+ *                                                    Fig. 3 right: alpha = 1 means no LS)
+ *     - a rotation of the residual (here the normalized Sylvester Hadamard
+ *       matrix over head_dim)                          (Abstract; Fig. 1 step 4; Fig. 6)
+ *     - group-wise asymmetric INT2/INT4 quantization with per-group scale and
+ *       offset, group size g          (Fig. 1 caption: g=32; Table 8 caption: the
+ *                                      bit width counts codes, scales, offsets
+ *                                      and LS coefficients)
+ *     - loop-wise mixed precision: a bit width per loop        (Table 5; Fig. 1 step 5)
+ *   reconstruct (FP64):  x_hat = a*y + H_n (z + s*q)     (Abstract: the residual
+ *                                                          form keeps reconstruction
+ *                                                          cheap)
+ *   attention (FP64):    softmax(scale * q . x_hat^T) v_hat per loop, one query
+ *                        per loop                        (Abstract: decode over the
+ *                                                          compressed cache)
+ *
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function.  Where floating point decides an integer code, the FP32 steps are
+ * spelled out one IEEE operation at a time (build with -ffp-contract=off), so
+ * that a device implementation doing the same operations gets the same bytes.
+ *
+ * Plane layouts (token-major per (batch, head); all little-endian):
+ *   ref    bf16 [B][H][cap][d]
+ *   codes  u8   [B][H][cap][d*bits/8]   code i at bits [bits*(i % (8/bits)), +bits)
+ *                                        of byte i*bits/8
+ *   meta   f16  [B][H][cap][d/g][2]      (scale, zero) per group
+ *   alpha  f16  [B][H][cap]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define RQO_MAX_D 256
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 bits -> float: the 16 stored bits are the top half of an fp32. */
+float rqo_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* IEEE binary16 bits -> float, by the definition of the format. */
+float rqo_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1f;
+    int man = h & 0x3ff;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)man, -24);            /* subnormal: man * 2^-24 */
+    else if (exp == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man + 1024), exp - 25); /* (1 + man/1024) * 2^(exp-15) */
+    return (float)(sign ? -v : v);
+}
+
+/* float -> IEEE binary16, round to nearest, ties to even; overflow -> inf.
+ * Written as "snap to the grid of representable halves near |x|", which is
+ * the definition of round-to-nearest on that grid. */
+uint16_t rqo_f32_to_f16(float xf)
+{
+    if (isnan(xf))
+        return 0x7e00;
+    uint16_t sign = signbit(xf) ? 0x8000 : 0;
+    double a = fabs((double)xf);
+    /* Halfway between 65504 (largest finite half) and 65536 is 65520; RNE
+     * sends 65520 to the even neighbour 65536, which is out of range. */
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    double quantum;
+    if (a < ldexp(1.0, -14)) {
+        quantum = ldexp(1.0, -24);              /* subnormal spacing */
+    } else {
+        int e;
+        frexp(a, &e);                           /* a in [2^(e-1), 2^e) */
+        quantum = ldexp(1.0, e - 1 - 10);       /* 10 fraction bits */
+    }
+    double r = nearbyint(a / quantum) * quantum;  /* exact scaling, RNE */
+    if (r == 0.0)
+        return sign;
+    if (r < ldexp(1.0, -14))
+        return sign | (uint16_t)(r / ldexp(1.0, -24));
+    int e;
+    frexp(r, &e);
+    int exp_field = (e - 1) + 15;
+    int man = (int)(r / ldexp(1.0, e - 1 - 10)) - 1024;
+    return sign | (uint16_t)(exp_field << 10) | (uint16_t)man;
+}
+
+/* Storage conversion used by the encoder: RNE, but a result that would be
+ * infinite is stored as the largest finite half of that sign (reading: the pages
+ * store scales, offsets and LS coefficients in 16 bits and never mention
+ * overflow; saturating keeps every stored value finite). */
+uint16_t rqo_f32_to_f16_sat(float x)
+{
+    uint16_t h = rqo_f32_to_f16(x);
+    if (!isnan(x) && (h & 0x7fff) == 0x7c00)
+        return (h & 0x8000) | 0x7bff;
+    return h;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encoder steps (FP32 contract)                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Pairwise-halving sum of n (a power of two) floats: for m = n/2, n/4, ..., 1
+ * a[i] <- a[i] + a[i+m] for i < m.  Destroys a.  The reduction order is part
+ * of the bit-exact contract (the pages give no arithmetic detail). */
+float rqo_tree_sum(float *a, int n)
+{
+    for (int m = n / 2; m >= 1; m /= 2)
+        for (int i = 0; i < m; ++i)
+            a[i] = a[i] + a[i + m];
+    return a[0];
+}
+
+/* Least-square coefficient before storage rounding: the alpha that minimises
+ * ||x - alpha*y||^2 is <x,y>/<y,y> (ResidualQuant page, Fig. 2 shows the
+ * residual K2 - alpha2*K1; Fig. 3 right compares with alpha = 1).
+ * Reading: <y,y> == 0 gives alpha = 0 (nothing to predict from). */
+float rqo_alpha_f32(const uint16_t *x, const uint16_t *y, int d)
+{
+    float num[RQO_MAX_D], den[RQO_MAX_D];
+    for (int i = 0; i < d; ++i) {
+        float xf = rqo_bf16_to_f32(x[i]);
+        float yf = rqo_bf16_to_f32(y[i]);
+        num[i] = xf * yf;
+        den[i] = yf * yf;
+    }
+    float n = rqo_tree_sum(num, d);
+    float s = rqo_tree_sum(den, d);
+    return s > 0.0f ? n / s : 0.0f;
+}
+
+/* Stored coefficient: one FP16 value per (loop, batch, head, token), for K and
+ * V separately.  Reading of the pages' effective-bitwidth accounting, which
+ * counts LS coefficients and adds 0.1 bit per value for residual loops over
+ * direct ones (Table 5: 2.5 -> 2.6, 3.0 -> 3.1, 4.5 -> 4.6), i.e. 16 bits per
+ * head_dim-vector. */
+uint16_t rqo_alpha_bits(const uint16_t *x, const uint16_t *y, int d)
+{
+    return rqo_f32_to_f16_sat(rqo_alpha_f32(x, y, d));
+}
+
+/* Normalized Walsh-Hadamard rotation in place: butterflies for
+ * h = 1, 2, 4, ..., d/2 on pairs (i, i+h), (u_i, u_{i+h}) <- (u_i + u_{i+h},
+ * u_i - u_{i+h}), then one multiplication by c = fp32(1/sqrt(d)).
+ * The result is c * H_d * u with H_d the Sylvester-ordered Hadamard matrix.
+ * Reading: the pages name their rotation (shared OptR-H; OSCAR) without
+ * defining it; the plain orthogonal rotation is the normalized Hadamard
+ * matrix, shared by K and V, all loops and heads (Fig. 6 uses one
+ * shared rotation). */
+void rqo_fwht_f32(float *u, int d)
+{
+    for (int h = 1; h < d; h *= 2)
+        for (int j = 0; j < d; j += 2 * h)
+            for (int i = j; i < j + h; ++i) {
+                float a = u[i], b = u[i + h];
+                u[i] = a + b;
+                u[i + h] = a - b;
+            }
+    float c = (float)(1.0 / sqrt((double)d));
+    for (int i = 0; i < d; ++i)
+        u[i] = u[i] * c;
+}
+
+/* Quantize one group of g values to `bits`-bit codes with an asymmetric
+ * min/max grid: scale s = (max - min) / (2^bits - 1), offset z = min, both
+ * stored FP16; code = clamp(round_half_even((u - z) * (1/s)), 0, 2^bits - 1).
+ * Readings: the offset is a floating-point minimum (not an integer zero
+ * point); no clipping; the reciprocal of the stored scale is taken once per
+ * group; a zero stored scale (constant group) gives all-zero codes. */
+void rqo_quantize_group(const float *u, int g, int bits, uint8_t *codes,
+                        uint16_t *s16, uint16_t *z16)
+{
+    float mn = u[0], mx = u[0];
+    for (int i = 1; i < g; ++i) {
+        if (u[i] < mn) mn = u[i];
+        if (u[i] > mx) mx = u[i];
+    }
+    float levels = (float)((1 << bits) - 1);
+    *s16 = rqo_f32_to_f16_sat((mx - mn) / levels);
+    *z16 = rqo_f32_to_f16_sat(mn);
+    float s = rqo_f16_to_f32(*s16);
+    float z = rqo_f16_to_f32(*z16);
+    if (s == 0.0f) {
+        memset(codes, 0, (size_t)g);
+        return;
+    }
+    float inv = 1.0f / s;
+    for (int i = 0; i < g; ++i) {
+        float t = (u[i] - z) * inv;
+        t = nearbyintf(t);                      /* ties to even */
+        if (t < 0.0f) t = 0.0f;
+        if (t > levels) t = levels;
+        codes[i] = (uint8_t)t;
+    }
+}
+
+/* LSB-first packing of `bits`-bit codes into bytes. */
+void rqo_pack(const uint8_t *codes, int d, int bits, uint8_t *out)
+{
+    int per = 8 / bits;
+    memset(out, 0, (size_t)(d * bits / 8));
+    for (int i = 0; i < d; ++i)
+        out[i / per] |= (uint8_t)(codes[i] << (bits * (i % per)));
+}
+
+void rqo_unpack(const uint8_t *packed, int d, int bits, uint8_t *codes)
+{
+    int per = 8 / bits;
+    for (int i = 0; i < d; ++i)
+        codes[i] = (uint8_t)((packed[i / per] >> (bits * (i % per))) & ((1 << bits) - 1));
+}
+
+/* Encode one head_dim vector x of a residual loop against the reference y. */
+void rqo_encode_vector(const uint16_t *x, const uint16_t *y, int d, int g,
+                       int bits, int rotate, uint8_t *packed, uint16_t *meta,
+                       uint16_t *alpha)
+{
+    float u[RQO_MAX_D];
+    uint8_t codes[RQO_MAX_D];
+    *alpha = rqo_alpha_bits(x, y, d);
+    float a = rqo_f16_to_f32(*alpha);          /* the stored value is what decode sees */
+    for (int i = 0; i < d; ++i)
+        u[i] = fmaf(-a, rqo_bf16_to_f32(y[i]), rqo_bf16_to_f32(x[i]));
+    if (rotate)
+        rqo_fwht_f32(u, d);
+    for (int i = 0; i < d; ++i)
+        u[i] = u[i] + 0.0f;                     /* -0 -> +0 before min/max */
+    for (int k = 0; k < d / g; ++k)
+        rqo_quantize_group(u + k * g, g, bits, codes + k * g, meta + 2 * k, meta + 2 * k + 1);
+    rqo_pack(codes, d, bits, packed);
+}
+
+/* Encode tokens [t0, t0+n) of residual loops 0..L-2 of every (b, h).
+ *   ref:  bf16 [B][H][cap][d]     (the final loop, already in the cache)
+ *   xin:  bf16 [L-1][B][H][n][d]  (the earlier loops' new vectors)
+ *   codes[l], meta[l], alpha[l]:  planes of loop l (layouts at the top)  */
+void rqo_encode(int L, int B, int H, int d, int g, int cap, int rotate,
+                const int *bits, const uint16_t *ref, const uint16_t *xin,
+                int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha)
+{
+    int G = d / g;
+    for (int l = 0; l < L - 1; ++l) {
+        int nb = d * bits[l] / 8;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < H; ++h)
+                for (int t = 0; t < n; ++t) {
+                    size_t bh = (size_t)b * H + h;
+                    size_t slot = bh * cap + (size_t)(t0 + t);
+                    const uint16_t *x = xin + ((((size_t)l * B + b) * H + h) * n + t) * d;
+                    const uint16_t *y = ref + slot * d;
+                    rqo_encode_vector(x, y, d, g, bits[l], rotate,
+                                      codes[l] + slot * nb, meta[l] + slot * 2 * G,
+                                      alpha[l] + slot);
+                }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reconstruction and attention (FP64)                                       */
+/* ------------------------------------------------------------------------ */
+
+/* x_hat = a*y + H_d (z + s*q) / sqrt(d)  (or without the rotation). */
+void rqo_reconstruct_vector(const uint8_t *packed, const uint16_t *meta,
+                            uint16_t alpha, const uint16_t *y, int d, int g,
+                            int bits, int rotate, double *out)
+{
+    uint8_t codes[RQO_MAX_D];
+    double u[RQO_MAX_D];
+    rqo_unpack(packed, d, bits, codes);
+    for (int i = 0; i < d; ++i) {
+        int k = i / g;
+        double s = rqo_f16_to_f32(meta[2 * k]);
+        double z = rqo_f16_to_f32(meta[2 * k + 1]);
+        u[i] = z + s * (double)codes[i];
+    }
+    if (rotate) {
+        for (int h = 1; h < d; h *= 2)
+            for (int j = 0; j < d; j += 2 * h)
+                for (int i = j; i < j + h; ++i) {
+                    double a = u[i], b = u[i + h];
+                    u[i] = a + b;
+                    u[i + h] = a - b;
+                }
+        double c = 1.0 / sqrt((double)d);
+        for (int i = 0; i < d; ++i)
+            u[i] *= c;
+    }
+    double a = rqo_f16_to_f32(alpha);
+    for (int i = 0; i < d; ++i)
+        out[i] = a * (double)rqo_bf16_to_f32(y[i]) + u[i];
+}
+
+/* Reconstruct tokens [t0, t0+n) of residual loop `loop` for every (b, h):
+ * out is float64 [B][H][n][d]. */
+void rqo_reconstruct(int B, int H, int d, int g, int cap, int rotate, int bits,
+                     const uint16_t *ref, const uint8_t *codes,
+                     const uint16_t *meta, const uint16_t *alpha, int t0, int n,
+                     double *out)
+{
+    int G = d / g, nb = d * bits / 8;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = 0; t < n; ++t) {
+                size_t slot = ((size_t)b * H + h) * cap + (size_t)(t0 + t);
+                rqo_reconstruct_vector(codes + slot * nb, meta + slot * 2 * G,
+                                       alpha[slot], ref + slot * d, d, g, bits,
+                                       rotate, out + (((size_t)b * H + h) * n + t) * d);
+            }
+}
+
+/* Softmax attention of one query over n keys/values, in FP64:
+ * s_t = scale * <q, k_t>, p = softmax(s) (max-subtracted), out = sum_t p_t v_t. */
+void rqo_attention(const double *q, const double *k, const double *v, int n,
+                   int d, double scale, double *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i)
+            acc += q[i] * k[(size_t)t * d + i];
+        s[t] = scale * acc;
+        if (s[t] > m) m = s[t];
+    }
+    double den = 0.0;
+    for (int i = 0; i < d; ++i)
+        out[i] = 0.0;
+    for (int t = 0; t < n; ++t) {
+        double p = exp(s[t] - m);
+        den += p;
+        for (int i = 0; i < d; ++i)
+            out[i] += p * v[(size_t)t * d + i];
+    }
+    for (int i = 0; i < d; ++i)
+        out[i] /= den;
+    free(s);
+}
+
+/* One decode row: attention of loop `loop`'s query of (b, h) over tokens
+ * [0, n_ctx) of that loop's cache, reconstructed in FP64.  The final loop
+ * (loop == L-1) attends over the BF16 reference itself.
+ *   kref/vref: bf16 [B][H][cap][d]; kc/vc etc.: the loop's planes (ignored for
+ *   the final loop); q: bf16 [L][B][H][d]; out: float64 [d]. */
+void rqo_decode_row(int L, int B, int H, int d, int g, int cap, int rotate,
+                    int bits, const uint16_t *kref, const uint8_t *kc,
+                    const uint16_t *km, const uint16_t *ka,
+                    const uint16_t *vref, const uint8_t *vc,
+                    const uint16_t *vm, const uint16_t *va, const uint16_t *q,
+                    int loop, int b, int h, int n_ctx, double scale,
+                    double *out)
+{
+    size_t bh = (size_t)b * H + h;
+    double *kh = (double *)malloc(sizeof(double) * (size_t)n_ctx * d);
+    double *vh = (double *)malloc(sizeof(double) * (size_t)n_ctx * d);
+    double qd[RQO_MAX_D];
+    const uint16_t *qrow = q + (((size_t)loop * B + b) * H + h) * d;
+    for (int i = 0; i < d; ++i)
+        qd[i] = rqo_bf16_to_f32(qrow[i]);
+    int G = d / g, nb = d * bits / 8;
+    for (int t = 0; t < n_ctx; ++t) {
+        size_t slot = bh * cap + (size_t)t;
+        if (loop == L - 1) {
+            for (int i = 0; i < d; ++i) {
+                kh[(size_t)t * d + i] = rqo_bf16_to_f32(kref[slot * d + i]);
+                vh[(size_t)t * d + i] = rqo_bf16_to_f32(vref[slot * d + i]);
+            }
+        } else {
+            rqo_reconstruct_vector(kc + slot * nb, km + slot * 2 * G, ka[slot],
+                                   kref + slot * d, d, g, bits, rotate, kh + (size_t)t * d);
+            rqo_reconstruct_vector(vc + slot * nb, vm + slot * 2 * G, va[slot],
+                                   vref + slot * d, d, g, bits, rotate, vh + (size_t)t * d);
+        }
+    }
+    rqo_attention(qd, kh, vh, n_ctx, d, scale, out);
+    free(kh);
+    free(vh);
+}

@@ -1,0 +1,122 @@
+"""Seeded synthetic looped-model KV and queries.
+
+Shared by the tests, the benchmark and the CPU oracle's inputs; it holds none
+of the method's arithmetic, only random draws with the shapes and statistics
+of the workloads:
+
+* reference (final-loop) K and V: N(0, 1) scaled per channel by a standard
+  deviation drawn from LogNormal(0, 0.5) -- one draw per (layer, head,
+  channel), separately for K and V -- to mimic the post-RoPE outlier channels
+  the ResidualQuant page shows in its key-magnitude figures (Fig. 2, Fig. 5);
+* an earlier loop l: c_l * reference + N(0, sigma_l^2), so loops are similar to
+  the final loop, as the page observes (Abstract) and as its Table 1 trend
+  suggests (later loops closer to the last-loop reference);
+* queries: N(0, 1), one per loop.
+
+Everything is drawn in float32 from a seeded torch.Generator and rounded to
+bfloat16.  Tensors come back on `device`; the draw happens on the generator's
+device (CPU by default, so that the oracle and the GPU see the same values).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+
+@dataclass
+class Workload:
+    name: str
+    n_loops: int
+    batch: int
+    heads: int
+    d: int
+    g: int
+    n_ctx: int
+    bits: List[int]                 # per residual loop (length n_loops - 1)
+    c: List[float]                  # similarity coefficient per residual loop
+    sigma: List[float]              # residual noise std per residual loop
+    rotate: int = 1
+    layers: int = 1
+    steps: int = 0                  # append-decode steps after the prefill
+    seed: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+# The five workloads: a tiny CPU-checkable case, the 8k-context INT2 decode,
+# mixed precision with appends, 32k context over 24 layers, and the 8k
+# peak-batch sweep.
+WORKLOADS = {
+    "tiny": Workload("tiny", n_loops=2, batch=1, heads=1, d=64, g=32, n_ctx=128,
+                     bits=[2], c=[0.9], sigma=[0.1], rotate=0, seed=0),
+    "int2-8k": Workload("int2-8k", n_loops=4, batch=16, heads=16, d=128, g=32, n_ctx=8192,
+                        bits=[2, 2, 2], c=[0.8, 0.85, 0.9], sigma=[0.15, 0.12, 0.1],
+                        rotate=1, seed=1),
+    "mixed-8k-append": Workload("mixed-8k-append", n_loops=4, batch=64, heads=16, d=128, g=32,
+                                n_ctx=8192, bits=[4, 2, 2], c=[0.8, 0.85, 0.9],
+                                sigma=[0.15, 0.12, 0.1], rotate=1, steps=64, seed=2),
+    "int2-32k-24l": Workload("int2-32k-24l", n_loops=4, batch=8, heads=16, d=128, g=32,
+                             n_ctx=32768, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
+                             sigma=[0.15, 0.12, 0.1], rotate=1, layers=24, seed=3),
+    "peak-batch-8k": Workload("peak-batch-8k", n_loops=4, batch=0, heads=16, d=128, g=32,
+                              n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
+                              sigma=[0.15, 0.12, 0.1], rotate=1, layers=24, seed=4),
+}
+
+
+def generator(seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def channel_std(gen: torch.Generator, heads: int, d: int) -> torch.Tensor:
+    """Per (head, channel) standard deviation ~ LogNormal(0, 0.5)."""
+    dev = gen.device
+    return torch.exp(0.5 * torch.randn(heads, d, generator=gen, device=dev))
+
+
+def draw_kv(gen: torch.Generator, n_loops: int, batch: int, heads: int, n: int, d: int,
+            c: Sequence[float], sigma: Sequence[float], std: Optional[torch.Tensor] = None):
+    """One side (K or V) of one layer.
+
+    Returns (ref, loops): ref bf16 [B, H, n, d] is the final loop; loops bf16
+    [L-1, B, H, n, d] are the earlier loops, loop l = c[l]*ref + N(0, sigma[l]^2)
+    (computed in float32 before rounding)."""
+    dev = gen.device
+    if std is None:
+        std = channel_std(gen, heads, d)
+    ref = torch.randn(batch, heads, n, d, generator=gen, device=dev) * std[None, :, None, :]
+    loops = torch.empty(n_loops - 1, batch, heads, n, d, dtype=torch.bfloat16, device=dev)
+    for l in range(n_loops - 1):
+        noise = torch.randn(batch, heads, n, d, generator=gen, device=dev)
+        loops[l] = (c[l] * ref + sigma[l] * noise).to(torch.bfloat16)
+    return ref.to(torch.bfloat16), loops
+
+
+def draw_queries(gen: torch.Generator, n_loops: int, batch: int, heads: int, d: int):
+    """bf16 [L, B, H, d], N(0, 1)."""
+    return torch.randn(n_loops, batch, heads, d, generator=gen, device=gen.device).to(torch.bfloat16)
+
+
+def draw_layer(w: Workload, seed: Optional[int] = None, batch: Optional[int] = None,
+               n: Optional[int] = None, device: str = "cpu"):
+    """K side, V side and queries for one layer of workload `w`.
+
+    Returns dict(k_ref, k_loops, v_ref, v_loops, q) with tokens [0, n)."""
+    gen = generator(w.seed if seed is None else seed, device)
+    B = w.batch if batch is None else batch
+    n = w.n_ctx if n is None else n
+    k_std = channel_std(gen, w.heads, w.d)
+    v_std = channel_std(gen, w.heads, w.d)
+    k_ref, k_loops = draw_kv(gen, w.n_loops, B, w.heads, n, w.d, w.c, w.sigma, k_std)
+    v_ref, v_loops = draw_kv(gen, w.n_loops, B, w.heads, n, w.d, w.c, w.sigma, v_std)
+    q = draw_queries(gen, w.n_loops, B, w.heads, w.d)
+    return dict(k_ref=k_ref, k_loops=k_loops, v_ref=v_ref, v_loops=v_loops, q=q,
+                k_std=k_std, v_std=v_std)
+
+
+def bf16_bits(t: torch.Tensor):
+    """bf16 tensor -> numpy uint16 bit patterns (CPU)."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view("uint16")
