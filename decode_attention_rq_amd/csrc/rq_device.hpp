@@ -1,0 +1,130 @@
+// rq_device.hpp -- device helpers shared by the gfx950 kernels of librq.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+// Low / high bf16 of a packed pair, widened exactly to fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default
+// rounding mode), saturating an infinite result to +-65504.
+__device__ __forceinline__ uint32_t f32_to_f16_sat(float x) {
+  uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)x);
+  if ((h & 0x7fffu) == 0x7c00u) h = (h & 0x8000u) | 0x7bffu;
+  return h;
+}
+
+// ---------------------------------------------------------------------------
+// lane exchange
+// ---------------------------------------------------------------------------
+
+// Value of `x` in lane (lane ^ mask).  Masks < 32 stay inside 32-lane halves
+// and use ds_swizzle (bitmask mode, no LDS allocation); 32 uses ds_bpermute.
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(MASK > 0 && MASK < 64 && (MASK & (MASK - 1)) == 0, "power-of-two lane mask");
+  if constexpr (MASK < 32) {
+    // offset[15] = 0: and_mask = 0x1f, or_mask = 0, xor_mask = MASK
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                                  0x1f | (MASK << 10)));
+  } else {
+    int src = (int)(__lane_id() ^ MASK) << 2;
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
+  }
+}
+
+template <int MASK>
+__device__ __forceinline__ uint32_t xor_lane_u(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, xor_lane<MASK>(__builtin_bit_cast(float, x)));
+}
+
+// Sum over aligned groups of N lanes (N a power of two <= 64), every lane of
+// the group receiving the total (xor butterfly).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += xor_lane<1>(x);
+  if constexpr (N >= 4) x += xor_lane<2>(x);
+  if constexpr (N >= 8) x += xor_lane<4>(x);
+  if constexpr (N >= 16) x += xor_lane<8>(x);
+  if constexpr (N >= 32) x += xor_lane<16>(x);
+  if constexpr (N >= 64) x += xor_lane<32>(x);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, xor_lane<1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, xor_lane<2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, xor_lane<4>(x));
+  if constexpr (N >= 16) x = fmaxf(x, xor_lane<8>(x));
+  if constexpr (N >= 32) x = fmaxf(x, xor_lane<16>(x));
+  if constexpr (N >= 64) x = fmaxf(x, xor_lane<32>(x));
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_min(float x) {
+  if constexpr (N >= 2) x = fminf(x, xor_lane<1>(x));
+  if constexpr (N >= 4) x = fminf(x, xor_lane<2>(x));
+  if constexpr (N >= 8) x = fminf(x, xor_lane<4>(x));
+  if constexpr (N >= 16) x = fminf(x, xor_lane<8>(x));
+  if constexpr (N >= 32) x = fminf(x, xor_lane<16>(x));
+  if constexpr (N >= 64) x = fminf(x, xor_lane<32>(x));
+  return x;
+}
+
+// One cross-lane butterfly stage of the Walsh-Hadamard transform: element i
+// of this lane pairs with element i of lane (lane ^ MASK).  The lane with the
+// MASK bit clear holds the lower index a and keeps a + b; its partner keeps
+// a - b.  Same two IEEE operations, same operand order, as the sequential
+// definition.
+template <int MASK>
+__device__ __forceinline__ float wht_stage(float own, int lane) {
+  float other = xor_lane<MASK>(own);
+  return (lane & MASK) ? (other - own) : (own + other);
+}
+
+// In-register Walsh-Hadamard transform (unnormalized) of a D-vector spread
+// over D/8 consecutive lanes, 8 consecutive elements per lane (element
+// 8*(lane % (D/8)) + p in v[p]).  Stages run h = 1, 2, 4 inside the lane,
+// then h = 8, 16, ... across lanes.
+template <int D>
+__device__ __forceinline__ void wht8(float (&v)[8], int lane) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 2 * h) {
+#pragma unroll
+      for (int i = j; i < j + h; ++i) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  constexpr int LANES = D / 8;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if constexpr (LANES >= 2) v[p] = wht_stage<1>(v[p], lane);
+    if constexpr (LANES >= 4) v[p] = wht_stage<2>(v[p], lane);
+    if constexpr (LANES >= 8) v[p] = wht_stage<4>(v[p], lane);
+    if constexpr (LANES >= 16) v[p] = wht_stage<8>(v[p], lane);
+    if constexpr (LANES >= 32) v[p] = wht_stage<16>(v[p], lane);
+  }
+}
+
+}  // namespace rq

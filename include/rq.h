@@ -1,0 +1,165 @@
+/*
+ * rq.h -- C ABI of librq.so: ResidualQuant KV-cache encoder, reconstruction
+ * and fused decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (ResidualQuant page, "ResidualQuant: KV Cache Quantization for
+ * Looped Transformers with 2-Bit Residuals", Abstract and Fig. 1): a looped
+ * Transformer keeps one KV cache per loop.  The final loop's K and V are the
+ * reference, kept here in BF16; each earlier loop l is stored as a residual
+ * against it -- scaled by a least-squares coefficient (Fig. 1 step 3, Fig. 2),
+ * rotated (Fig. 1 step 4), and quantized per group of g values to INT2 or
+ * INT4 with a per-group scale and offset (Fig. 1, Table 5), with a bit width
+ * chosen per loop (loop-wise mixed precision, Table 5).  Decode attends, for
+ * every loop, over that loop's cache reconstructed from the reference and its
+ * residual (Abstract: the smaller cache is read with less memory traffic).
+ *
+ * Conventions for every entry point:
+ *   - Loops are numbered 0 .. n_loops-1; loop n_loops-1 is the BF16 reference.
+ *   - All data pointers are DEVICE pointers on the current HIP device, except
+ *     the rq_layout / rq_cache structs themselves, which are host memory and
+ *     are only read during the call.
+ *   - The library allocates nothing and frees nothing; the caller owns every
+ *     buffer.  It keeps no state between calls except a per-device cache of
+ *     the compute-unit count, and is safe to call from several host threads.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting for it.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and no output is touched.
+ *   - Every plane must be 16-byte aligned.  Planes are contiguous and
+ *     token-major within one (batch, head): with cap = layout.capacity,
+ *       ref    bf16 [batch][heads][cap][head_dim]
+ *       codes  u8   [batch][heads][cap][head_dim*bits/8]  code i of a vector at
+ *              bits [bits*(i % (8/bits)), +bits) of byte i*bits/8
+ *       meta   f16  [batch][heads][cap][head_dim/group][2]   (scale, zero)
+ *       alpha  f16  [batch][heads][cap]
+ *   - Non-finite inputs are not supported (results unspecified, no fault).
+ */
+#ifndef RQ_H_
+#define RQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RQ_OK = 0,
+    RQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad range, empty mask */
+    RQ_ERR_UNSUPPORTED = -2,  /* head_dim, group, bits or loop count outside the supported set */
+    RQ_ERR_WORKSPACE = -3,    /* decode workspace smaller than rq_decode_workspace_bytes */
+    RQ_ERR_DEVICE = -4        /* a HIP call or kernel launch reported an error */
+} rq_status;
+
+/* 32 loops covers the pages' longest schedules (Table 8: 32-loop Huginn as
+ * 2 x [2^15, 4]) and lets one uint32_t mask name every loop. */
+#define RQ_MAX_LOOPS 32
+
+/* Shape of one layer's cache.  Host struct, read-only. */
+typedef struct {
+    int32_t n_loops;             /* L >= 2; loop L-1 is the BF16 reference            */
+    int32_t batch;               /* B >= 1                                            */
+    int32_t n_heads;             /* H >= 1 (KV heads; one query per KV head per loop) */
+    int32_t head_dim;            /* d in {64, 128, 256}                               */
+    int32_t group;               /* g in {16, 32}; d % g == 0                         */
+    int32_t capacity;            /* token slots per (batch, head) in every plane, >= 1 */
+    int32_t rotate;              /* 1: normalized Hadamard rotation of residuals; 0: none */
+    int32_t bits[RQ_MAX_LOOPS];  /* bits[l] in {2, 4} for l < L-1 (entry L-1 unused)  */
+} rq_layout;
+
+/* One side (K or V) of one layer's cache: caller-owned device planes.
+ * Entries l >= L-1 of the arrays are ignored. */
+typedef struct {
+    void *ref;                   /* bf16 [B][H][cap][d], written by the caller      */
+    void *codes[RQ_MAX_LOOPS];   /* u8   [B][H][cap][d*bits[l]/8]                  */
+    void *meta[RQ_MAX_LOOPS];    /* f16  [B][H][cap][d/g][2]                       */
+    void *alpha[RQ_MAX_LOOPS];   /* f16  [B][H][cap]                               */
+} rq_cache;
+
+/*
+ * rq_encode -- write the residual codes of loops 0..L-2 for tokens [t0, t0+n).
+ *
+ * Follows the ResidualQuant page: residual against the final loop (Fig. 1
+ * step 2), least-squares scale (step 3; Fig. 2), rotation (step 4), group
+ * quantization with a per-loop bit width (steps 1 and 5; Table 5).  For each
+ * (loop l < L-1, batch b, head h, token t) and separately for K and V, with
+ * x the loop-l vector and y = ref[b][h][t] (both BF16, widened exactly):
+ *   alpha = fp16(<x,y> / <y,y>)   (0 if <y,y> = 0; dot products are FP32
+ *                                   pairwise-halving sums; FP16 stores are
+ *                                   round-to-nearest-even, saturating)
+ *   r     = fma(-alpha, y, x)                                     (FP32)
+ *   u     = fp32(1/sqrt(d)) * H_d r     if rotate (H_d Sylvester Hadamard,
+ *                                        butterflies h = 1, 2, ..., d/2)
+ *   per group k of g consecutive dims:  s = fp16((max - min) / (2^b - 1)),
+ *     z = fp16(min),  code = clamp(rne((u - z) * (1/s)), 0, 2^b - 1)
+ *     (all codes 0 if s = 0)
+ * The result is bit-identical to that FP32 definition.
+ *
+ *   k, v    caches; their ref planes must already hold tokens [t0, t0+n)
+ *   k_in    bf16 [L-1][B][H][n][d] contiguous: the new K vectors of loops 0..L-2
+ *   v_in    same for V
+ *   t0, n   0 <= t0, 0 <= n, t0 + n <= capacity (n = 0 is a no-op)
+ * Writes codes/meta/alpha of loops 0..L-2 at slots [t0, t0+n); nothing else.
+ */
+rq_status rq_encode(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
+                    const void *k_in, const void *v_in, int32_t t0, int32_t n,
+                    void *hip_stream);
+
+/*
+ * rq_decode_workspace_bytes -- bytes of scratch rq_decode_attn needs for
+ * `n_ctx` tokens and `n_splits` token splits (0 = the split count the library
+ * would choose, see rq_decode_splits).  Returns 0 for an invalid layout.
+ */
+size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_ctx, int32_t n_splits);
+
+/* rq_decode_splits -- the token-split count rq_decode_attn uses when asked
+ * for 0 splits (a function of the layout, n_ctx and the device); < 0 on an
+ * invalid layout or device error. */
+int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
+
+/*
+ * rq_decode_attn -- one decode step of one layer: for every loop l in
+ * loop_mask and every (b, h),
+ *   out[l][b][h] = softmax(sm_scale * q[l][b][h] . K_l^T) V_l
+ * over tokens [0, n_ctx), where K_l, V_l are loop l's keys and values
+ * reconstructed as alpha*y + H_n (z + s*code) (the reference itself for loop
+ * L-1).  ResidualQuant page, Abstract: decode attention over every loop's
+ * compressed cache.  The rotation is applied to the query and to the
+ * accumulated output instead of to every key and value (H_n is symmetric and
+ * orthonormal), and the reference is read once for all loops in the mask.
+ *
+ *   q          bf16 [L][B][H][d]: one query per loop (rows not in the mask unread)
+ *   loop_mask  bit l set = compute loop l; non-zero, no bit >= L
+ *   n_ctx      1 <= n_ctx <= capacity
+ *   sm_scale   finite softmax scale (1/sqrt(d) for standard attention)
+ *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise
+ *   out        f32 [L][B][H][d]; rows of loops not in the mask are not written
+ *   workspace  device scratch of at least rq_decode_workspace_bytes(layout,
+ *              n_ctx, n_splits) bytes, 16-byte aligned; contents need no
+ *              initialisation and are garbage afterwards
+ * Results agree with an FP64 evaluation of the same definition to within a
+ * few 1e-4 of the row's largest output magnitude.
+ */
+rq_status rq_decode_attn(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
+                         const void *q, uint32_t loop_mask, int32_t n_ctx, float sm_scale,
+                         int32_t n_splits, float *out, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
+/*
+ * rq_reconstruct -- dequantize loop `loop` (< L-1) for tokens [t0, t0+n):
+ *   out[b][h][t - t0] = alpha*y + H_n (z + s*code)          (FP32)
+ * ResidualQuant page, Abstract (the residual form keeps reconstruction
+ * cheap).  out is f32 [B][H][n][d]; 0 <= t0, 1 <= n, t0 + n <= capacity.
+ */
+rq_status rq_reconstruct(const rq_layout *layout, const rq_cache *c, int32_t loop,
+                         int32_t t0, int32_t n, float *out, void *hip_stream);
+
+/* Static description of a status code; never NULL. */
+const char *rq_status_string(rq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H_ */

@@ -128,14 +128,25 @@ uint16_t rqo_f32_to_f16_sat(float x)
 /* ------------------------------------------------------------------------ */
 
 /* Pairwise-halving sum of n (a power of two) floats: for m = n/2, n/4, ..., 1
- * a[i] <- a[i] + a[i+m] for i < m.  Destroys a.  The reduction order is part
- * of the bit-exact contract (the pages give no arithmetic detail). */
+ * a[i] <- a[i] + a[i+m] for i < m.  Destroys a. */
 float rqo_tree_sum(float *a, int n)
 {
     for (int m = n / 2; m >= 1; m /= 2)
         for (int i = 0; i < m; ++i)
             a[i] = a[i] + a[i + m];
     return a[0];
+}
+
+/* Sum of the d (a power of two, >= 8) terms of a dot product, in the order
+ * the bit-exact contract fixes (the pages give no arithmetic detail): each
+ * block of 8 consecutive terms is summed by pairwise halving (distances 4, 2,
+ * 1), then the d/8 block sums are summed by pairwise halving.  Destroys a. */
+float rqo_dot_sum(float *a, int d)
+{
+    float blocks[RQO_MAX_D / 8];
+    for (int c = 0; c < d / 8; ++c)
+        blocks[c] = rqo_tree_sum(a + 8 * c, 8);
+    return rqo_tree_sum(blocks, d / 8);
 }
 
 /* Least-square coefficient before storage rounding: the alpha that minimises
@@ -151,8 +162,8 @@ float rqo_alpha_f32(const uint16_t *x, const uint16_t *y, int d)
         num[i] = xf * yf;
         den[i] = yf * yf;
     }
-    float n = rqo_tree_sum(num, d);
-    float s = rqo_tree_sum(den, d);
+    float n = rqo_dot_sum(num, d);
+    float s = rqo_dot_sum(den, d);
     return s > 0.0f ? n / s : 0.0f;
 }
 

@@ -44,6 +44,8 @@ def lib():
         L.rqo_f32_to_f16_sat.argtypes = [C.c_float]
         L.rqo_tree_sum.restype = C.c_float
         L.rqo_tree_sum.argtypes = [_f32p, C.c_int]
+        L.rqo_dot_sum.restype = C.c_float
+        L.rqo_dot_sum.argtypes = [_f32p, C.c_int]
         L.rqo_alpha_f32.restype = C.c_float
         L.rqo_alpha_f32.argtypes = [_u16p, _u16p, C.c_int]
         L.rqo_alpha_bits.restype = C.c_uint16
@@ -110,6 +112,11 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 def tree_sum(a: np.ndarray) -> float:
     a = np.array(a, dtype=np.float32)
     return float(lib().rqo_tree_sum(a, a.size))
+
+
+def dot_sum(a: np.ndarray) -> float:
+    a = np.array(a, dtype=np.float32)
+    return float(lib().rqo_dot_sum(a, a.size))
 
 
 def alpha_f32(x_bits: np.ndarray, y_bits: np.ndarray) -> float:

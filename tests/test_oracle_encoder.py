@@ -95,15 +95,29 @@ def test_tree_sum_order_worked_example(oracle):
     assert seq == 1.0
 
 
+def test_dot_sum_order_worked_example(oracle):
+    """The dot-product order (blocks of 8 by halving, then over blocks), worked
+    by hand on 16 terms with a = 2^24 at 0, 1 at 1 and 4, -2^24 at 8:
+    block 0: (2^24 + 1, 1, 0, 0) -> (2^24, 1) -> 2^24 (each 2^24 + 1 rounds to
+    the even 2^24); block 1: -2^24; total 0.  Plain halving over all 16 terms
+    pairs 2^24 with -2^24 first and gives the exact 2."""
+    a = np.zeros(16, dtype=np.float32)
+    a[0], a[1], a[4], a[8] = 2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)
+    assert oracle.dot_sum(a) == 0.0
+    assert oracle.tree_sum(a) == 2.0
+
+
 def test_tree_sum_exact_and_bounded(oracle):
     rng = np.random.default_rng(3)
     ints = rng.integers(-1000, 1000, size=256).astype(np.float32)
     assert oracle.tree_sum(ints) == float(ints.sum(dtype=np.float64))
+    assert oracle.dot_sum(ints) == float(ints.sum(dtype=np.float64))
     for d in (64, 128, 256):
         a = (rng.standard_normal(d) * 10).astype(np.float32)
-        err = abs(oracle.tree_sum(a) - float(np.sum(a.astype(np.float64))))
         gamma = np.log2(d) * 2.0 ** -24 / (1 - np.log2(d) * 2.0 ** -24)
-        assert err <= gamma * float(np.abs(a).sum())
+        for f in (oracle.tree_sum, oracle.dot_sum):
+            err = abs(f(a) - float(np.sum(a.astype(np.float64))))
+            assert err <= gamma * float(np.abs(a).sum())
 
 
 # --------------------------------------------------------------------------
