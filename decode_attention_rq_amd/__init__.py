@@ -1,0 +1,180 @@
+"""Python binding of librq.so: ResidualQuant KV cache on MI355X (gfx950).
+
+Argument marshalling only: every step of encode, reconstruction and decode
+runs in the library's HIP kernels (see include/rq.h).  torch supplies device
+memory and the stream.  Importing this module fails if librq.so has not been
+built (python decode_attention_rq_amd/build.py, or __graft_entry__.build()).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librq.so")
+RQ_MAX_LOOPS = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python decode_attention_rq_amd/build.py`")
+
+_lib = C.CDLL(LIB_PATH)
+
+
+class rq_layout(C.Structure):
+    _fields_ = [("n_loops", C.c_int32), ("batch", C.c_int32), ("n_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("group", C.c_int32), ("capacity", C.c_int32),
+                ("rotate", C.c_int32), ("bits", C.c_int32 * RQ_MAX_LOOPS)]
+
+
+class rq_cache(C.Structure):
+    _fields_ = [("ref", C.c_void_p), ("codes", C.c_void_p * RQ_MAX_LOOPS),
+                ("meta", C.c_void_p * RQ_MAX_LOOPS), ("alpha", C.c_void_p * RQ_MAX_LOOPS)]
+
+
+_P = C.POINTER
+_lib.rq_status_string.restype = C.c_char_p
+_lib.rq_status_string.argtypes = [C.c_int]
+_lib.rq_encode.restype = C.c_int
+_lib.rq_encode.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), C.c_void_p, C.c_void_p,
+                           C.c_int32, C.c_int32, C.c_void_p]
+_lib.rq_decode_workspace_bytes.restype = C.c_size_t
+_lib.rq_decode_workspace_bytes.argtypes = [_P(rq_layout), C.c_int32, C.c_int32]
+_lib.rq_decode_splits.restype = C.c_int32
+_lib.rq_decode_splits.argtypes = [_P(rq_layout), C.c_int32]
+_lib.rq_decode_attn.restype = C.c_int
+_lib.rq_decode_attn.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), C.c_void_p, C.c_uint32,
+                                C.c_int32, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
+                                C.c_size_t, C.c_void_p]
+_lib.rq_reconstruct.restype = C.c_int
+_lib.rq_reconstruct.argtypes = [_P(rq_layout), _P(rq_cache), C.c_int32, C.c_int32, C.c_int32,
+                                C.c_void_p, C.c_void_p]
+
+STATUS = {0: "RQ_OK", -1: "RQ_ERR_INVALID_ARG", -2: "RQ_ERR_UNSUPPORTED", -3: "RQ_ERR_WORKSPACE",
+          -4: "RQ_ERR_DEVICE"}
+
+
+class RQError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(rq_status_string(status))
+
+
+def rq_status_string(status: int) -> str:
+    return _lib.rq_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RQError(status)
+
+
+@dataclass
+class Layout:
+    """Shape of one layer's cache (mirrors rq_layout)."""
+    n_loops: int
+    batch: int
+    n_heads: int
+    head_dim: int
+    group: int
+    capacity: int
+    rotate: int = 1
+    bits: Sequence[int] = field(default_factory=list)   # per residual loop
+
+    def c(self) -> rq_layout:
+        s = rq_layout(self.n_loops, self.batch, self.n_heads, self.head_dim, self.group,
+                      self.capacity, self.rotate)
+        for i, b in enumerate(list(self.bits)[:RQ_MAX_LOOPS]):
+            s.bits[i] = int(b)
+        return s
+
+
+class Cache:
+    """One side (K or V) of a layer's cache: torch tensors in the plane layout
+    of include/rq.h (the library reads and writes them in place)."""
+
+    def __init__(self, layout: Layout, device="cuda", ref: Optional[torch.Tensor] = None):
+        L, B, H, d, g, cap = (layout.n_loops, layout.batch, layout.n_heads, layout.head_dim,
+                              layout.group, layout.capacity)
+        self.layout = layout
+        self.ref = ref if ref is not None else torch.zeros(B, H, cap, d, dtype=torch.bfloat16, device=device)
+        self.codes: List[torch.Tensor] = [
+            torch.zeros(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device)
+            for l in range(L - 1)]
+        self.meta: List[torch.Tensor] = [
+            torch.zeros(B, H, cap, d // g, 2, dtype=torch.float16, device=device) for _ in range(L - 1)]
+        self.alpha: List[torch.Tensor] = [
+            torch.zeros(B, H, cap, dtype=torch.float16, device=device) for _ in range(L - 1)]
+
+    def c(self) -> rq_cache:
+        s = rq_cache()
+        s.ref = self.ref.data_ptr()
+        for l in range(len(self.codes)):
+            s.codes[l] = self.codes[l].data_ptr()
+            s.meta[l] = self.meta[l].data_ptr()
+            s.alpha[l] = self.alpha[l].data_ptr()
+        return s
+
+    def nbytes(self) -> int:
+        t = [self.ref] + self.codes + self.meta + self.alpha
+        return sum(x.numel() * x.element_size() for x in t)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def rq_encode(layout: Layout, k: Cache, v: Cache, k_in: torch.Tensor, v_in: torch.Tensor,
+              t0: int, n: int, stream=None) -> None:
+    """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous."""
+    lay, kc, vc = layout.c(), k.c(), v.c()
+    _check(_lib.rq_encode(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(k_in), _ptr(v_in),
+                          int(t0), int(n), _stream(stream)))
+
+
+def rq_decode_workspace_bytes(layout: Layout, n_ctx: int, n_splits: int = 0) -> int:
+    lay = layout.c()
+    return int(_lib.rq_decode_workspace_bytes(C.byref(lay), int(n_ctx), int(n_splits)))
+
+
+def rq_decode_splits(layout: Layout, n_ctx: int) -> int:
+    lay = layout.c()
+    s = int(_lib.rq_decode_splits(C.byref(lay), int(n_ctx)))
+    if s < 0:
+        raise RQError(s)
+    return s
+
+
+def rq_decode_attn(layout: Layout, k: Cache, v: Cache, q: torch.Tensor, loop_mask: int, n_ctx: int,
+                   sm_scale: float, out: torch.Tensor, workspace: torch.Tensor, n_splits: int = 0,
+                   stream=None) -> None:
+    """q: bf16 [L, B, H, d]; out: f32 [L, B, H, d]; workspace: device bytes."""
+    lay, kc, vc = layout.c(), k.c(), v.c()
+    _check(_lib.rq_decode_attn(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(q), int(loop_mask),
+                               int(n_ctx), float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def rq_reconstruct(layout: Layout, c: Cache, loop: int, t0: int, n: int, out: torch.Tensor,
+                   stream=None) -> None:
+    """out: f32 [B, H, n, d]."""
+    lay, cc = layout.c(), c.c()
+    _check(_lib.rq_reconstruct(C.byref(lay), C.byref(cc), int(loop), int(t0), int(n), _ptr(out),
+                               _stream(stream)))
+
+
+def workspace_for(layout: Layout, n_ctx: int, n_splits: int = 0, device="cuda") -> torch.Tensor:
+    """A zero-filled decode workspace (the library keeps it reusable)."""
+    nbytes = rq_decode_workspace_bytes(layout, n_ctx, n_splits)
+    if nbytes == 0:
+        raise RQError(-1)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)

@@ -1,0 +1,271 @@
+// rq_api.cpp -- the extern "C" entry points of librq.so: validate on the
+// host, fill the kernel argument blocks, enqueue on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "rq.h"
+#include "rq_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Layout checks shared by every entry point.
+rq_status check_layout(const rq_layout *L) {
+  if (L == nullptr) return RQ_ERR_INVALID_ARG;
+  if (L->n_loops < 2 || L->n_loops > RQ_MAX_LOOPS) return RQ_ERR_UNSUPPORTED;
+  if (L->batch < 1 || L->n_heads < 1 || L->capacity < 1) return RQ_ERR_INVALID_ARG;
+  if ((int64_t)L->batch * L->n_heads > 65535) return RQ_ERR_UNSUPPORTED;   // grid y limit
+  if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return RQ_ERR_UNSUPPORTED;
+  if (L->group != 16 && L->group != 32) return RQ_ERR_UNSUPPORTED;
+  if (L->head_dim % L->group != 0) return RQ_ERR_UNSUPPORTED;
+  if (L->rotate != 0 && L->rotate != 1) return RQ_ERR_INVALID_ARG;
+  for (int l = 0; l < L->n_loops - 1; ++l)
+    if (L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
+  // token indices are int32 inside the kernels
+  if ((int64_t)L->batch * L->n_heads * L->capacity > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  return RQ_OK;
+}
+
+rq_status check_cache(const rq_layout *L, const rq_cache *c) {
+  if (c == nullptr || !aligned16(c->ref)) return RQ_ERR_INVALID_ARG;
+  for (int l = 0; l < L->n_loops - 1; ++l)
+    if (!aligned16(c->codes[l]) || !aligned16(c->meta[l]) || !aligned16(c->alpha[l]))
+      return RQ_ERR_INVALID_ARG;
+  return RQ_OK;
+}
+
+float rot_const(int d) { return (float)(1.0 / std::sqrt((double)d)); }
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Token splits for a decode step: enough workgroups to give every compute
+// unit several, but never fewer than 256 tokens per split.
+int auto_splits(const rq_layout *L, int n_ctx, int cus) {
+  const int64_t bh = (int64_t)L->batch * L->n_heads;
+  const int64_t target = (int64_t)cus * 4;
+  int64_t s = (target + bh - 1) / bh;
+  const int64_t max_by_len = n_ctx / 256 > 0 ? n_ctx / 256 : 1;
+  if (s > max_by_len) s = max_by_len;
+  if (s > 256) s = 256;
+  if (s < 1) s = 1;
+  if (const char *env = std::getenv("RQ_DECODE_SPLITS")) {
+    const int v = std::atoi(env);
+    if (v >= 1) s = v < n_ctx ? v : n_ctx;
+  }
+  return (int)s;
+}
+
+// Workspace: [BH] uint32 counters (padded to 256 bytes), then the split
+// records f32 [S][kMaxSlots][BH][2D+2].
+size_t counter_bytes(const rq_layout *L) {
+  const size_t c = (size_t)L->batch * L->n_heads * sizeof(uint32_t);
+  return (c + 255) & ~(size_t)255;
+}
+
+size_t workspace_for(const rq_layout *L, int n_splits) {
+  return counter_bytes(L) + (size_t)n_splits * rq::kMaxSlots * (size_t)L->batch * L->n_heads *
+                                (size_t)(2 * L->head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rq_status_string(rq_status s) {
+  switch (s) {
+    case RQ_OK: return "RQ_OK";
+    case RQ_ERR_INVALID_ARG: return "RQ_ERR_INVALID_ARG: null or misaligned pointer, or an argument out of range";
+    case RQ_ERR_UNSUPPORTED: return "RQ_ERR_UNSUPPORTED: head_dim, group, bits or loop count outside the supported set";
+    case RQ_ERR_WORKSPACE: return "RQ_ERR_WORKSPACE: decode workspace smaller than rq_decode_workspace_bytes";
+    case RQ_ERR_DEVICE: return "RQ_ERR_DEVICE: a HIP call or kernel launch failed";
+  }
+  return "unknown rq_status";
+}
+
+rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, const void *k_in,
+                    const void *v_in, int32_t t0, int32_t n, void *hip_stream) {
+  rq_status st = check_layout(L);
+  if (st != RQ_OK) return st;
+  if ((st = check_cache(L, k)) != RQ_OK || (st = check_cache(L, v)) != RQ_OK) return st;
+  if (!aligned16(k_in) || !aligned16(v_in)) return RQ_ERR_INVALID_ARG;
+  if (t0 < 0 || n < 0 || (int64_t)t0 + n > L->capacity) return RQ_ERR_INVALID_ARG;
+  if (n == 0) return RQ_OK;
+
+  rq::EncodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  const rq_cache *sides[2] = {k, v};
+  const void *ins[2] = {k_in, v_in};
+  for (int s = 0; s < 2; ++s) {
+    a.side[s].ref = static_cast<const uint16_t *>(sides[s]->ref);
+    a.side[s].xin = static_cast<const uint16_t *>(ins[s]);
+    for (int l = 0; l < L->n_loops - 1; ++l) {
+      a.side[s].codes[l] = static_cast<uint8_t *>(sides[s]->codes[l]);
+      a.side[s].meta[l] = static_cast<uint32_t *>(sides[s]->meta[l]);
+      a.side[s].alpha[l] = static_cast<uint16_t *>(sides[s]->alpha[l]);
+    }
+  }
+  for (int l = 0; l < L->n_loops - 1; ++l) a.bits[l] = L->bits[l];
+  a.n_res = L->n_loops - 1;
+  a.bh = L->batch * L->n_heads;
+  a.cap = L->capacity;
+  a.t0 = t0;
+  a.n = n;
+  a.group = L->group;
+  a.rotate = L->rotate;
+  a.rot_c = rot_const(L->head_dim);
+  const int vpw = 64 / (L->head_dim / 8);
+  a.chunks = (n + vpw - 1) / vpw;
+  if ((int64_t)a.bh * a.chunks * 2 > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
+  a.tasks_per_side = a.bh * a.chunks;
+  (void)hipGetLastError();
+  return rq::launch_encode(a, L->head_dim, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? RQ_OK : RQ_ERR_DEVICE;
+}
+
+int32_t rq_decode_splits(const rq_layout *L, int32_t n_ctx) {
+  if (check_layout(L) != RQ_OK || n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  const int cus = cu_count();
+  if (cus <= 0) return RQ_ERR_DEVICE;
+  return auto_splits(L, n_ctx, cus);
+}
+
+size_t rq_decode_workspace_bytes(const rq_layout *L, int32_t n_ctx, int32_t n_splits) {
+  if (check_layout(L) != RQ_OK || n_ctx < 1 || n_ctx > L->capacity || n_splits < 0) return 0;
+  int s = n_splits;
+  if (s == 0) {
+    s = rq_decode_splits(L, n_ctx);
+    if (s <= 0) return 0;
+  }
+  if (s > n_ctx) s = n_ctx;
+  return workspace_for(L, s);
+}
+
+rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *v, const void *q,
+                         uint32_t loop_mask, int32_t n_ctx, float sm_scale, int32_t n_splits,
+                         float *out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  rq_status st = check_layout(L);
+  if (st != RQ_OK) return st;
+  if (k == nullptr || v == nullptr || !aligned16(k->ref) || !aligned16(v->ref)) return RQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return RQ_ERR_INVALID_ARG;
+  if (loop_mask == 0) return RQ_ERR_INVALID_ARG;
+  if (L->n_loops < 32 && (loop_mask >> L->n_loops) != 0) return RQ_ERR_INVALID_ARG;
+  if (n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
+  if (n_splits < 0 || n_splits > n_ctx) return RQ_ERR_INVALID_ARG;
+  const int ref_loop = L->n_loops - 1;
+  for (int l = 0; l < ref_loop; ++l) {
+    if (!((loop_mask >> l) & 1u)) continue;
+    if (!aligned16(k->codes[l]) || !aligned16(k->meta[l]) || !aligned16(k->alpha[l]) ||
+        !aligned16(v->codes[l]) || !aligned16(v->meta[l]) || !aligned16(v->alpha[l]))
+      return RQ_ERR_INVALID_ARG;
+  }
+  int S = n_splits;
+  if (S == 0) {
+    S = rq_decode_splits(L, n_ctx);
+    if (S <= 0) return RQ_ERR_DEVICE;
+  }
+  if (workspace_bytes < workspace_for(L, S)) return RQ_ERR_WORKSPACE;
+  // every split non-empty
+  const int tps = (n_ctx + S - 1) / S;
+  S = (n_ctx + tps - 1) / tps;
+
+  rq::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.kref = static_cast<const uint16_t *>(k->ref);
+  a.vref = static_cast<const uint16_t *>(v->ref);
+  a.q = static_cast<const uint16_t *>(q);
+  a.counters = static_cast<uint32_t *>(workspace);
+  a.ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + counter_bytes(L));
+  a.out = out;
+  a.bh = L->batch * L->n_heads;
+  a.cap = L->capacity;
+  a.n_ctx = n_ctx;
+  a.n_splits = S;
+  a.tps = tps;
+  a.group = L->group;
+  a.rotate = L->rotate;
+  a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
+  a.rot_c = L->rotate ? rot_const(L->head_dim) : 1.0f;
+
+  int res[RQ_MAX_LOOPS], nres = 0;
+  for (int l = 0; l < ref_loop; ++l)
+    if ((loop_mask >> l) & 1u) res[nres++] = l;
+  bool want_ref = (loop_mask >> ref_loop) & 1u;
+  (void)hipGetLastError();
+  // Passes of at most kMaxRes residual loops; the first also computes the
+  // reference loop.  Each pass reads the reference once.
+  int done = 0;
+  do {
+    const int cnt = (nres - done) < rq::kMaxRes ? (nres - done) : rq::kMaxRes;
+    for (int i = 0; i < cnt; ++i) {
+      const int l = res[done + i];
+      a.kc[i] = static_cast<const uint8_t *>(k->codes[l]);
+      a.vc[i] = static_cast<const uint8_t *>(v->codes[l]);
+      a.km[i] = static_cast<const uint32_t *>(k->meta[l]);
+      a.vm[i] = static_cast<const uint32_t *>(v->meta[l]);
+      a.ka[i] = static_cast<const uint16_t *>(k->alpha[l]);
+      a.va[i] = static_cast<const uint16_t *>(v->alpha[l]);
+      a.bits[i] = L->bits[l];
+      a.qloop[i] = l;
+    }
+    if (want_ref) a.qloop[cnt] = ref_loop;
+    if (rq::launch_decode(a, L->head_dim, cnt, want_ref, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
+      return RQ_ERR_DEVICE;
+    want_ref = false;
+    done += cnt;
+  } while (done < nres);
+  return RQ_OK;
+}
+
+rq_status rq_reconstruct(const rq_layout *L, const rq_cache *c, int32_t loop, int32_t t0, int32_t n,
+                         float *out, void *hip_stream) {
+  rq_status st = check_layout(L);
+  if (st != RQ_OK) return st;
+  if (loop < 0 || loop >= L->n_loops - 1) return RQ_ERR_INVALID_ARG;
+  if (c == nullptr || !aligned16(c->ref) || !aligned16(c->codes[loop]) || !aligned16(c->meta[loop]) ||
+      !aligned16(c->alpha[loop]) || !aligned16(out))
+    return RQ_ERR_INVALID_ARG;
+  if (t0 < 0 || n < 1 || (int64_t)t0 + n > L->capacity) return RQ_ERR_INVALID_ARG;
+  rq::ReconArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.ref = static_cast<const uint16_t *>(c->ref);
+  a.codes = static_cast<const uint8_t *>(c->codes[loop]);
+  a.meta = static_cast<const uint32_t *>(c->meta[loop]);
+  a.alpha = static_cast<const uint16_t *>(c->alpha[loop]);
+  a.out = out;
+  a.bits = L->bits[loop];
+  a.bh = L->batch * L->n_heads;
+  a.cap = L->capacity;
+  a.t0 = t0;
+  a.n = n;
+  a.group = L->group;
+  a.rotate = L->rotate;
+  a.rot_c = rot_const(L->head_dim);
+  const int vpw = 64 / (L->head_dim / 8);
+  a.chunks = (n + vpw - 1) / vpw;
+  if ((int64_t)a.bh * a.chunks > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return rq::launch_reconstruct(a, L->head_dim, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? RQ_OK : RQ_ERR_DEVICE;
+}
+
+}  // extern "C"

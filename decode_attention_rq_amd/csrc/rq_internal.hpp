@@ -1,0 +1,69 @@
+// rq_internal.hpp -- launchers behind the C ABI (host side, arguments already
+// validated by rq_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq.h"
+
+namespace rq {
+
+// Kernel argument blocks.  Plane pointers are per residual loop.
+struct EncodeSide {
+  const uint16_t *ref;               // bf16 [BH][cap][D]
+  const uint16_t *xin;               // bf16 [L-1][BH][n][D]
+  uint8_t *codes[RQ_MAX_LOOPS];
+  uint32_t *meta[RQ_MAX_LOOPS];      // (scale | zero << 16) per group
+  uint16_t *alpha[RQ_MAX_LOOPS];
+};
+
+struct EncodeArgs {
+  EncodeSide side[2];                // K, V
+  int32_t bits[RQ_MAX_LOOPS];
+  int32_t n_res;                     // L - 1
+  int32_t bh;                        // B * H
+  int32_t cap, t0, n;
+  int32_t group;
+  int32_t rotate;
+  float rot_c;                       // fp32(1/sqrt(D))
+  int32_t chunks;                    // ceil(n / vectors per wave)
+  int32_t tasks_per_side;            // bh * chunks
+};
+
+struct ReconArgs {
+  const uint16_t *ref;
+  const uint8_t *codes;
+  const uint32_t *meta;
+  const uint16_t *alpha;
+  float *out;                        // f32 [BH][n][D]
+  int32_t bits, bh, cap, t0, n, group, rotate;
+  float rot_c;
+  int32_t chunks;
+};
+
+constexpr int kMaxRes = 3;           // residual loops per decode pass
+constexpr int kMaxSlots = 4;         // residual loops + the reference loop
+
+struct DecodeArgs {
+  const uint16_t *kref, *vref;       // bf16 [BH][cap][D]
+  const uint8_t *kc[kMaxRes], *vc[kMaxRes];
+  const uint32_t *km[kMaxRes], *vm[kMaxRes];
+  const uint16_t *ka[kMaxRes], *va[kMaxRes];
+  int32_t bits[kMaxRes];
+  const uint16_t *q;                 // bf16 [L][BH][D]
+  int32_t qloop[kMaxSlots];          // slot -> loop index (residual slots first)
+  float *ws;                         // f32 [S][kMaxSlots][BH][2D+2] split records
+  uint32_t *counters;                // [BH] finished splits; zero between calls
+  float *out;                        // f32 [L][BH][D]
+  int32_t bh, cap, n_ctx, n_splits, tps;
+  int32_t group, rotate;
+  float qscale;                      // sm_scale * log2(e)
+  float rot_c;
+};
+
+hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
+
+}  // namespace rq

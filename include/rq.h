@@ -85,15 +85,17 @@ typedef struct {
  * quantization with a per-loop bit width (steps 1 and 5; Table 5).  For each
  * (loop l < L-1, batch b, head h, token t) and separately for K and V, with
  * x the loop-l vector and y = ref[b][h][t] (both BF16, widened exactly):
- *   alpha = fp16(<x,y> / <y,y>)   (0 if <y,y> = 0; dot products are FP32
- *                                   pairwise-halving sums; FP16 stores are
- *                                   round-to-nearest-even, saturating)
+ *   alpha = fp16(<x,y> / <y,y>)   (0 if <y,y> = 0; each dot product sums
+ *                                   its FP32 terms in blocks of 8 by pairwise
+ *                                   halving, then the block sums by pairwise
+ *                                   halving; FP16 stores round to nearest
+ *                                   even and saturate at +-65504)
  *   r     = fma(-alpha, y, x)                                     (FP32)
  *   u     = fp32(1/sqrt(d)) * H_d r     if rotate (H_d Sylvester Hadamard,
  *                                        butterflies h = 1, 2, ..., d/2)
  *   per group k of g consecutive dims:  s = fp16((max - min) / (2^b - 1)),
  *     z = fp16(min),  code = clamp(rne((u - z) * (1/s)), 0, 2^b - 1)
- *     (all codes 0 if s = 0)
+ *     (u canonicalized to +0 where it is -0; all codes 0 if s = 0)
  * The result is bit-identical to that FP32 definition.
  *
  *   k, v    caches; their ref planes must already hold tokens [t0, t0+n)
@@ -136,8 +138,11 @@ int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
  *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise
  *   out        f32 [L][B][H][d]; rows of loops not in the mask are not written
  *   workspace  device scratch of at least rq_decode_workspace_bytes(layout,
- *              n_ctx, n_splits) bytes, 16-byte aligned; contents need no
- *              initialisation and are garbage afterwards
+ *              n_ctx, n_splits) bytes, 16-byte aligned.  It must be zero-filled
+ *              before its first use; every call leaves it in a state that the
+ *              next call accepts (its leading counters back at zero), so one
+ *              workspace serves any number of calls on one stream.  Calls that
+ *              may run concurrently need separate workspaces.
  * Results agree with an FP64 evaluation of the same definition to within a
  * few 1e-4 of the row's largest output magnitude.
  */

@@ -1,0 +1,178 @@
+"""C ABI checks that need no GPU: librq.so loads, exports every entry point
+include/rq.h declares, and rejects invalid arguments on the host before any
+HIP call (fake, never-dereferenced device addresses are used; every case here
+fails validation, so nothing is ever enqueued)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+
+@pytest.fixture(scope="module")
+def rq():
+    import decode_attention_rq_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["rq_encode", "rq_decode_workspace_bytes", "rq_decode_splits",
+                            "rq_decode_attn", "rq_reconstruct", "rq_status_string"])
+
+
+def test_library_exports_every_declared_symbol(rq):
+    lib = C.CDLL(rq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(rq):
+    for code, name in rq.STATUS.items():
+        assert rq.rq_status_string(code).startswith(name)
+    assert rq.rq_status_string(12345) == "unknown rq_status"
+
+
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def _layout(rq, **kw):
+    lay = rq.Layout(n_loops=4, batch=2, n_heads=2, head_dim=128, group=32, capacity=64, rotate=1,
+                    bits=[2, 2, 2])
+    for k, v in kw.items():
+        setattr(lay, k, v)
+    return lay
+
+
+def _cache(rq, n_loops=4, bad=None):
+    c = rq.rq_cache()
+    c.ref = FAKE
+    for l in range(n_loops - 1):
+        c.codes[l] = FAKE + 0x1000 * (l + 1)
+        c.meta[l] = FAKE + 0x100000 * (l + 1)
+        c.alpha[l] = FAKE + 0x10000000 * (l + 1)
+    if bad:
+        field, l, val = bad
+        if field == "ref":
+            c.ref = val
+        else:
+            getattr(c, field)[l] = val
+    return c
+
+
+def _encode(rq, lay, k=None, v=None, kin=FAKE, vin=FAKE, t0=0, n=8):
+    L = lay.c()
+    k = k or _cache(rq, lay.n_loops)
+    v = v or _cache(rq, lay.n_loops)
+    return rq._lib.rq_encode(C.byref(L), C.byref(k), C.byref(v), kin, vin, t0, n, None)
+
+
+def _decode(rq, lay, mask=0b1111, n_ctx=32, scale=0.1, splits=2, out=FAKE, ws=FAKE,
+            ws_bytes=1 << 30, q=FAKE, k=None, v=None):
+    L = lay.c()
+    k = k or _cache(rq, lay.n_loops)
+    v = v or _cache(rq, lay.n_loops)
+    return rq._lib.rq_decode_attn(C.byref(L), C.byref(k), C.byref(v), q, mask, n_ctx, scale, splits,
+                                  out, ws, ws_bytes, None)
+
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_loops=1), UNSUPPORTED), (dict(n_loops=33), UNSUPPORTED),
+    (dict(batch=0), INVALID), (dict(n_heads=0), INVALID), (dict(capacity=0), INVALID),
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=32), UNSUPPORTED),
+    (dict(group=8), UNSUPPORTED), (dict(group=64), UNSUPPORTED),
+    (dict(rotate=2), INVALID), (dict(bits=[2, 3, 2]), UNSUPPORTED), (dict(bits=[2, 2, 8]), UNSUPPORTED),
+    (dict(batch=70000), UNSUPPORTED), (dict(batch=1024, n_heads=64, capacity=1 << 20), UNSUPPORTED),
+])
+def test_layout_validation(rq, kw, code):
+    lay = _layout(rq, **kw)
+    assert _encode(rq, lay) == code
+    assert _decode(rq, lay) == code
+    L = lay.c()
+    c = _cache(rq, max(2, min(lay.n_loops, 32)))
+    assert rq._lib.rq_reconstruct(C.byref(L), C.byref(c), 0, 0, 4, FAKE, None) == code
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(L), 16, 2) == 0
+    assert rq._lib.rq_decode_splits(C.byref(L), 16) == INVALID
+
+
+def test_null_layout_and_caches(rq):
+    k = _cache(rq)
+    assert rq._lib.rq_encode(None, C.byref(k), C.byref(k), FAKE, FAKE, 0, 1, None) == INVALID
+    lay = _layout(rq).c()
+    assert rq._lib.rq_encode(C.byref(lay), None, C.byref(k), FAKE, FAKE, 0, 1, None) == INVALID
+    assert rq._lib.rq_decode_attn(C.byref(lay), C.byref(k), None, FAKE, 1, 4, 0.1, 1, FAKE, FAKE,
+                                  1 << 30, None) == INVALID
+
+
+@pytest.mark.parametrize("bad", [("ref", 0, 0), ("ref", 0, FAKE + 8), ("codes", 1, 0),
+                                 ("meta", 2, FAKE + 4), ("alpha", 0, 0)])
+def test_encode_plane_pointers(rq, bad):
+    lay = _layout(rq)
+    assert _encode(rq, lay, k=_cache(rq, bad=bad)) == INVALID
+    assert _encode(rq, lay, v=_cache(rq, bad=bad)) == INVALID
+
+
+@pytest.mark.parametrize("t0,n", [(-1, 4), (0, -1), (60, 5), (64, 1), (1 << 30, 1 << 30)])
+def test_encode_token_range(rq, t0, n):
+    assert _encode(rq, _layout(rq), t0=t0, n=n) == INVALID
+
+
+def test_encode_inputs(rq):
+    lay = _layout(rq)
+    assert _encode(rq, lay, kin=0) == INVALID
+    assert _encode(rq, lay, vin=FAKE + 2) == INVALID
+
+
+def test_encode_empty_range_is_a_noop(rq):
+    # n = 0 validates and returns before touching the device
+    assert _encode(rq, _layout(rq), t0=64, n=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=0), INVALID), (dict(mask=0b10000), INVALID), (dict(mask=1 << 31), INVALID),
+    (dict(n_ctx=0), INVALID), (dict(n_ctx=65), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(splits=-1), INVALID), (dict(splits=33), INVALID),
+    (dict(out=0), INVALID), (dict(out=FAKE + 4), INVALID), (dict(q=0), INVALID), (dict(ws=0), INVALID),
+    (dict(ws_bytes=0), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+])
+def test_decode_validation(rq, kw, code):
+    assert _decode(rq, _layout(rq), **kw) == code
+
+
+def test_decode_only_checks_planes_of_masked_loops(rq):
+    lay = _layout(rq)
+    k = _cache(rq, bad=("codes", 1, 0))
+    assert _decode(rq, lay, mask=0b0010, k=k) == INVALID
+    # loop 1 not in the mask: its null plane is not looked at; a too-small
+    # workspace then shows the pointer checks passed
+    assert _decode(rq, lay, mask=0b1101, k=k, ws_bytes=1) == WORKSPACE
+
+
+def test_workspace_size_formula(rq):
+    lay = _layout(rq).c()
+    # 256 bytes of counters (4 (b,h), padded), then
+    # 2 splits * 4 slots * (2*2) (b,h) * (2*128+2) floats
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 2) == 256 + 2 * 4 * 4 * 258 * 4
+    # more splits than tokens are clamped to one token per split
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 3, 8) == 256 + 3 * 4 * 4 * 258 * 4
+
+
+@pytest.mark.parametrize("loop,t0,n", [(-1, 0, 4), (3, 0, 4), (0, -1, 4), (0, 0, 0), (0, 62, 4)])
+def test_reconstruct_validation(rq, loop, t0, n):
+    L = _layout(rq).c()
+    c = _cache(rq)
+    assert rq._lib.rq_reconstruct(C.byref(L), C.byref(c), loop, t0, n, FAKE, None) == INVALID
+    assert rq._lib.rq_reconstruct(C.byref(L), C.byref(c), 0, 0, 4, FAKE + 8, None) == INVALID
