@@ -173,8 +173,8 @@ def rq_reconstruct(layout: Layout, c: Cache, loop: int, t0: int, n: int, out: to
 
 
 def workspace_for(layout: Layout, n_ctx: int, n_splits: int = 0, device="cuda") -> torch.Tensor:
-    """A zero-filled decode workspace (the library keeps it reusable)."""
+    """A decode workspace of the size the library asks for."""
     nbytes = rq_decode_workspace_bytes(layout, n_ctx, n_splits)
     if nbytes == 0:
         raise RQError(-1)
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)

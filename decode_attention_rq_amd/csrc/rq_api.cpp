@@ -56,11 +56,11 @@ int cu_count() {
   return n;
 }
 
-// Token splits for a decode step: enough workgroups to give every compute
-// unit several, but never fewer than 256 tokens per split.
+// Token splits for a decode step: one 8-wave workgroup per compute unit at
+// least, never fewer than 256 tokens per split.
 int auto_splits(const rq_layout *L, int n_ctx, int cus) {
   const int64_t bh = (int64_t)L->batch * L->n_heads;
-  const int64_t target = (int64_t)cus * 4;
+  const int64_t target = (int64_t)cus;
   int64_t s = (target + bh - 1) / bh;
   const int64_t max_by_len = n_ctx / 256 > 0 ? n_ctx / 256 : 1;
   if (s > max_by_len) s = max_by_len;
@@ -73,16 +73,12 @@ int auto_splits(const rq_layout *L, int n_ctx, int cus) {
   return (int)s;
 }
 
-// Workspace: [BH] uint32 counters (padded to 256 bytes), then the split
-// records f32 [S][kMaxSlots][BH][2D+2].
-size_t counter_bytes(const rq_layout *L) {
-  const size_t c = (size_t)L->batch * L->n_heads * sizeof(uint32_t);
-  return (c + 255) & ~(size_t)255;
-}
-
+// Workspace: the split records f32 [S][kMaxSlots][BH][2D+2]; none for S = 1
+// (a 256-byte minimum keeps the pointer checks uniform).
 size_t workspace_for(const rq_layout *L, int n_splits) {
-  return counter_bytes(L) + (size_t)n_splits * rq::kMaxSlots * (size_t)L->batch * L->n_heads *
-                                (size_t)(2 * L->head_dim + 2) * sizeof(float);
+  if (n_splits <= 1) return 256;
+  return (size_t)n_splits * rq::kMaxSlots * (size_t)L->batch * L->n_heads *
+         (size_t)(2 * L->head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -192,8 +188,7 @@ rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *
   a.kref = static_cast<const uint16_t *>(k->ref);
   a.vref = static_cast<const uint16_t *>(v->ref);
   a.q = static_cast<const uint16_t *>(q);
-  a.counters = static_cast<uint32_t *>(workspace);
-  a.ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + counter_bytes(L));
+  a.ws = static_cast<float *>(workspace);
   a.out = out;
   a.bh = L->batch * L->n_heads;
   a.cap = L->capacity;

@@ -12,16 +12,16 @@
 // with q' = H_n q, so the per-token work is the reference dot product, the
 // code dot products and FMA accumulation; H_n is applied once per output.
 //
-// One kernel per call (per pass of up to three residual loops): a workgroup
-// per (token split, batch*head); 4 waves, each taking every 4th tile of
-// ROWS*TR tokens.  Lanes: D/8 lanes per token, 8 consecutive dims per lane,
-// ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane reads ROWS
-// consecutive reference rows, and every loop of the pass shares that load.
-// Online softmax per (row, loop) in the exp2 domain; rows, then waves
-// (through LDS), are merged by log-sum-exp into one record per (split, loop,
-// batch*head) in the workspace.  The last workgroup of a batch*head to finish
-// (an atomic counter in the workspace, reset by that workgroup) merges the
-// splits, un-rotates the residual accumulator and normalises.
+// Kernel P, one launch per pass of up to three residual loops: a workgroup
+// of W waves per (token split, batch*head), each wave taking every W-th tile
+// of ROWS*TR tokens.  Lanes: D/8 lanes per token, 8 consecutive dims per
+// lane, ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane
+// reads ROWS consecutive reference rows, and every loop of the pass shares
+// that load.  Online softmax per (row, loop) in the exp2 domain; rows, then
+// waves (through LDS), are merged by log-sum-exp.  With one split the
+// workgroup finishes the output itself (un-rotation of the residual
+// accumulator, normalisation); with several it writes one record per (split,
+// loop, batch*head) to the workspace and kernel M merges the records.
 
 #include <float.h>
 
@@ -39,8 +39,6 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D>
-__device__ __forceinline__ void merge_splits(const DecodeArgs &a, int bh, int s, bool residual, int lane);
 
 // Merge the online-softmax states of rows at lane distance MASK.
 template <int MASK, int NS, int NR>
@@ -62,244 +60,13 @@ __device__ __forceinline__ void merge_rows(float (&m)[NS], float (&l)[NS], float
   }
 }
 
-template <int D, int NR, bool REF, int TR>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int LANES = D / 8;
-  constexpr int ROWS = kWave / LANES;
-  constexpr int NS = NR + (REF ? 1 : 0);
-  constexpr int NRA = NR > 0 ? NR : 1;
-  constexpr int TILE = ROWS * TR;
-  constexpr int REC = 2 * D + 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane % LANES, r = lane / LANES;
-  const int split = blockIdx.x, bh = blockIdx.y;
-  const int t_begin = split * a.tps;
-  const int t_end = min(t_begin + a.tps, a.n_ctx);
-  const int gl = a.group / 8;
-  const int G = D / a.group;
-  const int k = j / gl;
-
-  // ---- prologue: queries of every loop in the pass -------------------------
-  uint32_t qb[NS][4];
-  float qr[NRA][8], sig[NRA];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
-    qb[s][0] = w.x; qb[s][1] = w.y; qb[s][2] = w.z; qb[s][3] = w.w;
-  }
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    float f[8];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(qb[i][p]); f[2 * p + 1] = bf16hi(qb[i][p]); }
-    if (a.rotate) wht8<D>(f, lane);
-    float sacc = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) { qr[i][p] = f[p] * (a.rot_c * a.qscale); sacc += qr[i][p]; }
-    sig[i] = sacc;
-  }
-
-  float m[NS], l[NS], oref[NS][8], ores[NRA][8], zacc[NRA];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    m[s] = -FLT_MAX; l[s] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < NRA; ++i) {
-    zacc[i] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
-  }
-
-  // ---- token tiles ----------------------------------------------------------
-  for (int base = t_begin + wave * TILE; base < t_end; base += 4 * TILE) {
-    uint4 yk[TR], yv[TR];
-    uint32_t kcw[TR][NRA], kmw[TR][NRA], kaw[TR][NRA], vcw[TR][NRA], vmw[TR][NRA], vaw[TR][NRA];
-    bool valid[TR];
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      const int t = base + u * ROWS + r;
-      valid[u] = t < t_end;
-      const size_t slot = (size_t)bh * a.cap + (size_t)(valid[u] ? t : t_end - 1);
-      yk[u] = *reinterpret_cast<const uint4 *>(a.kref + slot * D + 8 * j);
-      yv[u] = *reinterpret_cast<const uint4 *>(a.vref + slot * D + 8 * j);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (a.bits[i] == 2) {
-          kcw[u][i] = reinterpret_cast<const uint16_t *>(a.kc[i] + slot * (D / 4))[j];
-          vcw[u][i] = reinterpret_cast<const uint16_t *>(a.vc[i] + slot * (D / 4))[j];
-        } else {
-          kcw[u][i] = reinterpret_cast<const uint32_t *>(a.kc[i] + slot * (D / 2))[j];
-          vcw[u][i] = reinterpret_cast<const uint32_t *>(a.vc[i] + slot * (D / 2))[j];
-        }
-        kmw[u][i] = a.km[i][slot * G + k];
-        vmw[u][i] = a.vm[i][slot * G + k];
-        kaw[u][i] = a.ka[i][slot];
-        vaw[u][i] = a.va[i][slot];
-      }
-    }
-
-    // scores
-    float sc[TR][NS];
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      float part[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float dy = dot2bf(qb[s][0], yk[u].x, 0.0f);
-        dy = dot2bf(qb[s][1], yk[u].y, dy);
-        dy = dot2bf(qb[s][2], yk[u].z, dy);
-        dy = dot2bf(qb[s][3], yk[u].w, dy);
-        part[s] = dy;
-      }
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int bits = a.bits[i];
-        const uint32_t mask = (1u << bits) - 1u;
-        float dc = 0.0f;
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          dc = __builtin_fmaf(qr[i][p], (float)((kcw[u][i] >> (bits * p)) & mask), dc);
-        const float sK = f16_to_f32(kmw[u][i] & 0xffffu), zK = f16_to_f32(kmw[u][i] >> 16);
-        const float aK = f16_to_f32(kaw[u][i]);
-        part[i] = __builtin_fmaf(aK * a.qscale, part[i], __builtin_fmaf(sK, dc, zK * sig[i]));
-      }
-      if (REF) part[NR] *= a.qscale;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float tot = group_sum<LANES>(part[s]);
-        sc[u][s] = valid[u] ? tot : -INFINITY;
-      }
-    }
-
-    // online softmax: one rescale per tile
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      float mt = sc[0][s];
-#pragma unroll
-      for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u][s]);
-      const float mn = fmaxf(m[s], mt);
-      const float f = fexp2(m[s] - mn);
-      m[s] = mn;
-      l[s] *= f;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) oref[s][p] *= f;
-      if (s < NR) {
-        zacc[s] *= f;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) ores[s][p] *= f;
-      }
-    }
-
-    // values
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      const float y[8] = {bf16lo(yv[u].x), bf16hi(yv[u].x), bf16lo(yv[u].y), bf16hi(yv[u].y),
-                          bf16lo(yv[u].z), bf16hi(yv[u].z), bf16lo(yv[u].w), bf16hi(yv[u].w)};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float pr = fexp2(sc[u][s] - m[s]);
-        l[s] += pr;
-        if (s < NR) {
-          const int bits = a.bits[s];
-          const uint32_t mask = (1u << bits) - 1u;
-          const float sV = f16_to_f32(vmw[u][s] & 0xffffu), zV = f16_to_f32(vmw[u][s] >> 16);
-          const float wr = pr * f16_to_f32(vaw[u][s]);
-          const float wq = pr * sV;
-          zacc[s] = __builtin_fmaf(pr, zV, zacc[s]);
-#pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
-            ores[s][p] = __builtin_fmaf(wq, (float)((vcw[u][s] >> (bits * p)) & mask), ores[s][p]);
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
-        }
-      }
-    }
-  }
-
-  // ---- merge rows, then waves -----------------------------------------------
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-#pragma unroll
-    for (int p = 0; p < 8; ++p) ores[i][p] += zacc[i];
-  }
-  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l, oref, ores);
-  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l, oref, ores);
-  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l, oref, ores);
-
-  __shared__ float sm[4][NS][REC];
-  if (r == 0) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (j == 0) { sm[wave][s][0] = m[s]; sm[wave][s][1] = l[s]; }
-#pragma unroll
-      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
-      if (s < NR) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
-      }
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < NS * REC; e += 256) {
-    const int s = e / REC, c = e - s * REC;
-    if (s >= NR && c >= 2 + D) continue;             // the reference loop has no residual part
-    const float M = fmaxf(fmaxf(sm[0][s][0], sm[1][s][0]), fmaxf(sm[2][s][0], sm[3][s][0]));
-    float v;
-    if (c == 0) {
-      v = M;
-    } else {
-      v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v = __builtin_fmaf(fexp2(sm[w][s][0] - M), sm[w][s][c], v);
-    }
-    a.ws[(((size_t)split * kMaxSlots + s) * a.bh + bh) * REC + c] = v;
-  }
-
-  // ---- the last split of this batch*head merges all splits -----------------
-  __shared__ int last;
-  __threadfence();                                   // release this split's record
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(a.counters + bh, 1u) == (unsigned)(a.n_splits - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();                                   // acquire the other splits' records
-  if (wave < NS) merge_splits<D>(a, bh, wave, wave < NR, lane);
-  if (threadIdx.x == 0) a.counters[bh] = 0u;         // ready for the next call
-}
-
-// Log-sum-exp over the splits' records of one (batch*head, slot), then
-// o = (o_ref + H_n o_res) / l.  One wave; lane holds dims lane + 64*e.
+// Output row of one (loop slot, batch*head), lane holding dims lane + 64*e:
+// out = (o_ref + H_n o_res) / l.  H_n runs as butterflies across lanes
+// (distances 1..32) and across the lane's E = D/64 elements.
 template <int D>
-__device__ __forceinline__ void merge_splits(const DecodeArgs &a, int bh, int s, bool residual, int lane) {
+__device__ __forceinline__ void finish_row(const DecodeArgs &a, int bh, int s, bool residual, int lane,
+                                           float L, float (&o)[D / 64], float (&w)[D / 64]) {
   constexpr int E = D / 64;
-  constexpr int REC = 2 * D + 2;
-  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
-  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
-
-  float M = -FLT_MAX;
-  for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
-  M = group_max<64>(M);
-
-  float L = 0.0f, o[E], w[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) { o[e] = 0.0f; w[e] = 0.0f; }
-  for (int sp = 0; sp < a.n_splits; ++sp) {
-    const float *rec = rec0 + sp * stride;
-    const float f = fexp2(rec[0] - M);
-    L = __builtin_fmaf(f, rec[1], L);
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(f, rec[2 + lane + 64 * e], o[e]);
-    if (residual) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) w[e] = __builtin_fmaf(f, rec[2 + D + lane + 64 * e], w[e]);
-    }
-  }
   if (residual) {
     if (a.rotate) {
 #pragma unroll
@@ -335,28 +102,425 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, int bh, int s,
   for (int e = 0; e < E; ++e) out[lane + 64 * e] = o[e] * invL;
 }
 
-template <int D, int NR, bool REF>
-static hipError_t launch_partial(const DecodeArgs &a, hipStream_t st) {
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// fma(a, h, c) where h is one half of `w` read as an FP16 number (v_fma_mix_f32
+// takes the half directly, no conversion instruction).
+template <int HI>
+__device__ __forceinline__ float fma_half(float a, uint32_t w, float c) {
+  const half2_t h = __builtin_bit_cast(half2_t, w);
+  return __builtin_fmaf(a, (float)h[HI], c);
+}
+
+// The 8 codes of one lane as 8 FP16 halves, each holding one code in its
+// mantissa bits: a half whose bit pattern is c << b (b + width <= 10) is the
+// subnormal number c * 2^(b-24), exact.  Code p lands in half (p / 4) of word
+// w[p % 4] for INT2 and in half (p / 4) of word w[p % 4] for INT4 as well,
+// at mantissa bit position pos(p) (see code_pos).
+//   INT2 (16-bit word x, code p at bits 2p): bytes x0 = c0..c3, x1 = c4..c7 are
+//   spread to the two halves, then masked per code.
+//   INT4 (32-bit word x, code p at bits 4p): halves already hold c0..c3 and
+//   c4..c7; codes 2, 3 (6, 7) are shifted down by 8 bits first.
+template <bool INT4>
+__device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
+  if constexpr (INT4) {
+    const uint32_t y = x >> 8;
+    w[0] = x & 0x000F000Fu;
+    w[1] = x & 0x00F000F0u;
+    w[2] = y & 0x000F000Fu;
+    w[3] = y & 0x00F000F0u;
+  } else {
+    const uint32_t X = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [x.b0, 0, x.b1, 0]
+    w[0] = X & 0x00030003u;
+    w[1] = X & 0x000C000Cu;
+    w[2] = X & 0x00300030u;
+    w[3] = X & 0x00C000C0u;
+  }
+}
+
+// Mantissa bit position of code p in its half (so its half reads c * 2^(pos-24)).
+template <bool INT4>
+__host__ __device__ constexpr int code_pos(int p) {
+  return INT4 ? 4 * (p & 1) : 2 * (p & 3);
+}
+
+// Sum over the lane's 8 codes of coef[p] * half_p  (coef pre-multiplied by
+// 2^(24 - pos) makes this sum_p coef'[p] * c_p).
+template <bool INT4>
+__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fma_half<0>(coef[q], w[q], acc);
+    acc = fma_half<1>(coef[q + 4], w[q], acc);
+  }
+  return acc;
+}
+
+// acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
+template <bool INT4>
+__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = fma_half<0>(wgt, w[q], acc[q]);
+    acc[q + 4] = fma_half<1>(wgt, w[q], acc[q + 4]);
+  }
+}
+
+// Load from a uniform base plus a 32-bit byte offset (global_load with an
+// SGPR base and a 32-bit VGPR offset; no 64-bit address arithmetic per lane).
+template <typename T>
+__device__ __forceinline__ T ldg(const void *base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+template <int TR, int NRA>
+struct Tile {
+  uint4 yk[TR], yv[TR];
+  uint32_t kc[TR][NRA], km[TR][NRA], ka[TR][NRA], vc[TR][NRA], vm[TR][NRA], va[TR][NRA];
+};
+
+// Scores above the running max by more than this (log2 units) trigger a
+// rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int NR, bool REF, int B4, int TR, int W>
+__global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
+  constexpr int LANES = D / 8;
+  constexpr int ROWS = kWave / LANES;
+  constexpr int NS = NR + (REF ? 1 : 0);
+  constexpr int NRA = NR > 0 ? NR : 1;
+  constexpr int TILE = ROWS * TR;
+  constexpr int STEP = W * TILE;
+  constexpr int REC = 2 * D + 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LANES, r = lane / LANES;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int t_begin = split * a.tps;
+  const int t_end = min(t_begin + a.tps, a.n_ctx);
+  const int G = D / a.group;
+  const int k = j / (a.group / 8);
+
+  // Plane bases of this (batch, head): uniform, so they live in SGPRs and
+  // every load is base + 32-bit lane offset.
+  const size_t row0 = (size_t)bh * a.cap;
+  const uint16_t *kref = a.kref + row0 * D;
+  const uint16_t *vref = a.vref + row0 * D;
+  const uint8_t *kc[NRA], *vc[NRA];
+  const uint32_t *km[NRA], *vm[NRA];
+  const uint16_t *ka[NRA], *va[NRA];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int cb = ((B4 >> i) & 1) ? D / 2 : D / 4;
+    kc[i] = a.kc[i] + row0 * cb;
+    vc[i] = a.vc[i] + row0 * cb;
+    km[i] = a.km[i] + row0 * G;
+    vm[i] = a.vm[i] + row0 * G;
+    ka[i] = a.ka[i] + row0;
+    va[i] = a.va[i] + row0;
+  }
+
+  // ---- prologue: queries of every loop in the pass -------------------------
+  // Reference dots use the BF16 query pairs as stored; residual dots use
+  // q' = H_n q * scale * log2(e) in FP32, each element pre-multiplied by
+  // 2^(24 - pos) for its code's position in code_halves.
+  uint32_t qb[NS][4];
+  float qr[NRA][8], sig[NRA];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+    qb[s][0] = w.x; qb[s][1] = w.y; qb[s][2] = w.z; qb[s][3] = w.w;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float f[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(qb[i][p]); f[2 * p + 1] = bf16hi(qb[i][p]); }
+    if (a.rotate) wht8<D>(f, lane);
+    float tot = 0.0f;
+    const bool int4 = (B4 >> i) & 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float v = f[p] * (a.rot_c * a.qscale);
+      tot += v;
+      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
+      qr[i][p] = v * (float)(1 << (24 - pos));
+    }
+    sig[i] = tot;
+  }
+
+  float m[NS], l[NS], oref[NS][8], ores[NRA][8], zacc[NRA];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    m[s] = -FLT_MAX; l[s] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NRA; ++i) {
+    zacc[i] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
+  }
+
+  auto load = [&](Tile<TR, NRA> &T, int base) {
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      const uint32_t t = (uint32_t)min(base + u * ROWS + r, t_end - 1);
+      T.yk[u] = ldg<uint4>(kref, t * (2 * D) + 16 * j);
+      T.yv[u] = ldg<uint4>(vref, t * (2 * D) + 16 * j);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if ((B4 >> i) & 1) {
+          T.kc[u][i] = ldg<uint32_t>(kc[i], t * (D / 2) + 4 * j);
+          T.vc[u][i] = ldg<uint32_t>(vc[i], t * (D / 2) + 4 * j);
+        } else {
+          T.kc[u][i] = ldg<uint16_t>(kc[i], t * (D / 4) + 2 * j);
+          T.vc[u][i] = ldg<uint16_t>(vc[i], t * (D / 4) + 2 * j);
+        }
+        T.km[u][i] = ldg<uint32_t>(km[i], (t * G + k) * 4);
+        T.vm[u][i] = ldg<uint32_t>(vm[i], (t * G + k) * 4);
+        T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
+        T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
+      }
+    }
+  };
+
+  auto process = [&](const Tile<TR, NRA> &T, int base) {
+    // scores (log2 units)
+    float sc[TR][NS];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      float part[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float dy = dot2bf(qb[s][0], T.yk[u].x, 0.0f);
+        dy = dot2bf(qb[s][1], T.yk[u].y, dy);
+        dy = dot2bf(qb[s][2], T.yk[u].z, dy);
+        part[s] = dot2bf(qb[s][3], T.yk[u].w, dy);
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float dc = ((B4 >> i) & 1) ? code_dot<true>(T.kc[u][i], qr[i], 0.0f)
+                                         : code_dot<false>(T.kc[u][i], qr[i], 0.0f);
+        const float sK = f16_to_f32(T.km[u][i] & 0xffffu), zK = f16_to_f32(T.km[u][i] >> 16);
+        const float aK = f16_to_f32(T.ka[u][i]);
+        part[i] = __builtin_fmaf(aK * a.qscale, part[i], __builtin_fmaf(sK, dc, zK * sig[i]));
+      }
+      if (REF) part[NR] *= a.qscale;
+      const bool valid = base + u * ROWS + r < t_end;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float tot = group_sum_dpp<LANES>(part[s]);
+        sc[u][s] = valid ? tot : -INFINITY;
+      }
+    }
+
+    // online softmax; rescale only when the max grows by more than the slack
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float mt = sc[0][s];
+#pragma unroll
+      for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u][s]);
+      if (mt > m[s] + kRescaleSlack) {
+        const float f = fexp2(m[s] - mt);
+        m[s] = mt;
+        l[s] *= f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+        if (s < NR) {
+          zacc[s] *= f;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+        }
+      }
+    }
+
+    // values
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      const float y[8] = {bf16lo(T.yv[u].x), bf16hi(T.yv[u].x), bf16lo(T.yv[u].y), bf16hi(T.yv[u].y),
+                          bf16lo(T.yv[u].z), bf16hi(T.yv[u].z), bf16lo(T.yv[u].w), bf16hi(T.yv[u].w)};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float pr = fexp2(sc[u][s] - m[s]);
+        l[s] += pr;
+        if (s < NR) {
+          const float sV = f16_to_f32(T.vm[u][s] & 0xffffu), zV = f16_to_f32(T.vm[u][s] >> 16);
+          const float wr = pr * f16_to_f32(T.va[u][s]);
+          zacc[s] = __builtin_fmaf(pr, zV, zacc[s]);
+#pragma unroll
+          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
+          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], pr * sV, ores[s]);
+          else code_axpy<false>(T.vc[u][s], pr * sV, ores[s]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
+        }
+      }
+    }
+  };
+
+  // ---- token tiles: two tile buffers, the next one loading while the other
+  // is processed ------------------------------------------------------------
+  int base = t_begin + wave * TILE;
+  Tile<TR, NRA> ta, tb;
+  if (base < t_end) load(ta, base);
+  while (base < t_end) {
+    if (base + STEP < t_end) load(tb, base + STEP);
+    process(ta, base);
+    base += STEP;
+    if (base >= t_end) break;
+    if (base + STEP < t_end) load(ta, base + STEP);
+    process(tb, base);
+    base += STEP;
+  }
+
+  // undo the 2^(pos-24) factors of the value codes, add the offsets' share
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const bool int4 = (B4 >> i) & 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
+      ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - pos)), zacc[i]);
+    }
+  }
+
+  // ---- merge rows, then waves -----------------------------------------------
+  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l, oref, ores);
+  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l, oref, ores);
+  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l, oref, ores);
+
+  __shared__ float sm[W][NS][REC];
+  if (r == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (j == 0) { sm[wave][s][0] = m[s]; sm[wave][s][1] = l[s]; }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
+      if (s < NR) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
+      }
+    }
+  }
+  __syncthreads();
+  // wave s combines loop slot s over the W waves
+  if (wave < NS) {
+    const int s = wave;
+    const bool residual = s < NR;
+    float M = sm[0][s][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w][s][0]);
+    float f[W];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) { f[w] = fexp2(sm[w][s][0] - M); L = __builtin_fmaf(f[w], sm[w][s][1], L); }
+    constexpr int E = D / 64;
+    float o[E], q[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      o[e] = 0.0f; q[e] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        o[e] = __builtin_fmaf(f[w], sm[w][s][2 + lane + 64 * e], o[e]);
+        if (residual) q[e] = __builtin_fmaf(f[w], sm[w][s][2 + D + lane + 64 * e], q[e]);
+      }
+    }
+    if (a.n_splits == 1) {
+      finish_row<D>(a, bh, s, residual, lane, L, o, q);
+    } else {
+      float *rec = a.ws + (((size_t)split * kMaxSlots + s) * a.bh + bh) * REC;
+      if (lane == 0) { rec[0] = M; rec[1] = L; }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        rec[2 + lane + 64 * e] = o[e];
+        if (residual) rec[2 + D + lane + 64 * e] = q[e];
+      }
+    }
+  }
+}
+
+// Kernel M: one wave per (batch*head, loop slot): log-sum-exp over the
+// splits' records, then finish_row.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, int n_res) {
+  constexpr int E = D / 64;
+  constexpr int REC = 2 * D + 2;
+  const int bh = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const bool residual = s < n_res;
+  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
+  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
+
+  float M = -FLT_MAX;
+  for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
+  M = group_max<64>(M);
+
+  float L = 0.0f, o[E], q[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) { o[e] = 0.0f; q[e] = 0.0f; }
+  for (int sp = 0; sp < a.n_splits; ++sp) {
+    const float *rec = rec0 + sp * stride;
+    const float f = fexp2(rec[0] - M);
+    L = __builtin_fmaf(f, rec[1], L);
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(f, rec[2 + lane + 64 * e], o[e]);
+    if (residual) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[e] = __builtin_fmaf(f, rec[2 + D + lane + 64 * e], q[e]);
+    }
+  }
+  finish_row<D>(a, bh, s, residual, lane, L, o, q);
+}
+
+template <int D, int NR, bool REF, int B4>
+static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   constexpr int TR = 2;
-  const dim3 grid(a.n_splits, a.bh), block(256);
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, TR>), grid, block, 0, st, a);
+  constexpr int W = 8;
+  const dim3 grid(a.n_splits, a.bh), block(64 * W);
+  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, W>), grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.bh, NR + (REF ? 1 : 0)), dim3(64), 0, st, a, NR);
   return hipGetLastError();
+}
+
+// Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
+template <int D, int NR, bool REF>
+static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
+  int b4 = 0;
+  for (int i = 0; i < NR; ++i) b4 |= (a.bits[i] == 4) << i;
+  switch (b4) {
+    case 0: return launch_kernel<D, NR, REF, 0>(a, st);
+    case 1: if constexpr (NR >= 1) return launch_kernel<D, NR, REF, 1>(a, st); break;
+    case 2: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 2>(a, st); break;
+    case 3: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 3>(a, st); break;
+    case 4: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 4>(a, st); break;
+    case 5: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 5>(a, st); break;
+    case 6: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 6>(a, st); break;
+    case 7: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 7>(a, st); break;
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
   if (ref) {
     switch (n_res) {
-      case 0: return launch_partial<D, 0, true>(a, st);
-      case 1: return launch_partial<D, 1, true>(a, st);
-      case 2: return launch_partial<D, 2, true>(a, st);
-      case 3: return launch_partial<D, 3, true>(a, st);
+      case 0: return launch_bits<D, 0, true>(a, st);
+      case 1: return launch_bits<D, 1, true>(a, st);
+      case 2: return launch_bits<D, 2, true>(a, st);
+      case 3: return launch_bits<D, 3, true>(a, st);
     }
   } else {
     switch (n_res) {
-      case 1: return launch_partial<D, 1, false>(a, st);
-      case 2: return launch_partial<D, 2, false>(a, st);
-      case 3: return launch_partial<D, 3, false>(a, st);
+      case 1: return launch_bits<D, 1, false>(a, st);
+      case 2: return launch_bits<D, 2, false>(a, st);
+      case 3: return launch_bits<D, 3, false>(a, st);
     }
   }
   return hipErrorInvalidValue;

@@ -87,6 +87,31 @@ __device__ __forceinline__ float group_min(float x) {
   return x;
 }
 
+// DPP lane moves inside a 16-lane row (VALU only, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
+
+// Sum over aligned groups of N in {8, 16, 32} lanes, every lane receiving
+// the total.  After the quad sums, a mirror pairs each lane with one in the
+// other half of its 8 (then 16) lanes.
+template <int N>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group of 8, 16 or 32 lanes");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += xor_lane<16>(x);
+  return x;
+}
+
 // One cross-lane butterfly stage of the Walsh-Hadamard transform: element i
 // of this lane pairs with element i of lane (lane ^ MASK).  The lane with the
 // MASK bit clear holds the lower index a and keeps a + b; its partner keeps

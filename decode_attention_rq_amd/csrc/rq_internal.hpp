@@ -53,8 +53,7 @@ struct DecodeArgs {
   int32_t bits[kMaxRes];
   const uint16_t *q;                 // bf16 [L][BH][D]
   int32_t qloop[kMaxSlots];          // slot -> loop index (residual slots first)
-  float *ws;                         // f32 [S][kMaxSlots][BH][2D+2] split records
-  uint32_t *counters;                // [BH] finished splits; zero between calls
+  float *ws;                         // f32 [S][kMaxSlots][BH][2D+2] split records (S > 1)
   float *out;                        // f32 [L][BH][D]
   int32_t bh, cap, n_ctx, n_splits, tps;
   int32_t group, rotate;

@@ -138,11 +138,8 @@ int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
  *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise
  *   out        f32 [L][B][H][d]; rows of loops not in the mask are not written
  *   workspace  device scratch of at least rq_decode_workspace_bytes(layout,
- *              n_ctx, n_splits) bytes, 16-byte aligned.  It must be zero-filled
- *              before its first use; every call leaves it in a state that the
- *              next call accepts (its leading counters back at zero), so one
- *              workspace serves any number of calls on one stream.  Calls that
- *              may run concurrently need separate workspaces.
+ *              n_ctx, n_splits) bytes, 16-byte aligned; no initialisation
+ *              needed; calls that may run concurrently need separate ones
  * Results agree with an FP64 evaluation of the same definition to within a
  * few 1e-4 of the row's largest output magnitude.
  */

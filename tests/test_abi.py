@@ -163,11 +163,12 @@ def test_decode_only_checks_planes_of_masked_loops(rq):
 
 def test_workspace_size_formula(rq):
     lay = _layout(rq).c()
-    # 256 bytes of counters (4 (b,h), padded), then
     # 2 splits * 4 slots * (2*2) (b,h) * (2*128+2) floats
-    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 2) == 256 + 2 * 4 * 4 * 258 * 4
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 2) == 2 * 4 * 4 * 258 * 4
     # more splits than tokens are clamped to one token per split
-    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 3, 8) == 256 + 3 * 4 * 4 * 258 * 4
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 3, 8) == 3 * 4 * 4 * 258 * 4
+    # one split needs no records (a token 256 bytes)
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 1) == 256
 
 
 @pytest.mark.parametrize("loop,t0,n", [(-1, 0, 4), (3, 0, 4), (0, -1, 4), (0, 0, 0), (0, 62, 4)])
