@@ -34,8 +34,11 @@ def parse():
     p.add_argument("--workload", default="int2-8k")
     p.add_argument("--splits", type=int, default=0, help="token splits (0 = library's choice)")
     p.add_argument("--replicas", type=int, default=2)
-    p.add_argument("--cpu-sample", type=int, default=48, help="(batch, head) pairs the oracle decodes")
+    p.add_argument("--cpu-sample", type=int, default=256, help="(batch, head) pairs the oracle decodes")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16-baseline", action="store_true")
+    p.add_argument("--mode", default="decode", choices=["decode", "copy"],
+                   help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling")
     return p.parse_args()
 
 
@@ -101,8 +104,69 @@ def cpu_baseline(w, n_pairs: int):
             "ms_per_step": step_s * 1e3}
 
 
+def bf16_baseline(w, n, steps, warmup, splits_rq):
+    """The same decode step on a BF16 KV cache (every loop its own BF16 K, V),
+    timed the same way; the comparison the pages normalise against."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+
+    dev = "cuda"
+    lay = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, n, w.rotate, w.bits)
+    reps = []
+    for r in range(2):
+        d = synth.draw_layer(w, seed=w.seed + 17 * r, device=dev)
+        ks = [d["k_loops"][l] for l in range(w.n_loops - 1)] + [d["k_ref"]]
+        vs = [d["v_loops"][l] for l in range(w.n_loops - 1)] + [d["v_ref"]]
+        reps.append((ks, vs, d["q"].contiguous()))
+    splits = rq.rq_decode_splits(lay, n)
+    ws = rq.workspace_for(lay, n, splits, dev)
+    out = torch.empty(w.n_loops, w.batch, w.heads, w.d, device=dev)
+    mask = (1 << w.n_loops) - 1
+
+    def step(i):
+        ks, vs, q = reps[i % 2]
+        rq.rq_bf16_decode_attn(lay, ks, vs, q, mask, n, 1.0 / np.sqrt(w.d), out, ws, splits)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = w.batch * w.heads * n * 2 * w.n_loops * w.d * 2
+    del reps
+    torch.cuda.empty_cache()
+    return {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1), "bytes_per_step": nbytes,
+            "kernel": "rq_bf16_decode_attn: the same split-K kernel over BF16 K/V, one launch per loop"}
+
+
+def copy_probe():
+    """A plain device copy of 1 GiB, five times: its rocprofv3 FETCH_SIZE /
+    WRITE_SIZE per dispatch against the known 1 GiB gives the counter scale."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}))
+
+
 def main():
     args = parse()
+    if args.mode == "copy":
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1 (the per-(batch, head) "
               "work shards across GPUs without exchange, but no multi-GPU path is built)",
@@ -162,8 +226,8 @@ def main():
     tokens_per_s = w.batch / (ms_per_step / 1e3)
 
     per_tok = algorithmic_bytes_per_token(w)
-    alg_bytes = w.batch * w.heads * n * per_tok + 2 * w.n_loops * w.batch * w.heads * w.d * 2 \
-        + w.n_loops * w.batch * w.heads * w.d * 4
+    rows = w.n_loops * w.batch * w.heads
+    alg_bytes = w.batch * w.heads * n * per_tok + rows * w.d * 2 + rows * w.d * 4   # cache + q + out
     achieved = alg_bytes / (launch_ms.mean() / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
@@ -187,6 +251,15 @@ def main():
         "roofline": roofline,
         "wall_s": round(wall, 3),
     }
+    if not args.no_bf16_baseline:
+        del reps
+        torch.cuda.empty_cache()
+        bf = bf16_baseline(w, n, args.steps, args.warmup, splits)
+        res["bf16_baseline"] = bf
+        res["speedup_vs_bf16"] = round(tokens_per_s / bf["value"], 3)
+        # KV bytes per (batch, head, token): BF16 for every loop vs this layout;
+        # at equal KV memory the feasible batch grows by their ratio
+        res["batch_gain_at_equal_kv_memory"] = round(2 * w.n_loops * w.d * 2 / per_tok, 3)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample, w.batch * w.heads))
     print(json.dumps(res), flush=True)

@@ -49,6 +49,10 @@ _lib.rq_decode_attn.restype = C.c_int
 _lib.rq_decode_attn.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), C.c_void_p, C.c_uint32,
                                 C.c_int32, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                 C.c_size_t, C.c_void_p]
+_lib.rq_bf16_decode_attn.restype = C.c_int
+_lib.rq_bf16_decode_attn.argtypes = [_P(rq_layout), _P(C.c_void_p), _P(C.c_void_p), C.c_void_p,
+                                     C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.rq_reconstruct.restype = C.c_int
 _lib.rq_reconstruct.argtypes = [_P(rq_layout), _P(rq_cache), C.c_int32, C.c_int32, C.c_int32,
                                 C.c_void_p, C.c_void_p]
@@ -162,6 +166,18 @@ def rq_decode_attn(layout: Layout, k: Cache, v: Cache, q: torch.Tensor, loop_mas
     _check(_lib.rq_decode_attn(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(q), int(loop_mask),
                                int(n_ctx), float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops: Sequence[torch.Tensor],
+                        q: torch.Tensor, loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
+                        workspace: torch.Tensor, n_splits: int = 0, stream=None) -> None:
+    """BF16-KV baseline: k_loops / v_loops are n_loops bf16 [B, H, cap, d] tensors."""
+    lay = layout.c()
+    kp = (C.c_void_p * layout.n_loops)(*[_ptr(t) for t in k_loops])
+    vp = (C.c_void_p * layout.n_loops)(*[_ptr(t) for t in v_loops])
+    _check(_lib.rq_bf16_decode_attn(C.byref(lay), kp, vp, _ptr(q), int(loop_mask), int(n_ctx),
+                                    float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def rq_reconstruct(layout: Layout, c: Cache, loop: int, t0: int, n: int, out: torch.Tensor,

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "rq.h"
+#include "rq_baseline.h"
 #include "rq_internal.hpp"
 
 namespace {
@@ -228,6 +229,56 @@ rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *
     want_ref = false;
     done += cnt;
   } while (done < nres);
+  return RQ_OK;
+}
+
+rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *const *v_loops,
+                              const void *q, uint32_t loop_mask, int32_t n_ctx, float sm_scale,
+                              int32_t n_splits, float *out, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+  rq_status st = check_layout(L);
+  if (st != RQ_OK) return st;
+  if (k_loops == nullptr || v_loops == nullptr) return RQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return RQ_ERR_INVALID_ARG;
+  if (loop_mask == 0) return RQ_ERR_INVALID_ARG;
+  if (L->n_loops < 32 && (loop_mask >> L->n_loops) != 0) return RQ_ERR_INVALID_ARG;
+  if (n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
+  if (n_splits < 0 || n_splits > n_ctx) return RQ_ERR_INVALID_ARG;
+  for (int l = 0; l < L->n_loops; ++l)
+    if (((loop_mask >> l) & 1u) && (!aligned16(k_loops[l]) || !aligned16(v_loops[l])))
+      return RQ_ERR_INVALID_ARG;
+  int S = n_splits;
+  if (S == 0) {
+    S = rq_decode_splits(L, n_ctx);
+    if (S <= 0) return RQ_ERR_DEVICE;
+  }
+  if (workspace_bytes < workspace_for(L, S)) return RQ_ERR_WORKSPACE;
+  const int tps = (n_ctx + S - 1) / S;
+  S = (n_ctx + tps - 1) / tps;
+  rq::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.ws = static_cast<float *>(workspace);
+  a.out = out;
+  a.q = static_cast<const uint16_t *>(q);
+  a.bh = L->batch * L->n_heads;
+  a.cap = L->capacity;
+  a.n_ctx = n_ctx;
+  a.n_splits = S;
+  a.tps = tps;
+  a.group = 32;
+  a.qscale = sm_scale * 1.4426950408889634f;
+  a.rot_c = 1.0f;
+  (void)hipGetLastError();
+  // every loop attends over its own BF16 cache: the reference-only kernel
+  for (int l = 0; l < L->n_loops; ++l) {
+    if (!((loop_mask >> l) & 1u)) continue;
+    a.kref = static_cast<const uint16_t *>(k_loops[l]);
+    a.vref = static_cast<const uint16_t *>(v_loops[l]);
+    a.qloop[0] = l;
+    if (rq::launch_decode(a, L->head_dim, 0, true, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+      return RQ_ERR_DEVICE;
+  }
   return RQ_OK;
 }
 

@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rq.h", "rq_baseline.h")]
 
 
 @pytest.fixture(scope="module")
@@ -19,15 +19,16 @@ def rq():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["rq_encode", "rq_decode_workspace_bytes", "rq_decode_splits",
-                            "rq_decode_attn", "rq_reconstruct", "rq_status_string"])
+                            "rq_decode_attn", "rq_reconstruct", "rq_status_string",
+                            "rq_bf16_decode_attn"])
 
 
 def test_library_exports_every_declared_symbol(rq):
@@ -177,3 +178,16 @@ def test_reconstruct_validation(rq, loop, t0, n):
     c = _cache(rq)
     assert rq._lib.rq_reconstruct(C.byref(L), C.byref(c), loop, t0, n, FAKE, None) == INVALID
     assert rq._lib.rq_reconstruct(C.byref(L), C.byref(c), 0, 0, 4, FAKE + 8, None) == INVALID
+
+
+def test_bf16_baseline_validation(rq):
+    lay = _layout(rq).c()
+    planes = (C.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    bad = (C.c_void_p * 4)(FAKE, 0, FAKE, FAKE)
+    f = rq._lib.rq_bf16_decode_attn
+    assert f(C.byref(lay), planes, planes, FAKE, 0, 32, 0.1, 2, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(C.byref(lay), planes, bad, FAKE, 0b0010, 32, 0.1, 2, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(C.byref(lay), None, planes, FAKE, 1, 32, 0.1, 2, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(C.byref(lay), planes, planes, FAKE, 1, 65, 0.1, 2, FAKE, FAKE, 1 << 30, None) == INVALID
+    # loop 1's null plane is not looked at when loop 1 is not in the mask
+    assert f(C.byref(lay), planes, bad, FAKE, 0b1101, 32, 0.1, 2, FAKE, FAKE, 1, None) == WORKSPACE
