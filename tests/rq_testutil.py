@@ -64,8 +64,9 @@ class Case:
             sel = lambda t: t
         else:
             B, H = len(bh_list), 1
-            bi = torch.tensor([b for b, _ in bh_list])
-            hi = torch.tensor([h for _, h in bh_list])
+            dev = self.data["k_ref"].device
+            bi = torch.tensor([b for b, _ in bh_list], device=dev)
+            hi = torch.tensor([h for _, h in bh_list], device=dev)
 
             def sel(t, ax=0):
                 # t has batch at axis ax and heads at ax+1
@@ -80,9 +81,9 @@ class Case:
             kr, vr, kl, vl, q = (self.data["k_ref"], self.data["v_ref"], self.data["k_loops"],
                                  self.data["v_loops"], self.data["q"])
         else:
-            kr, vr = sel(self.data["k_ref"].cpu()), sel(self.data["v_ref"].cpu())
-            kl, vl = sel(self.data["k_loops"].cpu(), 1), sel(self.data["v_loops"].cpu(), 1)
-            q = sel(self.data["q"].cpu(), 1)
+            kr, vr = sel(self.data["k_ref"]).cpu(), sel(self.data["v_ref"]).cpu()
+            kl, vl = sel(self.data["k_loops"], 1).cpu(), sel(self.data["v_loops"], 1).cpu()
+            q = sel(self.data["q"], 1).cpu()
         lay["heads"] = H
         kp.ref[:] = bf16_bits(kr)
         vp.ref[:] = bf16_bits(vr)
