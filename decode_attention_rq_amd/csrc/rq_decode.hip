@@ -37,6 +37,14 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// First product of a dot chain: the three-operand v_dot2_f32_bf16 with an
+// inline zero accumulator (the builtin would zero a register first).
+__device__ __forceinline__ float dot2bf0(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
@@ -170,6 +178,11 @@ __device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]
   }
 }
 
+// The low / high FP16 half of a 32-bit word, for use as an fma operand
+// (v_fma_mix_f32 reads it in place).
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
+
 // Load from a uniform base plus a 32-bit byte offset (global_load with an
 // SGPR base and a 32-bit VGPR offset; no 64-bit address arithmetic per lane).
 template <typename T>
@@ -202,6 +215,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   const int t_begin = split * a.tps;
   const int t_end = min(t_begin + a.tps, a.n_ctx);
   const int G = D / a.group;
+  const int gshift = __builtin_ctz((unsigned)G);     // meta words per token = 2^gshift
   const int k = j / (a.group / 8);
 
   // Plane bases of this (batch, head): uniform, so they live in SGPRs and
@@ -225,8 +239,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 
   // ---- prologue: queries of every loop in the pass -------------------------
   // Reference dots use the BF16 query pairs as stored; residual dots use
-  // q' = H_n q * scale * log2(e) in FP32, each element pre-multiplied by
-  // 2^(24 - pos) for its code's position in code_halves.
+  // q' = H_n q in FP32, each element pre-multiplied by 2^(24 - pos) for its
+  // code's position in code_halves.  Scores are scaled by sm_scale*log2(e)
+  // after the row sum.
   uint32_t qb[NS][4];
   float qr[NRA][8], sig[NRA];
 #pragma unroll
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     const bool int4 = (B4 >> i) & 1;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const float v = f[p] * (a.rot_c * a.qscale);
+      const float v = f[p] * a.rot_c;
       tot += v;
       const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
       qr[i][p] = v * (float)(1 << (24 - pos));
@@ -281,8 +296,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           T.kc[u][i] = ldg<uint16_t>(kc[i], t * (D / 4) + 2 * j);
           T.vc[u][i] = ldg<uint16_t>(vc[i], t * (D / 4) + 2 * j);
         }
-        T.km[u][i] = ldg<uint32_t>(km[i], (t * G + k) * 4);
-        T.vm[u][i] = ldg<uint32_t>(vm[i], (t * G + k) * 4);
+        T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
+        T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
         T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
         T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
       }
@@ -294,10 +309,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     float sc[TR][NS];
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
+      // Partial scores of this lane's 8 dims, in units of 1/qscale: the
+      // reference dots are exact BF16 products; the residual dots and their
+      // offset terms carry q' without the softmax scale, and the FP16 scale,
+      // zero and LS coefficient enter v_fma_mix_f32 as stored.
       float part[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        float dy = dot2bf(qb[s][0], T.yk[u].x, 0.0f);
+        float dy = dot2bf0(qb[s][0], T.yk[u].x);
         dy = dot2bf(qb[s][1], T.yk[u].y, dy);
         dy = dot2bf(qb[s][2], T.yk[u].z, dy);
         part[s] = dot2bf(qb[s][3], T.yk[u].w, dy);
@@ -306,15 +325,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       for (int i = 0; i < NR; ++i) {
         const float dc = ((B4 >> i) & 1) ? code_dot<true>(T.kc[u][i], qr[i], 0.0f)
                                          : code_dot<false>(T.kc[u][i], qr[i], 0.0f);
-        const float sK = f16_to_f32(T.km[u][i] & 0xffffu), zK = f16_to_f32(T.km[u][i] >> 16);
-        const float aK = f16_to_f32(T.ka[u][i]);
-        part[i] = __builtin_fmaf(aK * a.qscale, part[i], __builtin_fmaf(sK, dc, zK * sig[i]));
+        const uint32_t mw = T.km[u][i];
+        const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
+        part[i] = __builtin_fmaf(h_lo(T.ka[u][i]), part[i], t);
       }
-      if (REF) part[NR] *= a.qscale;
       const bool valid = base + u * ROWS + r < t_end;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const float tot = group_sum_dpp<LANES>(part[s]);
+        const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
         sc[u][s] = valid ? tot : -INFINITY;
       }
     }
@@ -349,13 +367,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         const float pr = fexp2(sc[u][s] - m[s]);
         l[s] += pr;
         if (s < NR) {
-          const float sV = f16_to_f32(T.vm[u][s] & 0xffffu), zV = f16_to_f32(T.vm[u][s] >> 16);
-          const float wr = pr * f16_to_f32(T.va[u][s]);
-          zacc[s] = __builtin_fmaf(pr, zV, zacc[s]);
+          const uint32_t mw = T.vm[u][s];
+          const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
+          const float wq = __builtin_fmaf(h_lo(mw), pr, 0.0f);
+          zacc[s] = __builtin_fmaf(h_hi(mw), pr, zacc[s]);
 #pragma unroll
           for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
-          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], pr * sV, ores[s]);
-          else code_axpy<false>(T.vc[u][s], pr * sV, ores[s]);
+          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], wq, ores[s]);
+          else code_axpy<false>(T.vc[u][s], wq, ores[s]);
         } else {
 #pragma unroll
           for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
@@ -365,18 +384,23 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   };
 
   // ---- token tiles: two tile buffers, the next one loading while the other
-  // is processed ------------------------------------------------------------
+  // is processed.  The next tile is always loaded (its token indices clamped
+  // into the split), so the loads are straight-line code and the wait before
+  // processing a tile covers only that tile's loads.
   int base = t_begin + wave * TILE;
-  Tile<TR, NRA> ta, tb;
-  if (base < t_end) load(ta, base);
-  while (base < t_end) {
-    if (base + STEP < t_end) load(tb, base + STEP);
-    process(ta, base);
-    base += STEP;
-    if (base >= t_end) break;
-    if (base + STEP < t_end) load(ta, base + STEP);
-    process(tb, base);
-    base += STEP;
+  if (base < t_end) {
+    Tile<TR, NRA> ta, tb;
+    load(ta, base);
+    while (true) {
+      load(tb, base + STEP);
+      process(ta, base);
+      base += STEP;
+      if (base >= t_end) break;
+      load(ta, base + STEP);
+      process(tb, base);
+      base += STEP;
+      if (base >= t_end) break;
+    }
   }
 
   // undo the 2^(pos-24) factors of the value codes, add the offsets' share
