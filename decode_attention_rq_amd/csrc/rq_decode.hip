@@ -25,6 +25,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "rq_device.hpp"
 #include "rq_internal.hpp"
 
@@ -35,6 +37,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Value of x in lane 4*(lane/4) + S (DPP quad_perm broadcast).
+__device__ __forceinline__ float quad_bcast(float x, int s) {
+  switch (s) {
+    case 0: return dpp<0x00>(x);
+    case 1: return dpp<0x55>(x);
+    case 2: return dpp<0xAA>(x);
+    default: return dpp<0xFF>(x);
+  }
 }
 
 // First product of a dot chain: the three-operand v_dot2_f32_bf16 with an
@@ -48,16 +60,18 @@ __device__ __forceinline__ float dot2bf0(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
-// Merge the online-softmax states of rows at lane distance MASK.
+// Merge the online-softmax states of rows at lane distance MASK.  The lane's
+// running sum l_own belongs to loop slot `own` (lane index mod 4).
 template <int MASK, int NS, int NR>
-__device__ __forceinline__ void merge_rows(float (&m)[NS], float (&l)[NS], float (&oref)[NS][8],
+__device__ __forceinline__ void merge_rows(float (&m)[NS], float &l_own, int own, float (&oref)[NS][8],
                                            float (&ores)[NR > 0 ? NR : 1][8]) {
+  const float lo = xor_lane<MASK>(l_own);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const float mo = xor_lane<MASK>(m[s]);
     const float M = fmaxf(m[s], mo);
     const float fa = fexp2(m[s] - M), fb = fexp2(mo - M);
-    l[s] = l[s] * fa + xor_lane<MASK>(l[s]) * fb;
+    if (own == s) l_own = l_own * fa + lo * fb;
 #pragma unroll
     for (int p = 0; p < 8; ++p) oref[s][p] = oref[s][p] * fa + xor_lane<MASK>(oref[s][p]) * fb;
     if (s < NR) {
@@ -267,10 +281,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     sig[i] = tot;
   }
 
-  float m[NS], l[NS], oref[NS][8], ores[NRA][8], zacc[NRA];
+  // Softmax state: m per loop slot (uniform across a row); the running sum of
+  // loop slot own = j % 4 only, kept by the lanes that compute that slot's
+  // exponentials (lane j of a quad computes slot j's weight; the quad shares
+  // the four weights through DPP).
+  const int own = j & 3;
+  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    m[s] = -FLT_MAX; l[s] = 0.0f;
+    m[s] = -FLT_MAX;
 #pragma unroll
     for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
   }
@@ -304,7 +323,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  auto process = [&](const Tile<TR, NRA> &T, int base) {
+  auto process = [&](const Tile<TR, NRA> &T, int base, auto full_tile) {
+    constexpr bool FULL = decltype(full_tile)::value;
     // scores (log2 units)
     float sc[TR][NS];
 #pragma unroll
@@ -329,11 +349,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
         part[i] = __builtin_fmaf(h_lo(T.ka[u][i]), part[i], t);
       }
-      const bool valid = base + u * ROWS + r < t_end;
+      const bool valid = FULL || base + u * ROWS + r < t_end;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
-        sc[u][s] = valid ? tot : -INFINITY;
+        sc[u][s] = FULL ? tot : (valid ? tot : -INFINITY);
       }
     }
 
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       if (mt > m[s] + kRescaleSlack) {
         const float f = fexp2(m[s] - mt);
         m[s] = mt;
-        l[s] *= f;
+        if (own == s) l_own *= f;
 #pragma unroll
         for (int p = 0; p < 8; ++p) oref[s][p] *= f;
         if (s < NR) {
@@ -362,10 +382,21 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     for (int u = 0; u < TR; ++u) {
       const float y[8] = {bf16lo(T.yv[u].x), bf16hi(T.yv[u].x), bf16lo(T.yv[u].y), bf16hi(T.yv[u].y),
                           bf16lo(T.yv[u].z), bf16hi(T.yv[u].z), bf16lo(T.yv[u].w), bf16hi(T.yv[u].w)};
+      // one exponential per lane (slot own), shared across the quad
+      float x = sc[u][0] - m[0];
+#pragma unroll
+      for (int s = 1; s < NS; ++s) {
+        const float xs = sc[u][s] - m[s];
+        x = own == s ? xs : x;
+      }
+      const float p_own = fexp2(x);
+      l_own += p_own;
+      float pq[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pq[s] = quad_bcast(p_own, s);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const float pr = fexp2(sc[u][s] - m[s]);
-        l[s] += pr;
+        const float pr = pq[s];
         if (s < NR) {
           const uint32_t mw = T.vm[u][s];
           const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
@@ -393,11 +424,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     load(ta, base);
     while (true) {
       load(tb, base + STEP);
-      process(ta, base);
+      if (base + TILE <= t_end) process(ta, base, std::true_type{});
+      else process(ta, base, std::false_type{});
       base += STEP;
       if (base >= t_end) break;
       load(ta, base + STEP);
-      process(tb, base);
+      if (base + TILE <= t_end) process(tb, base, std::true_type{});
+      else process(tb, base, std::false_type{});
       base += STEP;
       if (base >= t_end) break;
     }
@@ -415,15 +448,16 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   }
 
   // ---- merge rows, then waves -----------------------------------------------
-  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l, oref, ores);
-  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l, oref, ores);
-  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l, oref, ores);
+  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l_own, own, oref, ores);
 
   __shared__ float sm[W][NS][REC];
   if (r == 0) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (j == 0) { sm[wave][s][0] = m[s]; sm[wave][s][1] = l[s]; }
+      if (j == 0) sm[wave][s][0] = m[s];
+      if (j == s) sm[wave][s][1] = l_own;
 #pragma unroll
       for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
       if (s < NR) {
