@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=127)
+    p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="int2-8k")
     p.add_argument("--splits", type=int, default=0, help="token splits (0 = library's choice)")
@@ -39,7 +39,11 @@ def parse():
     p.add_argument("--no-bf16-baseline", action="store_true")
     p.add_argument("--mode", default="decode", choices=["decode", "copy"],
                    help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling")
-    return p.parse_args()
+    a = p.parse_args()
+    a.steps_given = a.steps is not None
+    if a.steps is None:
+        a.steps = 127
+    return a
 
 
 def algorithmic_bytes_per_token(w) -> int:
@@ -162,6 +166,280 @@ def copy_probe():
     print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}))
 
 
+def layout_of(w, batch, cap):
+    import decode_attention_rq_amd as rq
+    return rq.Layout(w.n_loops, batch, w.heads, w.d, w.g, cap, w.rotate, w.bits)
+
+
+def timed(fn, steps, warmup):
+    """Mean ms per call of fn(i) over `steps` calls after `warmup`, bracketed by
+    device synchronisation (HIP events on the current stream)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def append_bench(args, w):
+    """Mixed-precision 8k workload: rq_encode prefill of 8192 tokens (timed
+    once), then `steps` append steps, each rq_encode of one new token per
+    (batch, head, loop) plus rq_decode_attn over the n+1 tokens.  The
+    reference slots (the final loop's own KV write) are in place beforehand."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+    from oracle.storage import layout_bytes_per_token
+
+    dev = "cuda"
+    n0, steps = w.n_ctx, w.steps
+    cap = n0 + steps
+    lay = layout_of(w, w.batch, cap)
+    data = synth.draw_layer(w, n=cap, device=dev)
+    k, v = rq.Cache(lay, dev), rq.Cache(lay, dev)
+    k.ref.copy_(data["k_ref"])
+    v.ref.copy_(data["v_ref"])
+    kin, vin, q = data["k_loops"], data["v_loops"], data["q"].contiguous()
+    pre_k, pre_v = kin[:, :, :, :n0].contiguous(), vin[:, :, :, :n0].contiguous()
+    step_in = [(kin[:, :, :, t:t + 1].contiguous(), vin[:, :, :, t:t + 1].contiguous()) for t in range(n0, cap)]
+    del data, kin, vin
+    torch.cuda.empty_cache()
+    # prefill: one timed call (after a warm-up encode of the first 64 tokens)
+    rq.rq_encode(lay, k, v, pre_k[:, :, :, :64].contiguous(), pre_v[:, :, :, :64].contiguous(), 0, 64)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    rq.rq_encode(lay, k, v, pre_k, pre_v, 0, n0)
+    e1.record()
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1)
+    res_bits = [b for b in w.bits]
+    enc_bytes_tok = 2 * (w.n_loops * w.d * 2) + 2 * sum(w.d * b // 8 + 4 * (w.d // w.g) + 2 for b in res_bits)
+    pre_bytes = w.batch * w.heads * n0 * enc_bytes_tok
+    del pre_k, pre_v
+    mask = (1 << w.n_loops) - 1
+    out = torch.empty(w.n_loops, w.batch, w.heads, w.d, device=dev)
+    ws = rq.workspace_for(lay, cap, rq.rq_decode_splits(lay, cap), dev)
+    scale = 1.0 / np.sqrt(w.d)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        t = n0 + s_
+        ev[s_][0].record()
+        rq.rq_encode(lay, k, v, step_in[s_][0], step_in[s_][1], t, 1)
+        ev[s_][1].record()
+        rq.rq_decode_attn(lay, k, v, q, mask, t + 1, scale, out, ws, rq.rq_decode_splits(lay, t + 1))
+        ev[s_][2].record()
+    torch.cuda.synchronize()
+    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    per_tok = layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
+    dec_bytes = w.batch * w.heads * (n0 + steps / 2) * per_tok
+    res = {"metric": "decode tokens/s with one-token append per step, mixed INT4/INT2 residual KV, 8k ctx",
+           "value": round(w.batch / (step_ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": steps, "warmup": 0, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: batch {w.batch}, {w.heads} heads, head_dim {w.d}, bits {w.bits} "
+                                  f"+ BF16 reference, g={w.g}, prefill {n0} tokens then {steps} append steps"},
+           "decode_ms_mean": round(float(dec_ms.mean()), 4),
+           "decode_hbm_gbs": round(dec_bytes / (dec_ms.mean() / 1e3) / 1e9, 1),
+           "append_encode_us_mean": round(float(enc_ms.mean()) * 1e3, 2),
+           "prefill_encode": {"ms": round(pre_ms, 3), "tokens": w.batch * w.heads * n0,
+                              "algorithmic_bytes": pre_bytes,
+                              "hbm_gbs": round(pre_bytes / (pre_ms / 1e3) / 1e9, 1),
+                              "frac_of_peak": round(pre_bytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del k, v, step_in
+    torch.cuda.empty_cache()
+    if not args.no_bf16_baseline:
+        # BF16 decode over the same growing context (no encode needed)
+        d2 = synth.draw_layer(w, n=cap, device=dev)
+        ks = [d2["k_loops"][l] for l in range(w.n_loops - 1)] + [d2["k_ref"]]
+        vs = [d2["v_loops"][l] for l in range(w.n_loops - 1)] + [d2["v_ref"]]
+        lay_b = layout_of(w, w.batch, cap)
+        ms = timed(lambda i: rq.rq_bf16_decode_attn(lay_b, ks, vs, d2["q"], mask, n0 + i + 1, scale, out, ws,
+                                                    rq.rq_decode_splits(lay_b, n0 + i + 1)), steps, 3)
+        res["bf16_baseline"] = {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4)}
+        res["speedup_vs_bf16"] = round(res["value"] / res["bf16_baseline"]["value"], 3)
+    return res
+
+
+def layers_bench(args, w):
+    """32k context over 24 layers: one step = 24 sequential rq_decode_attn
+    calls, each layer with its own caches and queries."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+    from oracle.storage import layout_bytes_per_token
+
+    dev, n = "cuda", w.n_ctx
+    lay = layout_of(w, w.batch, n)
+    layers = []
+    for li in range(w.layers):
+        d = synth.draw_layer(w, seed=w.seed * 100 + li, device=dev)
+        k, v = rq.Cache(lay, dev, zero=False), rq.Cache(lay, dev, zero=False)
+        k.ref.copy_(d["k_ref"])
+        v.ref.copy_(d["v_ref"])
+        rq.rq_encode(lay, k, v, d["k_loops"], d["v_loops"], 0, n)
+        layers.append((k, v, d["q"].contiguous()))
+        del d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    mask = (1 << w.n_loops) - 1
+    splits = rq.rq_decode_splits(lay, n)
+    ws = rq.workspace_for(lay, n, splits, dev)
+    out = torch.empty(w.n_loops, w.batch, w.heads, w.d, device=dev)
+    scale = 1.0 / np.sqrt(w.d)
+
+    def step(i):
+        for k, v, q in layers:
+            rq.rq_decode_attn(lay, k, v, q, mask, n, scale, out, ws, splits)
+
+    steps = args.steps if args.steps_given else 20
+    ms = timed(step, steps, 3)
+    nbytes = w.layers * w.batch * w.heads * n * layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
+    res = {"metric": "decode tokens/s + achieved HBM GB/s, INT2 residual KV, 32k ctx, 24 layers",
+           "value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": 3, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: {w.layers} layers x (batch {w.batch}, {w.heads} heads, head_dim {w.d}, "
+                                  f"{w.n_loops} loops, bits {w.bits} + BF16 reference), {n}-token context",
+                      "splits": splits},
+           "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes}
+    del layers
+    torch.cuda.empty_cache()
+    if not args.no_bf16_baseline:
+        bl = []
+        for li in range(w.layers):
+            d = synth.draw_layer(w, seed=w.seed * 100 + li, device=dev)
+            ks = [d["k_loops"][l].clone() for l in range(w.n_loops - 1)] + [d["k_ref"]]
+            vs = [d["v_loops"][l].clone() for l in range(w.n_loops - 1)] + [d["v_ref"]]
+            bl.append((ks, vs, d["q"].contiguous()))
+            del d
+            torch.cuda.empty_cache()
+
+        def bstep(i):
+            for ks, vs, q in bl:
+                rq.rq_bf16_decode_attn(lay, ks, vs, q, mask, n, scale, out, ws, splits)
+
+        bms = timed(bstep, max(3, steps // 2), 2)
+        bbytes = w.layers * w.batch * w.heads * n * 2 * w.n_loops * w.d * 2
+        res["bf16_baseline"] = {"value": round(w.batch / (bms / 1e3), 1), "unit": "tokens/s",
+                                "ms_per_step": round(bms, 4), "hbm_gbs": round(bbytes / (bms / 1e3) / 1e9, 1)}
+        res["speedup_vs_bf16"] = round(res["value"] / res["bf16_baseline"]["value"], 3)
+        del bl
+        torch.cuda.empty_cache()
+    return res
+
+
+def peak_batch_bench(args, w, budget=250e9):
+    """8k context, 24 layers: the largest batch whose KV cache fits the budget,
+    for this layout and for BF16 KV, and decode tokens/s over a batch sweep up
+    to each maximum (batch-prefix views of one allocation)."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+    from oracle.storage import layout_bytes_per_token
+
+    dev, n, L = "cuda", w.n_ctx, w.layers
+    rq_per_b = L * w.heads * n * layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
+    bf_per_b = L * w.heads * n * 2 * w.n_loops * w.d * 2
+    bmax_rq, bmax_bf = int(budget // rq_per_b), int(budget // bf_per_b)
+    mask = (1 << w.n_loops) - 1
+    scale = 1.0 / np.sqrt(w.d)
+    steps = args.steps if args.steps_given else 10
+
+    def sweep(bmax):
+        bs = [b for b in (1, 2, 4, 8, 16, 32, 64, 128) if b < bmax] + [bmax]
+        return bs
+
+    # ---- ResidualQuant caches at the maximum batch, encoded chunk by chunk
+    lay_max = layout_of(w, bmax_rq, n)
+    layers = [(rq.Cache(lay_max, dev, zero=False), rq.Cache(lay_max, dev, zero=False)) for _ in range(L)]
+    chunk = 8
+    for b0 in range(0, bmax_rq, chunk):
+        b1 = min(bmax_rq, b0 + chunk)
+        d = synth.draw_layer(w, seed=w.seed * 1000 + b0, batch=b1 - b0, device=dev)
+        lay_c = layout_of(w, b1 - b0, n)
+        for k, v in layers:
+            kc, vc = k.batch_view(b0, b1, lay_c), v.batch_view(b0, b1, lay_c)
+            kc.ref.copy_(d["k_ref"])
+            vc.ref.copy_(d["v_ref"])
+            rq.rq_encode(lay_c, kc, vc, d["k_loops"], d["v_loops"], 0, n)
+        del d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    qall = synth.draw_queries(synth.generator(w.seed, dev), w.n_loops, bmax_rq, w.heads, w.d)
+    rq_rows = []
+    for B in sweep(bmax_rq):
+        lay_b = layout_of(w, B, n)
+        views = [(k.batch_view(0, B, lay_b), v.batch_view(0, B, lay_b)) for k, v in layers]
+        q = qall[:, :B].contiguous()
+        splits = rq.rq_decode_splits(lay_b, n)
+        ws = rq.workspace_for(lay_b, n, splits, dev)
+        out = torch.empty(w.n_loops, B, w.heads, w.d, device=dev)
+
+        def step(i):
+            for kv_, vv_ in views:
+                rq.rq_decode_attn(lay_b, kv_, vv_, q, mask, n, scale, out, ws, splits)
+
+        ms = timed(step, steps, 2)
+        rq_rows.append({"batch": B, "ms_per_step": round(ms, 3), "tokens_per_s": round(B / (ms / 1e3), 1),
+                        "hbm_gbs": round(B * rq_per_b / (ms / 1e3) / 1e9, 1)})
+    del layers, views
+    torch.cuda.empty_cache()
+    # ---- BF16 caches at their maximum batch (values do not affect timing;
+    # the memory is left as allocated)
+    bf_rows = []
+    if not args.no_bf16_baseline:
+        lay_bf = layout_of(w, bmax_bf, n)
+        bl = [([torch.empty(bmax_bf, w.heads, n, w.d, dtype=torch.bfloat16, device=dev) for _ in range(w.n_loops)],
+               [torch.empty(bmax_bf, w.heads, n, w.d, dtype=torch.bfloat16, device=dev) for _ in range(w.n_loops)])
+              for _ in range(L)]
+        for B in sweep(bmax_bf):
+            lay_b = layout_of(w, B, n)
+            q = qall[:, :B].contiguous()
+            splits = rq.rq_decode_splits(lay_b, n)
+            ws = rq.workspace_for(lay_b, n, splits, dev)
+            out = torch.empty(w.n_loops, B, w.heads, w.d, device=dev)
+            views = [([t[:B] for t in ks], [t[:B] for t in vs]) for ks, vs in bl]
+
+            def bstep(i):
+                for ks, vs in views:
+                    rq.rq_bf16_decode_attn(lay_b, ks, vs, q, mask, n, scale, out, ws, splits)
+
+            ms = timed(bstep, steps, 2)
+            bf_rows.append({"batch": B, "ms_per_step": round(ms, 3), "tokens_per_s": round(B / (ms / 1e3), 1),
+                            "hbm_gbs": round(B * bf_per_b / (ms / 1e3) / 1e9, 1)})
+        del bl, views
+        torch.cuda.empty_cache()
+    peak_rq = max(r["tokens_per_s"] for r in rq_rows)
+    res = {"metric": "peak decode tokens/s and largest feasible batch at 8k ctx, 24 layers, 250 GB KV budget",
+           "value": peak_rq, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 2,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: {L} layers x ({w.heads} heads, head_dim {w.d}, {w.n_loops} loops, "
+                                  f"bits {w.bits} + BF16 reference), {n}-token context, KV budget {budget / 1e9:.0f} GB"},
+           "max_batch": {"residualquant": bmax_rq, "bf16": bmax_bf, "gain": round(bmax_rq / bmax_bf, 3)},
+           "max_pow2_batch": {"residualquant": 2 ** int(np.log2(bmax_rq)), "bf16": 2 ** int(np.log2(bmax_bf))},
+           "kv_bytes_per_batch_entry": {"residualquant": rq_per_b, "bf16": bf_per_b},
+           "sweep_residualquant": rq_rows}
+    if bf_rows:
+        peak_bf = max(r["tokens_per_s"] for r in bf_rows)
+        res["sweep_bf16"] = bf_rows
+        res["peak_gain_vs_bf16"] = round(peak_rq / peak_bf, 3)
+    return res
+
+
 def main():
     args = parse()
     if args.mode == "copy":
@@ -179,6 +457,15 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.workload == "mixed-8k-append":
+        print(json.dumps(append_bench(args, w)), flush=True)
+        return
+    if args.workload == "int2-32k-24l":
+        print(json.dumps(layers_bench(args, w)), flush=True)
+        return
+    if args.workload == "peak-batch-8k":
+        print(json.dumps(peak_batch_bench(args, w)), flush=True)
+        return
     dev = "cuda"
     lay = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, w.n_ctx, w.rotate, w.bits)
     n = w.n_ctx

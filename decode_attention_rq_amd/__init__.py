@@ -100,18 +100,22 @@ class Cache:
     """One side (K or V) of a layer's cache: torch tensors in the plane layout
     of include/rq.h (the library reads and writes them in place)."""
 
-    def __init__(self, layout: Layout, device="cuda", ref: Optional[torch.Tensor] = None):
+    def __init__(self, layout: Layout, device="cuda", ref: Optional[torch.Tensor] = None,
+                 zero: bool = True):
+        """zero=False leaves the planes uninitialised (for callers that write
+        every slot they later read)."""
         L, B, H, d, g, cap = (layout.n_loops, layout.batch, layout.n_heads, layout.head_dim,
                               layout.group, layout.capacity)
+        new = torch.zeros if zero else torch.empty
         self.layout = layout
-        self.ref = ref if ref is not None else torch.zeros(B, H, cap, d, dtype=torch.bfloat16, device=device)
+        self.ref = ref if ref is not None else new(B, H, cap, d, dtype=torch.bfloat16, device=device)
         self.codes: List[torch.Tensor] = [
-            torch.zeros(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device)
+            new(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device)
             for l in range(L - 1)]
         self.meta: List[torch.Tensor] = [
-            torch.zeros(B, H, cap, d // g, 2, dtype=torch.float16, device=device) for _ in range(L - 1)]
+            new(B, H, cap, d // g, 2, dtype=torch.float16, device=device) for _ in range(L - 1)]
         self.alpha: List[torch.Tensor] = [
-            torch.zeros(B, H, cap, dtype=torch.float16, device=device) for _ in range(L - 1)]
+            new(B, H, cap, dtype=torch.float16, device=device) for _ in range(L - 1)]
 
     def c(self) -> rq_cache:
         s = rq_cache()
@@ -121,6 +125,18 @@ class Cache:
             s.meta[l] = self.meta[l].data_ptr()
             s.alpha[l] = self.alpha[l].data_ptr()
         return s
+
+    def batch_view(self, b0: int, b1: int, layout: Layout) -> "Cache":
+        """The same planes restricted to batch entries [b0, b1) (batch is the
+        outermost plane axis, so the view is contiguous), for `layout` with
+        batch = b1 - b0."""
+        v = Cache.__new__(Cache)
+        v.layout = layout
+        v.ref = self.ref[b0:b1]
+        v.codes = [t[b0:b1] for t in self.codes]
+        v.meta = [t[b0:b1] for t in self.meta]
+        v.alpha = [t[b0:b1] for t in self.alpha]
+        return v
 
     def nbytes(self) -> int:
         t = [self.ref] + self.codes + self.meta + self.alpha
