@@ -223,6 +223,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   constexpr int TILE = ROWS * TR;
   constexpr int STEP = W * TILE;
   constexpr int REC = 2 * D + 2;
+  static_assert(W >= NS, "one merging wave per loop slot");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane % LANES, r = lane / LANES;
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -535,12 +536,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, in
   finish_row<D>(a, bh, s, residual, lane, L, o, q);
 }
 
+// Tiles per wave iteration and waves per workgroup.  Four waves (the fewest
+// that give every loop slot its own merging wave) let two workgroups share a
+// compute unit, so one workgroup's merge overlaps the other's streaming.
+constexpr int kTilesPerIter = 2;
+constexpr int kWaves = 4;
+
 template <int D, int NR, bool REF, int B4>
 static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
-  constexpr int TR = 2;
-  constexpr int W = 8;
-  const dim3 grid(a.n_splits, a.bh), block(64 * W);
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, W>), grid, block, 0, st, a);
+  const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
+  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, kTilesPerIter, kWaves>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.bh, NR + (REF ? 1 : 0)), dim3(64), 0, st, a, NR);
@@ -582,6 +587,24 @@ static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipS
     }
   }
   return hipErrorInvalidValue;
+}
+
+template <int D>
+static int blocks_per_cu_d() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves>, 64 * kWaves, 0) != hipSuccess)
+    return -1;
+  return n;
+}
+
+int decode_blocks_per_cu(int head_dim) {
+  switch (head_dim) {
+    case 64: return blocks_per_cu_d<64>();
+    case 128: return blocks_per_cu_d<128>();
+    case 256: return blocks_per_cu_d<256>();
+    default: return -1;
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {

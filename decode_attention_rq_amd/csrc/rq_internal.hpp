@@ -64,5 +64,8 @@ struct DecodeArgs {
 hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
+// Decode workgroups of this head_dim resident per compute unit at once (the
+// occupancy of the main decode kernel), or <= 0 on a HIP error.
+int decode_blocks_per_cu(int head_dim);
 
 }  // namespace rq
