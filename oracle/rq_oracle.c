@@ -23,12 +23,19 @@
  *                                      bit width counts codes, scales, offsets
  *                                      and LS coefficients)
  *     - loop-wise mixed precision: a bit width per loop        (Table 5; Fig. 1 step 5)
+ *   quantized anchor (FP32, bit-exact contract): the final loop itself stored
+ *       at INT4 with its own group size, the residuals taken against its
+ *       dequantized value                (Fig. 3 caption: Ascending [2,2,2,4];
+ *                                          Table 8 caption; Fig. 6 caption)
  *   reconstruct (FP64):  x_hat = a*y + H_n (z + s*q)     (Abstract: the residual
  *                                                          form keeps reconstruction
  *                                                          cheap)
  *   attention (FP64):    softmax(scale * q . x_hat^T) v_hat per loop, one query
- *                        per loop                        (Abstract: decode over the
- *                                                          compressed cache)
+ *                        per loop, optionally followed by recent tokens kept
+ *                        in BF16                         (Abstract: decode over the
+ *                                                          compressed cache;
+ *                                                          Table 10: recent BF16
+ *                                                          tokens)
  *
  * Where the pages leave a step open, the reading taken is stated at the
  * function.  Where floating point decides an integer code, the FP32 steps are
@@ -41,6 +48,8 @@
  *                                        of byte i*bits/8
  *   meta   f16  [B][H][cap][d/g][2]      (scale, zero) per group
  *   alpha  f16  [B][H][cap]
+ * With a quantized anchor the final loop has codes and meta planes of its own
+ * (its bit width and group size) and no ref plane.
  */
 #include <math.h>
 #include <stdint.h>
@@ -153,18 +162,26 @@ float rqo_dot_sum(float *a, int d)
  * ||x - alpha*y||^2 is <x,y>/<y,y> (ResidualQuant page, Fig. 2 shows the
  * residual K2 - alpha2*K1; Fig. 3 right compares with alpha = 1).
  * Reading: <y,y> == 0 gives alpha = 0 (nothing to predict from). */
-float rqo_alpha_f32(const uint16_t *x, const uint16_t *y, int d)
+float rqo_alpha_f32_y(const uint16_t *x, const float *y, int d)
 {
     float num[RQO_MAX_D], den[RQO_MAX_D];
     for (int i = 0; i < d; ++i) {
         float xf = rqo_bf16_to_f32(x[i]);
-        float yf = rqo_bf16_to_f32(y[i]);
-        num[i] = xf * yf;
-        den[i] = yf * yf;
+        num[i] = xf * y[i];
+        den[i] = y[i] * y[i];
     }
     float n = rqo_dot_sum(num, d);
     float s = rqo_dot_sum(den, d);
     return s > 0.0f ? n / s : 0.0f;
+}
+
+/* The same with a BF16 reference (products of two BF16 values are exact). */
+float rqo_alpha_f32(const uint16_t *x, const uint16_t *y, int d)
+{
+    float yf[RQO_MAX_D];
+    for (int i = 0; i < d; ++i)
+        yf[i] = rqo_bf16_to_f32(y[i]);
+    return rqo_alpha_f32_y(x, yf, d);
 }
 
 /* Stored coefficient: one FP16 value per (loop, batch, head, token), for K and
@@ -248,17 +265,11 @@ void rqo_unpack(const uint8_t *packed, int d, int bits, uint8_t *codes)
         codes[i] = (uint8_t)((packed[i / per] >> (bits * (i % per))) & ((1 << bits) - 1));
 }
 
-/* Encode one head_dim vector x of a residual loop against the reference y. */
-void rqo_encode_vector(const uint16_t *x, const uint16_t *y, int d, int g,
-                       int bits, int rotate, uint8_t *packed, uint16_t *meta,
-                       uint16_t *alpha)
+/* Rotate (optionally), canonicalise -0 to +0, quantize every group and pack:
+ * the part of encoding shared by residuals and a quantized anchor. */
+static void rqo_quantize_vector(float *u, int d, int g, int bits, int rotate,
+                                uint8_t *codes, uint8_t *packed, uint16_t *meta)
 {
-    float u[RQO_MAX_D];
-    uint8_t codes[RQO_MAX_D];
-    *alpha = rqo_alpha_bits(x, y, d);
-    float a = rqo_f16_to_f32(*alpha);          /* the stored value is what decode sees */
-    for (int i = 0; i < d; ++i)
-        u[i] = fmaf(-a, rqo_bf16_to_f32(y[i]), rqo_bf16_to_f32(x[i]));
     if (rotate)
         rqo_fwht_f32(u, d);
     for (int i = 0; i < d; ++i)
@@ -266,6 +277,62 @@ void rqo_encode_vector(const uint16_t *x, const uint16_t *y, int d, int g,
     for (int k = 0; k < d / g; ++k)
         rqo_quantize_group(u + k * g, g, bits, codes + k * g, meta + 2 * k, meta + 2 * k + 1);
     rqo_pack(codes, d, bits, packed);
+}
+
+/* Encode one head_dim vector x of a residual loop against an FP32 reference y
+ * (the BF16 final loop, or the dequantized anchor). */
+void rqo_encode_vector_y(const uint16_t *x, const float *y, int d, int g,
+                         int bits, int rotate, uint8_t *packed, uint16_t *meta,
+                         uint16_t *alpha)
+{
+    float u[RQO_MAX_D];
+    uint8_t codes[RQO_MAX_D];
+    *alpha = rqo_f32_to_f16_sat(rqo_alpha_f32_y(x, y, d));
+    float a = rqo_f16_to_f32(*alpha);          /* the stored value is what decode sees */
+    for (int i = 0; i < d; ++i)
+        u[i] = fmaf(-a, y[i], rqo_bf16_to_f32(x[i]));
+    rqo_quantize_vector(u, d, g, bits, rotate, codes, packed, meta);
+}
+
+/* Encode one head_dim vector x of a residual loop against the BF16 reference y. */
+void rqo_encode_vector(const uint16_t *x, const uint16_t *y, int d, int g,
+                       int bits, int rotate, uint8_t *packed, uint16_t *meta,
+                       uint16_t *alpha)
+{
+    float yf[RQO_MAX_D];
+    for (int i = 0; i < d; ++i)
+        yf[i] = rqo_bf16_to_f32(y[i]);
+    rqo_encode_vector_y(x, yf, d, g, bits, rotate, packed, meta, alpha);
+}
+
+/* Quantized anchor.  ResidualQuant page, Fig. 3 caption: the "Ascending"
+ * precision [2,2,2,4] gives the higher precision to the last loop, i.e. the
+ * reference itself is stored at INT4; Table 8 caption: every loop group ends
+ * in one INT4 anchor; Fig. 6 caption: INT4 anchors use group size 32 while
+ * INT2 residuals use 16.  Readings: the anchor is quantized directly (no
+ * reference, no LS coefficient) by the same group quantizer after the same
+ * shared rotation; the earlier loops take their residuals against the
+ * anchor as decode sees it, the dequantized anchor, so that reconstruction
+ * adds back exactly what the encoder subtracted.
+ *
+ * Dequantized value of a code q of a group with stored scale s and offset
+ * z: fmaf(q, s, z) in FP32 (one rounding); un-rotated by the same normalized
+ * Hadamard butterflies (c*H is its own inverse).  Writes the packed codes,
+ * the (scale, zero) pairs and the FP32 dequantized anchor yhat. */
+void rqo_anchor_vector(const uint16_t *y, int d, int g, int bits, int rotate,
+                       uint8_t *packed, uint16_t *meta, float *yhat)
+{
+    float u[RQO_MAX_D];
+    uint8_t codes[RQO_MAX_D];
+    for (int i = 0; i < d; ++i)
+        u[i] = rqo_bf16_to_f32(y[i]);
+    rqo_quantize_vector(u, d, g, bits, rotate, codes, packed, meta);
+    for (int i = 0; i < d; ++i) {
+        int k = i / g;
+        yhat[i] = fmaf((float)codes[i], rqo_f16_to_f32(meta[2 * k]), rqo_f16_to_f32(meta[2 * k + 1]));
+    }
+    if (rotate)
+        rqo_fwht_f32(yhat, d);
 }
 
 /* Encode tokens [t0, t0+n) of residual loops 0..L-2 of every (b, h).
@@ -293,17 +360,46 @@ void rqo_encode(int L, int B, int H, int d, int g, int cap, int rotate,
     }
 }
 
+/* Encode tokens [t0, t0+n) of all L loops with a quantized anchor:
+ *   xin: bf16 [L][B][H][n][d]  (loop L-1 is the anchor's input)
+ *   codes[l], meta[l] for l = 0..L-1 (the anchor's at L-1, group ga, abits
+ *   bits); alpha[l] for l = 0..L-2.  Per (b, h, token) the anchor is encoded
+ *   first and its dequantized value is every residual loop's reference. */
+void rqo_encode_anchored(int L, int B, int H, int d, int g, int ga, int abits,
+                         int cap, int rotate, const int *bits, const uint16_t *xin,
+                         int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha)
+{
+    int G = d / g, Ga = d / ga, nba = d * abits / 8;
+    float yhat[RQO_MAX_D];
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = 0; t < n; ++t) {
+                size_t bh = (size_t)b * H + h;
+                size_t slot = bh * cap + (size_t)(t0 + t);
+                const uint16_t *y = xin + ((((size_t)(L - 1) * B + b) * H + h) * n + t) * d;
+                rqo_anchor_vector(y, d, ga, abits, rotate, codes[L - 1] + slot * nba,
+                                  meta[L - 1] + slot * 2 * Ga, yhat);
+                for (int l = 0; l < L - 1; ++l) {
+                    int nb = d * bits[l] / 8;
+                    const uint16_t *x = xin + ((((size_t)l * B + b) * H + h) * n + t) * d;
+                    rqo_encode_vector_y(x, yhat, d, g, bits[l], rotate, codes[l] + slot * nb,
+                                        meta[l] + slot * 2 * G, alpha[l] + slot);
+                }
+            }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Reconstruction and attention (FP64)                                       */
 /* ------------------------------------------------------------------------ */
 
-/* x_hat = a*y + H_d (z + s*q) / sqrt(d)  (or without the rotation). */
-void rqo_reconstruct_vector(const uint8_t *packed, const uint16_t *meta,
-                            uint16_t alpha, const uint16_t *y, int d, int g,
-                            int bits, int rotate, double *out)
+/* Dequantize a vector in FP64: u = z + s*q per group, then H_d u / sqrt(d)
+ * (exact constant) when rotated.  For a residual this is r_hat; for a
+ * quantized anchor it is the anchor y_hat. */
+void rqo_dequant_f64(const uint8_t *packed, const uint16_t *meta, int d, int g,
+                     int bits, int rotate, double *out)
 {
     uint8_t codes[RQO_MAX_D];
-    double u[RQO_MAX_D];
+    double *u = out;
     rqo_unpack(packed, d, bits, codes);
     for (int i = 0; i < d; ++i) {
         int k = i / g;
@@ -323,9 +419,29 @@ void rqo_reconstruct_vector(const uint8_t *packed, const uint16_t *meta,
         for (int i = 0; i < d; ++i)
             u[i] *= c;
     }
+}
+
+/* x_hat = a*y + H_d (z + s*q) / sqrt(d)  (or without the rotation), y in FP64. */
+void rqo_reconstruct_vector_y(const uint8_t *packed, const uint16_t *meta,
+                              uint16_t alpha, const double *y, int d, int g,
+                              int bits, int rotate, double *out)
+{
+    double u[RQO_MAX_D];
+    rqo_dequant_f64(packed, meta, d, g, bits, rotate, u);
     double a = rqo_f16_to_f32(alpha);
     for (int i = 0; i < d; ++i)
-        out[i] = a * (double)rqo_bf16_to_f32(y[i]) + u[i];
+        out[i] = a * y[i] + u[i];
+}
+
+/* The same against the BF16 reference y. */
+void rqo_reconstruct_vector(const uint8_t *packed, const uint16_t *meta,
+                            uint16_t alpha, const uint16_t *y, int d, int g,
+                            int bits, int rotate, double *out)
+{
+    double yd[RQO_MAX_D];
+    for (int i = 0; i < d; ++i)
+        yd[i] = rqo_bf16_to_f32(y[i]);
+    rqo_reconstruct_vector_y(packed, meta, alpha, yd, d, g, bits, rotate, out);
 }
 
 /* Reconstruct tokens [t0, t0+n) of residual loop `loop` for every (b, h):
@@ -343,6 +459,31 @@ void rqo_reconstruct(int B, int H, int d, int g, int cap, int rotate, int bits,
                 rqo_reconstruct_vector(codes + slot * nb, meta + slot * 2 * G,
                                        alpha[slot], ref + slot * d, d, g, bits,
                                        rotate, out + (((size_t)b * H + h) * n + t) * d);
+            }
+}
+
+/* Reconstruct tokens [t0, t0+n) of loop `loop` against a quantized anchor
+ * (anchor planes ac/am, group ga, abits bits): the dequantized anchor for
+ * loop L-1 (pass loop = -1 and NULL residual planes), a*y_hat + r_hat for a
+ * residual loop.  out is float64 [B][H][n][d]. */
+void rqo_reconstruct_anchored(int B, int H, int d, int g, int ga, int abits, int cap,
+                              int rotate, int bits, const uint8_t *ac, const uint16_t *am,
+                              const uint8_t *codes, const uint16_t *meta,
+                              const uint16_t *alpha, int loop, int t0, int n, double *out)
+{
+    int G = d / g, nb = d * bits / 8, Ga = d / ga, nba = d * abits / 8;
+    double y[RQO_MAX_D];
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = 0; t < n; ++t) {
+                size_t slot = ((size_t)b * H + h) * cap + (size_t)(t0 + t);
+                double *o = out + (((size_t)b * H + h) * n + t) * d;
+                rqo_dequant_f64(ac + slot * nba, am + slot * 2 * Ga, d, ga, abits, rotate, y);
+                if (loop < 0)
+                    memcpy(o, y, sizeof(double) * (size_t)d);
+                else
+                    rqo_reconstruct_vector_y(codes + slot * nb, meta + slot * 2 * G, alpha[slot],
+                                             y, d, g, bits, rotate, o);
             }
 }
 
@@ -375,10 +516,69 @@ void rqo_attention(const double *q, const double *k, const double *v, int n,
 }
 
 /* One decode row: attention of loop `loop`'s query of (b, h) over tokens
- * [0, n_ctx) of that loop's cache, reconstructed in FP64.  The final loop
- * (loop == L-1) attends over the BF16 reference itself.
- *   kref/vref: bf16 [B][H][cap][d]; kc/vc etc.: the loop's planes (ignored for
- *   the final loop); q: bf16 [L][B][H][d]; out: float64 [d]. */
+ * [0, n_ctx) of that loop's cache, reconstructed in FP64, followed by n_tail
+ * tokens kept in BF16 (the loop's own K/V rows, tk/tv bf16 [n_tail][d]).
+ * The final loop (loop == L-1) attends over the reference itself: the BF16
+ * plane when abits == 0, else the dequantized anchor (planes kac/kam, vac/vam,
+ * group ga, abits bits).  kc/km/ka etc. are loop `loop`'s residual planes
+ * (ignored for the final loop); q: bf16 [L][B][H][d]; out: float64 [d].
+ * Reading for the tail: the current token's earlier-loop K/V cannot be
+ * encoded before its final loop has run, so recent tokens stay in BF16 and
+ * are attended as they are (RQ page, Table 10: "Recent 64" BF16 tokens). */
+void rqo_decode_row_ex(int L, int B, int H, int d, int g, int cap, int rotate,
+                       int bits, const uint16_t *kref, const uint8_t *kc,
+                       const uint16_t *km, const uint16_t *ka,
+                       const uint16_t *vref, const uint8_t *vc,
+                       const uint16_t *vm, const uint16_t *va,
+                       int ga, int abits, const uint8_t *kac, const uint16_t *kam,
+                       const uint8_t *vac, const uint16_t *vam,
+                       const uint16_t *tk, const uint16_t *tv, int n_tail,
+                       const uint16_t *q, int loop, int b, int h, int n_ctx,
+                       double scale, double *out)
+{
+    size_t bh = (size_t)b * H + h;
+    int n_all = n_ctx + n_tail;
+    double *kh = (double *)malloc(sizeof(double) * (size_t)n_all * d);
+    double *vh = (double *)malloc(sizeof(double) * (size_t)n_all * d);
+    double qd[RQO_MAX_D], yk[RQO_MAX_D], yv[RQO_MAX_D];
+    const uint16_t *qrow = q + (((size_t)loop * B + b) * H + h) * d;
+    for (int i = 0; i < d; ++i)
+        qd[i] = rqo_bf16_to_f32(qrow[i]);
+    int G = d / g, nb = d * bits / 8;
+    int Ga = abits ? d / ga : 0, nba = d * abits / 8;
+    for (int t = 0; t < n_ctx; ++t) {
+        size_t slot = bh * cap + (size_t)t;
+        if (abits) {
+            rqo_dequant_f64(kac + slot * nba, kam + slot * 2 * Ga, d, ga, abits, rotate, yk);
+            rqo_dequant_f64(vac + slot * nba, vam + slot * 2 * Ga, d, ga, abits, rotate, yv);
+        } else {
+            for (int i = 0; i < d; ++i) {
+                yk[i] = rqo_bf16_to_f32(kref[slot * d + i]);
+                yv[i] = rqo_bf16_to_f32(vref[slot * d + i]);
+            }
+        }
+        double *kt = kh + (size_t)t * d, *vt = vh + (size_t)t * d;
+        if (loop == L - 1) {
+            memcpy(kt, yk, sizeof(double) * (size_t)d);
+            memcpy(vt, yv, sizeof(double) * (size_t)d);
+        } else {
+            rqo_reconstruct_vector_y(kc + slot * nb, km + slot * 2 * G, ka[slot], yk, d, g,
+                                     bits, rotate, kt);
+            rqo_reconstruct_vector_y(vc + slot * nb, vm + slot * 2 * G, va[slot], yv, d, g,
+                                     bits, rotate, vt);
+        }
+    }
+    for (int t = 0; t < n_tail; ++t)
+        for (int i = 0; i < d; ++i) {
+            kh[(size_t)(n_ctx + t) * d + i] = rqo_bf16_to_f32(tk[(size_t)t * d + i]);
+            vh[(size_t)(n_ctx + t) * d + i] = rqo_bf16_to_f32(tv[(size_t)t * d + i]);
+        }
+    rqo_attention(qd, kh, vh, n_all, d, scale, out);
+    free(kh);
+    free(vh);
+}
+
+/* rqo_decode_row_ex with the BF16 reference and no tail. */
 void rqo_decode_row(int L, int B, int H, int d, int g, int cap, int rotate,
                     int bits, const uint16_t *kref, const uint8_t *kc,
                     const uint16_t *km, const uint16_t *ka,
@@ -387,29 +587,7 @@ void rqo_decode_row(int L, int B, int H, int d, int g, int cap, int rotate,
                     int loop, int b, int h, int n_ctx, double scale,
                     double *out)
 {
-    size_t bh = (size_t)b * H + h;
-    double *kh = (double *)malloc(sizeof(double) * (size_t)n_ctx * d);
-    double *vh = (double *)malloc(sizeof(double) * (size_t)n_ctx * d);
-    double qd[RQO_MAX_D];
-    const uint16_t *qrow = q + (((size_t)loop * B + b) * H + h) * d;
-    for (int i = 0; i < d; ++i)
-        qd[i] = rqo_bf16_to_f32(qrow[i]);
-    int G = d / g, nb = d * bits / 8;
-    for (int t = 0; t < n_ctx; ++t) {
-        size_t slot = bh * cap + (size_t)t;
-        if (loop == L - 1) {
-            for (int i = 0; i < d; ++i) {
-                kh[(size_t)t * d + i] = rqo_bf16_to_f32(kref[slot * d + i]);
-                vh[(size_t)t * d + i] = rqo_bf16_to_f32(vref[slot * d + i]);
-            }
-        } else {
-            rqo_reconstruct_vector(kc + slot * nb, km + slot * 2 * G, ka[slot],
-                                   kref + slot * d, d, g, bits, rotate, kh + (size_t)t * d);
-            rqo_reconstruct_vector(vc + slot * nb, vm + slot * 2 * G, va[slot],
-                                   vref + slot * d, d, g, bits, rotate, vh + (size_t)t * d);
-        }
-    }
-    rqo_attention(qd, kh, vh, n_ctx, d, scale, out);
-    free(kh);
-    free(vh);
+    rqo_decode_row_ex(L, B, H, d, g, cap, rotate, bits, kref, kc, km, ka, vref, vc, vm, va,
+                      g, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, q, loop, b, h, n_ctx,
+                      scale, out);
 }

@@ -78,6 +78,29 @@ def lib():
                                      + [_u16p, _u8p, _u16p, _u16p, _u16p, _u8p, _u16p, _u16p,
                                         _u16p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_double,
                                         _f64p])
+        L.rqo_alpha_f32_y.restype = C.c_float
+        L.rqo_alpha_f32_y.argtypes = [_u16p, _f32p, C.c_int]
+        L.rqo_encode_vector_y.restype = None
+        L.rqo_encode_vector_y.argtypes = [_u16p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int,
+                                          _u8p, _u16p, C.POINTER(C.c_uint16)]
+        L.rqo_anchor_vector.restype = None
+        L.rqo_anchor_vector.argtypes = [_u16p, C.c_int, C.c_int, C.c_int, C.c_int, _u8p, _u16p,
+                                        _f32p]
+        L.rqo_encode_anchored.restype = None
+        L.rqo_encode_anchored.argtypes = [C.c_int] * 9 + [_i32p, _u16p, C.c_int, C.c_int,
+                                                          C.c_void_p, C.c_void_p, C.c_void_p]
+        L.rqo_dequant_f64.restype = None
+        L.rqo_dequant_f64.argtypes = [_u8p, _u16p, C.c_int, C.c_int, C.c_int, C.c_int, _f64p]
+        L.rqo_reconstruct_anchored.restype = None
+        L.rqo_reconstruct_anchored.argtypes = ([C.c_int] * 9 + [_u8p, _u16p, C.c_void_p, C.c_void_p,
+                                                                C.c_void_p, C.c_int, C.c_int,
+                                                                C.c_int, _f64p])
+        L.rqo_decode_row_ex.restype = None
+        L.rqo_decode_row_ex.argtypes = ([C.c_int] * 8
+                                        + [C.c_void_p] * 8
+                                        + [C.c_int, C.c_int] + [C.c_void_p] * 6 + [C.c_int]
+                                        + [_u16p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_double,
+                                           _f64p])
         _lib = L
     return _lib
 
@@ -172,31 +195,89 @@ def encode_vector(x_bits, y_bits, g: int, bits: int, rotate: bool):
     return packed, meta, int(a.value)
 
 
-class Planes:
-    """One cache side (K or V): the BF16 reference and each residual loop's
-    codes / meta / alpha planes, as numpy arrays in the contract layout."""
+def anchor_vector(y_bits, g: int, bits: int, rotate: bool):
+    """Quantized anchor of one vector: returns (packed uint8[d*bits/8],
+    meta uint16[2*d/g], y_hat float32[d] -- the dequantized anchor)."""
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    d = y.size
+    packed = np.zeros(d * bits // 8, dtype=np.uint8)
+    meta = np.zeros(2 * (d // g), dtype=np.uint16)
+    yhat = np.zeros(d, dtype=np.float32)
+    lib().rqo_anchor_vector(y, d, g, bits, int(rotate), packed, meta, yhat)
+    return packed, meta, yhat
 
-    def __init__(self, n_loops, batch, heads, d, g, cap, bits):
-        self.ref = np.zeros((batch, heads, cap, d), dtype=np.uint16)
+
+def encode_vector_y(x_bits, y_f32, g: int, bits: int, rotate: bool):
+    """encode_vector against an FP32 reference (e.g. a dequantized anchor)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    y = np.ascontiguousarray(y_f32, dtype=np.float32)
+    d = x.size
+    packed = np.zeros(d * bits // 8, dtype=np.uint8)
+    meta = np.zeros(2 * (d // g), dtype=np.uint16)
+    a = C.c_uint16()
+    lib().rqo_encode_vector_y(x, y, d, g, bits, int(rotate), packed, meta, C.byref(a))
+    return packed, meta, int(a.value)
+
+
+def dequant_f64(packed, meta, d: int, g: int, bits: int, rotate: bool) -> np.ndarray:
+    """z + s*q per group, un-rotated, in FP64."""
+    out = np.zeros(d, dtype=np.float64)
+    lib().rqo_dequant_f64(np.ascontiguousarray(packed, dtype=np.uint8),
+                          np.ascontiguousarray(meta, dtype=np.uint16), d, g, bits, int(rotate), out)
+    return out
+
+
+def anchored(layout: dict) -> bool:
+    return int(layout.get("ref_bits", 0)) > 0
+
+
+def ref_group(layout: dict) -> int:
+    return int(layout.get("ref_group") or layout["g"])
+
+
+class Planes:
+    """One cache side (K or V), as numpy arrays in the contract layout: the
+    BF16 reference and each residual loop's codes / meta / alpha planes; with
+    a quantized anchor (ref_bits > 0) no reference plane, and codes / meta
+    lists one longer, the anchor's planes last."""
+
+    def __init__(self, n_loops, batch, heads, d, g, cap, bits, ref_bits=0, ref_group=None):
+        ga = ref_group or g
+        self.ref = None if ref_bits else np.zeros((batch, heads, cap, d), dtype=np.uint16)
         self.codes = [np.zeros((batch, heads, cap, d * bits[l] // 8), dtype=np.uint8)
                       for l in range(n_loops - 1)]
         self.meta = [np.zeros((batch, heads, cap, d // g, 2), dtype=np.uint16)
                      for l in range(n_loops - 1)]
         self.alpha = [np.zeros((batch, heads, cap), dtype=np.uint16)
                       for l in range(n_loops - 1)]
+        if ref_bits:
+            self.codes.append(np.zeros((batch, heads, cap, d * ref_bits // 8), dtype=np.uint8))
+            self.meta.append(np.zeros((batch, heads, cap, d // ga, 2), dtype=np.uint16))
+
+
+def _ptrs(arrs):
+    return (C.c_void_p * max(1, len(arrs)))(*[a.ctypes.data for a in arrs])
 
 
 def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) -> None:
-    """Encode tokens [t0, t0+n) of the residual loops into `planes` (in place).
-    layout: dict(n_loops, batch, heads, d, g, cap, rotate, bits);
-    x_bits: bf16 bits [L-1, B, H, n, d]; planes.ref already holds the reference."""
+    """Encode tokens [t0, t0+n) into `planes` (in place).
+    layout: dict(n_loops, batch, heads, d, g, cap, rotate, bits[, ref_bits,
+    ref_group]).  BF16 reference: x_bits is bf16 bits [L-1, B, H, n, d] and
+    planes.ref already holds the reference.  Quantized anchor: x_bits is
+    [L, B, H, n, d], the anchor's input last."""
     L, B, H = layout["n_loops"], layout["batch"], layout["heads"]
     d, g, cap = layout["d"], layout["g"], layout["cap"]
     bits = np.ascontiguousarray(layout["bits"][:L - 1], dtype=np.int32)
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    cp, mp, ap = _ptrs(planes.codes), _ptrs(planes.meta), _ptrs(planes.alpha)
+    if anchored(layout):
+        assert x.shape == (L, B, H, n, d)
+        lib().rqo_encode_anchored(L, B, H, d, g, ref_group(layout), int(layout["ref_bits"]), cap,
+                                  int(layout["rotate"]), bits, x, t0, n,
+                                  C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p),
+                                  C.cast(ap, C.c_void_p))
+        return
     assert x.shape == (L - 1, B, H, n, d)
-    ptrs = lambda arrs: (C.c_void_p * max(1, len(arrs)))(*[a.ctypes.data for a in arrs])
-    cp, mp, ap = ptrs(planes.codes), ptrs(planes.meta), ptrs(planes.alpha)
     lib().rqo_encode(L, B, H, d, g, cap, int(layout["rotate"]), bits,
                      np.ascontiguousarray(planes.ref), x, t0, n,
                      C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p), C.cast(ap, C.c_void_p))
@@ -207,9 +288,22 @@ def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) ->
 # ---------------------------------------------------------------------------
 
 def reconstruct(layout: dict, planes: Planes, loop: int, t0: int, n: int) -> np.ndarray:
-    """x_hat of loop `loop` < L-1 for tokens [t0, t0+n): float64 [B, H, n, d]."""
-    B, H, d = layout["batch"], layout["heads"], layout["d"]
+    """x_hat of loop `loop` for tokens [t0, t0+n): float64 [B, H, n, d].
+    BF16 reference: loop < L-1.  Quantized anchor: any loop; loop L-1 is the
+    dequantized anchor."""
+    L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
     out = np.zeros((B, H, n, d), dtype=np.float64)
+    if anchored(layout):
+        anchor = loop == L - 1
+        li = 0 if anchor else loop
+        lib().rqo_reconstruct_anchored(B, H, d, layout["g"], ref_group(layout),
+                                       int(layout["ref_bits"]), layout["cap"],
+                                       int(layout["rotate"]), int(layout["bits"][li]),
+                                       planes.codes[L - 1], planes.meta[L - 1],
+                                       planes.codes[li].ctypes.data, planes.meta[li].ctypes.data,
+                                       planes.alpha[li].ctypes.data, -1 if anchor else loop,
+                                       t0, n, out)
+        return out
     lib().rqo_reconstruct(B, H, d, layout["g"], layout["cap"], int(layout["rotate"]),
                           int(layout["bits"][loop]), planes.ref, planes.codes[loop],
                           planes.meta[loop], planes.alpha[loop], t0, n, out)
@@ -227,25 +321,48 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.n
 
 
 def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: int,
-               b: int, h: int, n_ctx: int, scale: float) -> np.ndarray:
-    """Attention output (float64 [d]) of loop `loop`'s query for (b, h)."""
+               b: int, h: int, n_ctx: int, scale: float, tail_k=None, tail_v=None) -> np.ndarray:
+    """Attention output (float64 [d]) of loop `loop`'s query for (b, h) over
+    the n_ctx cached tokens and then the tail rows (bf16 bits [T, d] of this
+    (loop, b, h)), if given."""
     L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
-    # The final loop attends over the reference alone; its plane arguments
-    # are ignored by the C side, so loop 0's planes stand in for them.
+    # The final loop attends over the reference alone; its residual plane
+    # arguments are ignored by the C side, so loop 0's planes stand in.
     li = 0 if loop == L - 1 else loop
     bits = int(layout["bits"][li])
     out = np.zeros(d, dtype=np.float64)
-    lib().rqo_decode_row(L, B, H, d, layout["g"], layout["cap"], int(layout["rotate"]), bits,
-                         kp.ref, kp.codes[li], kp.meta[li], kp.alpha[li],
-                         vp.ref, vp.codes[li], vp.meta[li], vp.alpha[li],
-                         np.ascontiguousarray(q_bits, dtype=np.uint16), loop, b, h, n_ctx,
-                         float(scale), out)
+    ptr = lambda a: None if a is None else np.ascontiguousarray(a).ctypes.data
+    keep = []
+
+    def tail(t):
+        if t is None:
+            return None
+        t = np.ascontiguousarray(t, dtype=np.uint16)
+        keep.append(t)
+        return t.ctypes.data
+    tk, tv = tail(tail_k), tail(tail_v)
+    n_tail = 0 if tail_k is None else int(np.asarray(tail_k).shape[0])
+    if anchored(layout):
+        abits, ga = int(layout["ref_bits"]), ref_group(layout)
+        anc = (kp.codes[L - 1], kp.meta[L - 1], vp.codes[L - 1], vp.meta[L - 1])
+        kref = vref = None
+    else:
+        abits, ga = 0, layout["g"]
+        anc = (None, None, None, None)
+        kref, vref = kp.ref, vp.ref
+    lib().rqo_decode_row_ex(L, B, H, d, layout["g"], layout["cap"], int(layout["rotate"]), bits,
+                            ptr(kref), ptr(kp.codes[li]), ptr(kp.meta[li]), ptr(kp.alpha[li]),
+                            ptr(vref), ptr(vp.codes[li]), ptr(vp.meta[li]), ptr(vp.alpha[li]),
+                            ga, abits, *[ptr(x) for x in anc], tk, tv, n_tail,
+                            np.ascontiguousarray(q_bits, dtype=np.uint16), loop, b, h, n_ctx,
+                            float(scale), out)
     return out
 
 
 def decode(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop_mask: int,
-           n_ctx: int, scale: float) -> np.ndarray:
-    """All rows: float64 [L, B, H, d]; rows of loops not in the mask are NaN."""
+           n_ctx: int, scale: float, tail_k=None, tail_v=None) -> np.ndarray:
+    """All rows: float64 [L, B, H, d]; rows of loops not in the mask are NaN.
+    tail_k / tail_v: optional bf16 bits [L, B, H, T, d]."""
     L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
     out = np.full((L, B, H, d), np.nan, dtype=np.float64)
     for l in range(L):
@@ -253,5 +370,7 @@ def decode(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop_mask: 
             continue
         for b in range(B):
             for h in range(H):
-                out[l, b, h] = decode_row(layout, kp, vp, q_bits, l, b, h, n_ctx, scale)
+                tk = None if tail_k is None else tail_k[l, b, h]
+                tv = None if tail_v is None else tail_v[l, b, h]
+                out[l, b, h] = decode_row(layout, kp, vp, q_bits, l, b, h, n_ctx, scale, tk, tv)
     return out

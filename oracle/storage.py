@@ -71,7 +71,20 @@ def layout_bits_per_value(n_loops: int, bits: List[int], g: int, d: int) -> floa
     return effective_bits(sched, d, meta_bits=32, alpha_bits=16)
 
 
-def layout_bytes_per_token(n_loops: int, bits: List[int], g: int, d: int) -> int:
-    """Bytes per (batch, head, token) for K plus V in this library's layout."""
-    per_side = 2 * d + sum(d * bits[l] // 8 + 4 * (d // g) + 2 for l in range(n_loops - 1))
+def layout_bytes_per_token(n_loops: int, bits: List[int], g: int, d: int, ref_bits: int = 0,
+                           ref_group: int = 0) -> int:
+    """Bytes per (batch, head, token) for K plus V in this library's layout:
+    the BF16 reference (ref_bits 0) or a quantized anchor (codes plus FP16
+    scale and zero per group of ref_group), plus every residual loop."""
+    ga = ref_group or g
+    ref = 2 * d if not ref_bits else d * ref_bits // 8 + 4 * (d // ga)
+    per_side = ref + sum(d * bits[l] // 8 + 4 * (d // g) + 2 for l in range(n_loops - 1))
     return 2 * per_side
+
+
+def loop_read_bytes_per_token(bits: int, g: int, d: int, ref_bits: int = 0, ref_group: int = 0) -> int:
+    """Bytes per (batch, head, token) that decoding ONE residual loop on its own
+    reads (K plus V): the reference or anchor and that loop's planes."""
+    ga = ref_group or g
+    ref = 2 * d if not ref_bits else d * ref_bits // 8 + 4 * (d // ga)
+    return 2 * (ref + d * bits // 8 + 4 * (d // g) + 2)

@@ -45,3 +45,19 @@ def test_this_layout():
     assert abs(storage.layout_bits_per_value(4, [2, 2, 2], 32, 128) - 6.34375) < 1e-12
     # bytes agree with bits: 2 sides * 4 loops * 128 values * bits / 8
     assert 2 * 4 * 128 * storage.layout_bits_per_value(4, [2, 2, 2], 32, 128) / 8 == 812
+
+
+def test_anchored_layout():
+    """The pages' final configuration [2,2,2,4] (Fig. 6 caption: INT2 residuals
+    at g=16, the INT4 anchor at g=32) in this layout, worked by hand per K or V
+    side of one (batch, head, token):
+      anchor: 128 * 4 / 8 = 64 B codes + 4 groups * 4 B (FP16 scale, zero) = 80 B
+      INT2 loop at g=16: 32 B codes + 8 groups * 4 B + 2 B alpha = 66 B
+    so the whole cache holds 2 * (80 + 3 * 66) = 556 B, and decoding one loop on
+    its own reads 2 * (80 + 66) = 292 B, against 2 * 256 = 512 B for that loop's
+    BF16 K and V."""
+    assert storage.layout_bytes_per_token(4, [2, 2, 2], 16, 128, ref_bits=4, ref_group=32) == 556
+    assert storage.loop_read_bytes_per_token(2, 16, 128, ref_bits=4, ref_group=32) == 292
+    assert storage.loop_read_bytes_per_token(2, 32, 128, ref_bits=4, ref_group=32) == 2 * (80 + 50)
+    # with the BF16 reference, one loop alone reads more than its BF16 K and V
+    assert storage.loop_read_bytes_per_token(2, 32, 128) == 2 * (256 + 50) > 512
