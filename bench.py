@@ -56,7 +56,7 @@ def algorithmic_bytes_per_token(w) -> int:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("rq_decode.hip", "rq_device.hpp", "rq_internal.hpp"):
+    for f in ("rq_decode.hip", "rq_decode_kernel.hpp", "rq_device.hpp", "rq_internal.hpp"):
         h.update(open(os.path.join(ROOT, "decode_attention_rq_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -27,12 +27,18 @@ _lib = C.CDLL(LIB_PATH)
 class rq_layout(C.Structure):
     _fields_ = [("n_loops", C.c_int32), ("batch", C.c_int32), ("n_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("group", C.c_int32), ("capacity", C.c_int32),
-                ("rotate", C.c_int32), ("bits", C.c_int32 * RQ_MAX_LOOPS)]
+                ("rotate", C.c_int32), ("bits", C.c_int32 * RQ_MAX_LOOPS),
+                ("ref_bits", C.c_int32), ("ref_group", C.c_int32)]
 
 
 class rq_cache(C.Structure):
     _fields_ = [("ref", C.c_void_p), ("codes", C.c_void_p * RQ_MAX_LOOPS),
                 ("meta", C.c_void_p * RQ_MAX_LOOPS), ("alpha", C.c_void_p * RQ_MAX_LOOPS)]
+
+
+class rq_tail(C.Structure):
+    _fields_ = [("k", C.c_void_p * RQ_MAX_LOOPS), ("v", C.c_void_p * RQ_MAX_LOOPS),
+                ("capacity", C.c_int32), ("n", C.c_int32)]
 
 
 _P = C.POINTER
@@ -49,6 +55,10 @@ _lib.rq_decode_attn.restype = C.c_int
 _lib.rq_decode_attn.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), C.c_void_p, C.c_uint32,
                                 C.c_int32, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                 C.c_size_t, C.c_void_p]
+_lib.rq_decode_attn_tail.restype = C.c_int
+_lib.rq_decode_attn_tail.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), _P(rq_tail), C.c_void_p,
+                                     C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.rq_bf16_decode_attn.restype = C.c_int
 _lib.rq_bf16_decode_attn.argtypes = [_P(rq_layout), _P(C.c_void_p), _P(C.c_void_p), C.c_void_p,
                                      C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
@@ -87,18 +97,28 @@ class Layout:
     capacity: int
     rotate: int = 1
     bits: Sequence[int] = field(default_factory=list)   # per residual loop
+    ref_bits: int = 0        # 0: BF16 reference; 2 or 4: quantized anchor
+    ref_group: int = 0       # the anchor's group size (0: group)
+
+    @property
+    def anchor_group(self) -> int:
+        return self.ref_group or self.group
 
     def c(self) -> rq_layout:
         s = rq_layout(self.n_loops, self.batch, self.n_heads, self.head_dim, self.group,
                       self.capacity, self.rotate)
         for i, b in enumerate(list(self.bits)[:RQ_MAX_LOOPS]):
             s.bits[i] = int(b)
+        s.ref_bits = int(self.ref_bits)
+        s.ref_group = int(self.ref_group)
         return s
 
 
 class Cache:
     """One side (K or V) of a layer's cache: torch tensors in the plane layout
-    of include/rq.h (the library reads and writes them in place)."""
+    of include/rq.h (the library reads and writes them in place).  With a
+    quantized anchor there is no `ref` (None) and codes / meta hold one more
+    plane, the anchor's, last."""
 
     def __init__(self, layout: Layout, device="cuda", ref: Optional[torch.Tensor] = None,
                  zero: bool = True):
@@ -108,7 +128,10 @@ class Cache:
                               layout.group, layout.capacity)
         new = torch.zeros if zero else torch.empty
         self.layout = layout
-        self.ref = ref if ref is not None else new(B, H, cap, d, dtype=torch.bfloat16, device=device)
+        if layout.ref_bits:
+            self.ref = None
+        else:
+            self.ref = ref if ref is not None else new(B, H, cap, d, dtype=torch.bfloat16, device=device)
         self.codes: List[torch.Tensor] = [
             new(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device)
             for l in range(L - 1)]
@@ -116,13 +139,18 @@ class Cache:
             new(B, H, cap, d // g, 2, dtype=torch.float16, device=device) for _ in range(L - 1)]
         self.alpha: List[torch.Tensor] = [
             new(B, H, cap, dtype=torch.float16, device=device) for _ in range(L - 1)]
+        if layout.ref_bits:
+            ga = layout.anchor_group
+            self.codes.append(new(B, H, cap, d * layout.ref_bits // 8, dtype=torch.uint8, device=device))
+            self.meta.append(new(B, H, cap, d // ga, 2, dtype=torch.float16, device=device))
 
     def c(self) -> rq_cache:
         s = rq_cache()
-        s.ref = self.ref.data_ptr()
+        s.ref = _ptr(self.ref)
         for l in range(len(self.codes)):
             s.codes[l] = self.codes[l].data_ptr()
             s.meta[l] = self.meta[l].data_ptr()
+        for l in range(len(self.alpha)):
             s.alpha[l] = self.alpha[l].data_ptr()
         return s
 
@@ -132,14 +160,14 @@ class Cache:
         batch = b1 - b0."""
         v = Cache.__new__(Cache)
         v.layout = layout
-        v.ref = self.ref[b0:b1]
+        v.ref = None if self.ref is None else self.ref[b0:b1]
         v.codes = [t[b0:b1] for t in self.codes]
         v.meta = [t[b0:b1] for t in self.meta]
         v.alpha = [t[b0:b1] for t in self.alpha]
         return v
 
     def nbytes(self) -> int:
-        t = [self.ref] + self.codes + self.meta + self.alpha
+        t = ([] if self.ref is None else [self.ref]) + self.codes + self.meta + self.alpha
         return sum(x.numel() * x.element_size() for x in t)
 
 
@@ -155,7 +183,8 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 def rq_encode(layout: Layout, k: Cache, v: Cache, k_in: torch.Tensor, v_in: torch.Tensor,
               t0: int, n: int, stream=None) -> None:
-    """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous."""
+    """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous ([L, B, H, n, d], the
+    anchor's input last, with a quantized anchor)."""
     lay, kc, vc = layout.c(), k.c(), v.c()
     _check(_lib.rq_encode(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(k_in), _ptr(v_in),
                           int(t0), int(n), _stream(stream)))
@@ -182,6 +211,39 @@ def rq_decode_attn(layout: Layout, k: Cache, v: Cache, q: torch.Tensor, loop_mas
     _check(_lib.rq_decode_attn(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(q), int(loop_mask),
                                int(n_ctx), float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class Tail:
+    """Recent BF16 tokens per loop: k[l], v[l] bf16 [B, H, capacity, d]
+    (None for loops never attended); n tokens [0, n) are attended."""
+
+    def __init__(self, k: Sequence[Optional[torch.Tensor]], v: Sequence[Optional[torch.Tensor]], n: int):
+        self.k, self.v, self.n = list(k), list(v), int(n)
+        caps = [t.shape[2] for t in self.k + self.v if t is not None]
+        self.capacity = min(caps) if caps else 0
+
+    def c(self) -> rq_tail:
+        s = rq_tail()
+        for l, t in enumerate(self.k):
+            s.k[l] = _ptr(t)
+        for l, t in enumerate(self.v):
+            s.v[l] = _ptr(t)
+        s.capacity = self.capacity
+        s.n = self.n
+        return s
+
+
+def rq_decode_attn_tail(layout: Layout, k: Cache, v: Cache, tail: Optional[Tail], q: torch.Tensor,
+                        loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
+                        workspace: torch.Tensor, n_splits: int = 0, stream=None) -> None:
+    """rq_decode_attn over n_ctx cached tokens followed by tail.n BF16 tokens."""
+    lay, kc, vc = layout.c(), k.c(), v.c()
+    tc = tail.c() if tail is not None else None
+    _check(_lib.rq_decode_attn_tail(C.byref(lay), C.byref(kc), C.byref(vc),
+                                    C.byref(tc) if tc is not None else None, _ptr(q),
+                                    int(loop_mask), int(n_ctx), float(sm_scale), int(n_splits),
+                                    _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops: Sequence[torch.Tensor],

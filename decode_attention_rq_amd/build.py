@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.cpp", "rq_encode.hip", "rq_reconstruct.hip", "rq_decode.hip"]
+SOURCES = ["rq_api.cpp", "rq_encode.hip", "rq_reconstruct.hip", "rq_decode.hip",
+           "rq_decode_anchor4.hip", "rq_decode_anchor2.hip"]
 ARCH = os.environ.get("RQ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -48,7 +49,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             sys.stderr.write(err + "\n")
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    link = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] + objs
+    link = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o",
+            LIB + ".tmp"] + objs
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

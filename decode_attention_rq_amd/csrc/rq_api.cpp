@@ -31,13 +31,26 @@ rq_status check_layout(const rq_layout *L) {
   if (L->rotate != 0 && L->rotate != 1) return RQ_ERR_INVALID_ARG;
   for (int l = 0; l < L->n_loops - 1; ++l)
     if (L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
+  if (L->ref_bits != 0 && L->ref_bits != 2 && L->ref_bits != 4) return RQ_ERR_UNSUPPORTED;
+  if (L->ref_bits != 0) {
+    const int ga = L->ref_group ? L->ref_group : L->group;
+    if (ga != 16 && ga != 32) return RQ_ERR_UNSUPPORTED;
+  }
   // token indices are int32 inside the kernels
   if ((int64_t)L->batch * L->n_heads * L->capacity > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   return RQ_OK;
 }
 
+int anchor_group(const rq_layout *L) { return L->ref_group ? L->ref_group : L->group; }
+
+// The reference planes: the BF16 ref plane, or the anchor's codes and meta.
+bool ref_planes_ok(const rq_layout *L, const rq_cache *c) {
+  if (L->ref_bits == 0) return aligned16(c->ref);
+  return aligned16(c->codes[L->n_loops - 1]) && aligned16(c->meta[L->n_loops - 1]);
+}
+
 rq_status check_cache(const rq_layout *L, const rq_cache *c) {
-  if (c == nullptr || !aligned16(c->ref)) return RQ_ERR_INVALID_ARG;
+  if (c == nullptr || !ref_planes_ok(L, c)) return RQ_ERR_INVALID_ARG;
   for (int l = 0; l < L->n_loops - 1; ++l)
     if (!aligned16(c->codes[l]) || !aligned16(c->meta[l]) || !aligned16(c->alpha[l]))
       return RQ_ERR_INVALID_ARG;
@@ -108,12 +121,12 @@ int auto_splits(const rq_layout *L, int n_ctx, int slots) {
   return (int)s;
 }
 
-// Workspace: the split records f32 [S][kMaxSlots][BH][2D+2]; none for S = 1
-// (a 256-byte minimum keeps the pointer checks uniform).
+// Workspace: the split records f32 [S][kMaxSlots][BH][2D+2], at least one
+// split's worth (a single split writes records when a BF16 tail follows).
 size_t workspace_for(const rq_layout *L, int n_splits) {
-  if (n_splits <= 1) return 256;
-  return (size_t)n_splits * rq::kMaxSlots * (size_t)L->batch * L->n_heads *
-         (size_t)(2 * L->head_dim + 2) * sizeof(float);
+  const size_t s = n_splits > 1 ? (size_t)n_splits : 1;
+  return s * rq::kMaxSlots * (size_t)L->batch * L->n_heads * (size_t)(2 * L->head_dim + 2) *
+         sizeof(float);
 }
 
 }  // namespace
@@ -152,7 +165,13 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
       a.side[s].meta[l] = static_cast<uint32_t *>(sides[s]->meta[l]);
       a.side[s].alpha[l] = static_cast<uint16_t *>(sides[s]->alpha[l]);
     }
+    if (L->ref_bits) {
+      a.side[s].codes[L->n_loops - 1] = static_cast<uint8_t *>(sides[s]->codes[L->n_loops - 1]);
+      a.side[s].meta[L->n_loops - 1] = static_cast<uint32_t *>(sides[s]->meta[L->n_loops - 1]);
+    }
   }
+  a.abits = L->ref_bits;
+  a.agroup = anchor_group(L);
   for (int l = 0; l < L->n_loops - 1; ++l) a.bits[l] = L->bits[l];
   a.n_res = L->n_loops - 1;
   a.bh = L->batch * L->n_heads;
@@ -172,14 +191,15 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
 }
 
 int32_t rq_decode_splits(const rq_layout *L, int32_t n_ctx) {
-  if (check_layout(L) != RQ_OK || n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  if (check_layout(L) != RQ_OK || n_ctx < 0 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  if (n_ctx == 0) return 1;
   const int slots = decode_slots(L->head_dim);
   if (slots <= 0) return RQ_ERR_DEVICE;
   return auto_splits(L, n_ctx, slots);
 }
 
 size_t rq_decode_workspace_bytes(const rq_layout *L, int32_t n_ctx, int32_t n_splits) {
-  if (check_layout(L) != RQ_OK || n_ctx < 1 || n_ctx > L->capacity || n_splits < 0) return 0;
+  if (check_layout(L) != RQ_OK || n_ctx < 0 || n_ctx > L->capacity || n_splits < 0) return 0;
   int s = n_splits;
   if (s == 0) {
     s = rq_decode_splits(L, n_ctx);
@@ -189,39 +209,63 @@ size_t rq_decode_workspace_bytes(const rq_layout *L, int32_t n_ctx, int32_t n_sp
   return workspace_for(L, s);
 }
 
-rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *v, const void *q,
-                         uint32_t loop_mask, int32_t n_ctx, float sm_scale, int32_t n_splits,
-                         float *out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, const rq_tail *tail,
+                      const void *q, uint32_t loop_mask, int32_t n_ctx, float sm_scale,
+                      int32_t n_splits, float *out, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
   rq_status st = check_layout(L);
   if (st != RQ_OK) return st;
-  if (k == nullptr || v == nullptr || !aligned16(k->ref) || !aligned16(v->ref)) return RQ_ERR_INVALID_ARG;
+  if (k == nullptr || v == nullptr) return RQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return RQ_ERR_INVALID_ARG;
   if (loop_mask == 0) return RQ_ERR_INVALID_ARG;
   if (L->n_loops < 32 && (loop_mask >> L->n_loops) != 0) return RQ_ERR_INVALID_ARG;
-  if (n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
+  const int n_tail = tail ? tail->n : 0;
+  if (tail && (tail->n < 0 || tail->capacity < tail->n)) return RQ_ERR_INVALID_ARG;
+  if (n_ctx < 0 || n_ctx > L->capacity || (int64_t)n_ctx + n_tail < 1) return RQ_ERR_INVALID_ARG;
+  if (n_tail > 0 && (int64_t)L->batch * L->n_heads * tail->capacity > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
-  if (n_splits < 0 || n_splits > n_ctx) return RQ_ERR_INVALID_ARG;
+  if (n_splits < 0 || (n_ctx > 0 && n_splits > n_ctx)) return RQ_ERR_INVALID_ARG;
   const int ref_loop = L->n_loops - 1;
-  for (int l = 0; l < ref_loop; ++l) {
+  if (n_ctx > 0 && !ref_planes_ok(L, k)) return RQ_ERR_INVALID_ARG;
+  if (n_ctx > 0 && !ref_planes_ok(L, v)) return RQ_ERR_INVALID_ARG;
+  for (int l = 0; l < L->n_loops; ++l) {
     if (!((loop_mask >> l) & 1u)) continue;
-    if (!aligned16(k->codes[l]) || !aligned16(k->meta[l]) || !aligned16(k->alpha[l]) ||
-        !aligned16(v->codes[l]) || !aligned16(v->meta[l]) || !aligned16(v->alpha[l]))
+    if (n_ctx > 0 && l < ref_loop &&
+        (!aligned16(k->codes[l]) || !aligned16(k->meta[l]) || !aligned16(k->alpha[l]) ||
+         !aligned16(v->codes[l]) || !aligned16(v->meta[l]) || !aligned16(v->alpha[l])))
       return RQ_ERR_INVALID_ARG;
+    if (n_tail > 0 && (!aligned16(tail->k[l]) || !aligned16(tail->v[l]))) return RQ_ERR_INVALID_ARG;
   }
-  int S = n_splits;
-  if (S == 0) {
-    S = rq_decode_splits(L, n_ctx);
-    if (S <= 0) return RQ_ERR_DEVICE;
+  int S = 0, tps = 0;
+  if (n_ctx > 0) {
+    S = n_splits;
+    if (S == 0) {
+      S = rq_decode_splits(L, n_ctx);
+      if (S <= 0) return RQ_ERR_DEVICE;
+    }
+    // every split non-empty
+    tps = (n_ctx + S - 1) / S;
+    S = (n_ctx + tps - 1) / tps;
   }
   if (workspace_bytes < workspace_for(L, S)) return RQ_ERR_WORKSPACE;
-  // every split non-empty
-  const int tps = (n_ctx + S - 1) / S;
-  S = (n_ctx + tps - 1) / tps;
 
   rq::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
-  a.kref = static_cast<const uint16_t *>(k->ref);
-  a.vref = static_cast<const uint16_t *>(v->ref);
+  if (L->ref_bits == 0) {
+    a.kref = static_cast<const uint16_t *>(k->ref);
+    a.vref = static_cast<const uint16_t *>(v->ref);
+  } else {
+    a.kac = static_cast<const uint8_t *>(k->codes[ref_loop]);
+    a.vac = static_cast<const uint8_t *>(v->codes[ref_loop]);
+    a.kam = static_cast<const uint32_t *>(k->meta[ref_loop]);
+    a.vam = static_cast<const uint32_t *>(v->meta[ref_loop]);
+    a.ref_rotated = L->rotate;
+  }
+  a.agroup = anchor_group(L);
   a.q = static_cast<const uint16_t *>(q);
   a.ws = static_cast<float *>(workspace);
   a.out = out;
@@ -230,6 +274,9 @@ rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *
   a.n_ctx = n_ctx;
   a.n_splits = S;
   a.tps = tps;
+  a.n_tail = n_tail;
+  a.tcap = tail ? tail->capacity : 0;
+  a.records = (S > 1 || n_tail > 0) ? 1 : 0;
   a.group = L->group;
   a.rotate = L->rotate;
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
@@ -239,12 +286,14 @@ rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *
   for (int l = 0; l < ref_loop; ++l)
     if ((loop_mask >> l) & 1u) res[nres++] = l;
   bool want_ref = (loop_mask >> ref_loop) & 1u;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
   // Passes of at most kMaxRes residual loops; the first also computes the
   // reference loop.  Each pass reads the reference once.
   int done = 0;
   do {
     const int cnt = (nres - done) < rq::kMaxRes ? (nres - done) : rq::kMaxRes;
+    for (int i = 0; i < rq::kMaxSlots; ++i) a.tk[i] = a.tv[i] = nullptr;
     for (int i = 0; i < cnt; ++i) {
       const int l = res[done + i];
       a.kc[i] = static_cast<const uint8_t *>(k->codes[l]);
@@ -255,15 +304,48 @@ rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *
       a.va[i] = static_cast<const uint16_t *>(v->alpha[l]);
       a.bits[i] = L->bits[l];
       a.qloop[i] = l;
+      if (n_tail > 0) {
+        a.tk[i] = static_cast<const uint16_t *>(tail->k[l]);
+        a.tv[i] = static_cast<const uint16_t *>(tail->v[l]);
+      }
     }
-    if (want_ref) a.qloop[cnt] = ref_loop;
-    if (rq::launch_decode(a, L->head_dim, cnt, want_ref, static_cast<hipStream_t>(hip_stream)) !=
-        hipSuccess)
-      return RQ_ERR_DEVICE;
+    if (want_ref) {
+      a.qloop[cnt] = ref_loop;
+      if (n_tail > 0) {
+        a.tk[cnt] = static_cast<const uint16_t *>(tail->k[ref_loop]);
+        a.tv[cnt] = static_cast<const uint16_t *>(tail->v[ref_loop]);
+      }
+    }
+    hipError_t e;
+    if (n_ctx > 0)
+      e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, stream);
+    else   // the tail alone: the merge kernel attends over it, no split records
+      e = rq::launch_merge(a, L->head_dim, cnt, cnt + (want_ref ? 1 : 0), stream);
+    if (e != hipSuccess) return RQ_ERR_DEVICE;
     want_ref = false;
     done += cnt;
   } while (done < nres);
   return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rq_decode_attn(const rq_layout *L, const rq_cache *k, const rq_cache *v, const void *q,
+                         uint32_t loop_mask, int32_t n_ctx, float sm_scale, int32_t n_splits,
+                         float *out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (n_ctx < 1) return RQ_ERR_INVALID_ARG;
+  return decode_impl(L, k, v, nullptr, q, loop_mask, n_ctx, sm_scale, n_splits, out, workspace,
+                     workspace_bytes, hip_stream);
+}
+
+rq_status rq_decode_attn_tail(const rq_layout *L, const rq_cache *k, const rq_cache *v,
+                              const rq_tail *tail, const void *q, uint32_t loop_mask,
+                              int32_t n_ctx, float sm_scale, int32_t n_splits, float *out,
+                              void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return decode_impl(L, k, v, tail, q, loop_mask, n_ctx, sm_scale, n_splits, out, workspace,
+                     workspace_bytes, hip_stream);
 }
 
 rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *const *v_loops,
@@ -292,6 +374,8 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
   S = (n_ctx + tps - 1) / tps;
   rq::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
+  a.records = S > 1 ? 1 : 0;
+  a.agroup = 32;
   a.ws = static_cast<float *>(workspace);
   a.out = out;
   a.q = static_cast<const uint16_t *>(q);
@@ -310,7 +394,7 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
     a.kref = static_cast<const uint16_t *>(k_loops[l]);
     a.vref = static_cast<const uint16_t *>(v_loops[l]);
     a.qloop[0] = l;
-    if (rq::launch_decode(a, L->head_dim, 0, true, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    if (rq::launch_decode(a, L->head_dim, 0, true, 0, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
       return RQ_ERR_DEVICE;
   }
   return RQ_OK;
@@ -320,19 +404,31 @@ rq_status rq_reconstruct(const rq_layout *L, const rq_cache *c, int32_t loop, in
                          float *out, void *hip_stream) {
   rq_status st = check_layout(L);
   if (st != RQ_OK) return st;
-  if (loop < 0 || loop >= L->n_loops - 1) return RQ_ERR_INVALID_ARG;
-  if (c == nullptr || !aligned16(c->ref) || !aligned16(c->codes[loop]) || !aligned16(c->meta[loop]) ||
-      !aligned16(c->alpha[loop]) || !aligned16(out))
+  const int ref_loop = L->n_loops - 1;
+  const bool anchor_loop = L->ref_bits != 0 && loop == ref_loop;
+  if (loop < 0 || loop > ref_loop || (loop == ref_loop && !anchor_loop)) return RQ_ERR_INVALID_ARG;
+  if (c == nullptr || !ref_planes_ok(L, c) || !aligned16(out)) return RQ_ERR_INVALID_ARG;
+  if (!anchor_loop &&
+      (!aligned16(c->codes[loop]) || !aligned16(c->meta[loop]) || !aligned16(c->alpha[loop])))
     return RQ_ERR_INVALID_ARG;
   if (t0 < 0 || n < 1 || (int64_t)t0 + n > L->capacity) return RQ_ERR_INVALID_ARG;
   rq::ReconArgs a;
   std::memset(&a, 0, sizeof a);
-  a.ref = static_cast<const uint16_t *>(c->ref);
-  a.codes = static_cast<const uint8_t *>(c->codes[loop]);
-  a.meta = static_cast<const uint32_t *>(c->meta[loop]);
-  a.alpha = static_cast<const uint16_t *>(c->alpha[loop]);
+  if (L->ref_bits == 0) {
+    a.ref = static_cast<const uint16_t *>(c->ref);
+  } else {
+    a.acodes = static_cast<const uint8_t *>(c->codes[ref_loop]);
+    a.ameta = static_cast<const uint32_t *>(c->meta[ref_loop]);
+  }
+  a.abits = L->ref_bits;
+  a.agroup = anchor_group(L);
+  if (!anchor_loop) {
+    a.codes = static_cast<const uint8_t *>(c->codes[loop]);
+    a.meta = static_cast<const uint32_t *>(c->meta[loop]);
+    a.alpha = static_cast<const uint16_t *>(c->alpha[loop]);
+    a.bits = L->bits[loop];
+  }
   a.out = out;
-  a.bits = L->bits[loop];
   a.bh = L->batch * L->n_heads;
   a.cap = L->capacity;
   a.t0 = t0;

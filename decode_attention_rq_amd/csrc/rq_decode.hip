@@ -1,511 +1,14 @@
-// rq_decode.hip -- fused decode attention over a ResidualQuant cache (gfx950).
-//
-// ResidualQuant page ("ResidualQuant: KV Cache Quantization for Looped
-// Transformers with 2-Bit Residuals"), Abstract: decode reads each loop's
-// compressed cache (BF16 reference + low-bit residual) and the smaller
-// traffic is what speeds it up.  For loop l and token t, with y the
-// reference vector and u = z + s*code the rotated, quantized residual:
-//   key    k_t = aK_t y_t + H_n u_t        value  v_t = aV_t y_t + H_n u'_t
-// Because H_n is symmetric and orthonormal the rotation is folded:
-//   q . k_t      = aK_t (q . y_t) + sum_k [ s_k (q'_k . code_k) + z_k sum(q'_k) ]
-//   sum_t p_t v_t = sum_t (p_t aV_t) y_t + H_n sum_t p_t u'_t
-// with q' = H_n q, so the per-token work is the reference dot product, the
-// code dot products and FMA accumulation; H_n is applied once per output.
-//
-// Kernel P, one launch per pass of up to three residual loops: a workgroup
-// of W waves per (token split, batch*head), each wave taking every W-th tile
-// of ROWS*TR tokens.  Lanes: D/8 lanes per token, 8 consecutive dims per
-// lane, ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane
-// reads ROWS consecutive reference rows, and every loop of the pass shares
-// that load.  Online softmax per (row, loop) in the exp2 domain; rows, then
-// waves (through LDS), are merged by log-sum-exp.  With one split the
-// workgroup finishes the output itself (un-rotation of the residual
-// accumulator, normalisation); with several it writes one record per (split,
-// loop, batch*head) to the workspace and kernel M merges the records.
+// rq_decode.hip -- decode launches for a BF16 reference, the split/tail
+// merge kernel, and the dispatch over reference kinds (gfx950).  The kernel
+// template and its description are in rq_decode_kernel.hpp.
 
-#include <float.h>
-
-#include <type_traits>
-
-#include "rq_device.hpp"
-#include "rq_internal.hpp"
+#include "rq_decode_kernel.hpp"
 
 namespace rq {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// Value of x in lane 4*(lane/4) + S (DPP quad_perm broadcast).
-__device__ __forceinline__ float quad_bcast(float x, int s) {
-  switch (s) {
-    case 0: return dpp<0x00>(x);
-    case 1: return dpp<0x55>(x);
-    case 2: return dpp<0xAA>(x);
-    default: return dpp<0xFF>(x);
-  }
-}
-
-// First product of a dot chain: the three-operand v_dot2_f32_bf16 with an
-// inline zero accumulator (the builtin would zero a register first).
-__device__ __forceinline__ float dot2bf0(uint32_t a, uint32_t b) {
-  float r;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-
-// Merge the online-softmax states of rows at lane distance MASK.  The lane's
-// running sum l_own belongs to loop slot `own` (lane index mod 4).
-template <int MASK, int NS, int NR>
-__device__ __forceinline__ void merge_rows(float (&m)[NS], float &l_own, int own, float (&oref)[NS][8],
-                                           float (&ores)[NR > 0 ? NR : 1][8]) {
-  const float lo = xor_lane<MASK>(l_own);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const float mo = xor_lane<MASK>(m[s]);
-    const float M = fmaxf(m[s], mo);
-    const float fa = fexp2(m[s] - M), fb = fexp2(mo - M);
-    if (own == s) l_own = l_own * fa + lo * fb;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) oref[s][p] = oref[s][p] * fa + xor_lane<MASK>(oref[s][p]) * fb;
-    if (s < NR) {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) ores[s][p] = ores[s][p] * fa + xor_lane<MASK>(ores[s][p]) * fb;
-    }
-    m[s] = M;
-  }
-}
-
-// Output row of one (loop slot, batch*head), lane holding dims lane + 64*e:
-// out = (o_ref + H_n o_res) / l.  H_n runs as butterflies across lanes
-// (distances 1..32) and across the lane's E = D/64 elements.
-template <int D>
-__device__ __forceinline__ void finish_row(const DecodeArgs &a, int bh, int s, bool residual, int lane,
-                                           float L, float (&o)[D / 64], float (&w)[D / 64]) {
-  constexpr int E = D / 64;
-  if (residual) {
-    if (a.rotate) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        w[e] = wht_stage<1>(w[e], lane);
-        w[e] = wht_stage<2>(w[e], lane);
-        w[e] = wht_stage<4>(w[e], lane);
-        w[e] = wht_stage<8>(w[e], lane);
-        w[e] = wht_stage<16>(w[e], lane);
-        w[e] = wht_stage<32>(w[e], lane);
-      }
-#pragma unroll
-      for (int h = 1; h < E; h *= 2) {
-#pragma unroll
-        for (int e0 = 0; e0 < E; e0 += 2 * h) {
-#pragma unroll
-          for (int e = e0; e < e0 + h; ++e) {
-            const float x = w[e], y = w[e + h];
-            w[e] = x + y;
-            w[e + h] = x - y;
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) w[e] *= a.rot_c;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += w[e];
-  }
-  const float invL = 1.0f / L;
-  float *out = a.out + ((size_t)a.qloop[s] * a.bh + bh) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) out[lane + 64 * e] = o[e] * invL;
-}
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-// fma(a, h, c) where h is one half of `w` read as an FP16 number (v_fma_mix_f32
-// takes the half directly, no conversion instruction).
-template <int HI>
-__device__ __forceinline__ float fma_half(float a, uint32_t w, float c) {
-  const half2_t h = __builtin_bit_cast(half2_t, w);
-  return __builtin_fmaf(a, (float)h[HI], c);
-}
-
-// The 8 codes of one lane as 8 FP16 halves, each holding one code in its
-// mantissa bits: a half whose bit pattern is c << b (b + width <= 10) is the
-// subnormal number c * 2^(b-24), exact.  Code p lands in half (p / 4) of word
-// w[p % 4] for INT2 and in half (p / 4) of word w[p % 4] for INT4 as well,
-// at mantissa bit position pos(p) (see code_pos).
-//   INT2 (16-bit word x, code p at bits 2p): bytes x0 = c0..c3, x1 = c4..c7 are
-//   spread to the two halves, then masked per code.
-//   INT4 (32-bit word x, code p at bits 4p): halves already hold c0..c3 and
-//   c4..c7; codes 2, 3 (6, 7) are shifted down by 8 bits first.
-template <bool INT4>
-__device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
-  if constexpr (INT4) {
-    const uint32_t y = x >> 8;
-    w[0] = x & 0x000F000Fu;
-    w[1] = x & 0x00F000F0u;
-    w[2] = y & 0x000F000Fu;
-    w[3] = y & 0x00F000F0u;
-  } else {
-    const uint32_t X = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [x.b0, 0, x.b1, 0]
-    w[0] = X & 0x00030003u;
-    w[1] = X & 0x000C000Cu;
-    w[2] = X & 0x00300030u;
-    w[3] = X & 0x00C000C0u;
-  }
-}
-
-// Mantissa bit position of code p in its half (so its half reads c * 2^(pos-24)).
-template <bool INT4>
-__host__ __device__ constexpr int code_pos(int p) {
-  return INT4 ? 4 * (p & 1) : 2 * (p & 3);
-}
-
-// Sum over the lane's 8 codes of coef[p] * half_p  (coef pre-multiplied by
-// 2^(24 - pos) makes this sum_p coef'[p] * c_p).
-template <bool INT4>
-__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc = fma_half<0>(coef[q], w[q], acc);
-    acc = fma_half<1>(coef[q + 4], w[q], acc);
-  }
-  return acc;
-}
-
-// acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
-template <bool INT4>
-__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc[q] = fma_half<0>(wgt, w[q], acc[q]);
-    acc[q + 4] = fma_half<1>(wgt, w[q], acc[q + 4]);
-  }
-}
-
-// The low / high FP16 half of a 32-bit word, for use as an fma operand
-// (v_fma_mix_f32 reads it in place).
-__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
-__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
-
-// Load from a uniform base plus a 32-bit byte offset (global_load with an
-// SGPR base and a 32-bit VGPR offset; no 64-bit address arithmetic per lane).
-template <typename T>
-__device__ __forceinline__ T ldg(const void *base, uint32_t byte_off) {
-  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
-}
-
-template <int TR, int NRA>
-struct Tile {
-  uint4 yk[TR], yv[TR];
-  uint32_t kc[TR][NRA], km[TR][NRA], ka[TR][NRA], vc[TR][NRA], vm[TR][NRA], va[TR][NRA];
-};
-
-// Scores above the running max by more than this (log2 units) trigger a
-// rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
-constexpr float kRescaleSlack = 8.0f;
-
-template <int D, int NR, bool REF, int B4, int TR, int W>
-__global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
-  constexpr int LANES = D / 8;
-  constexpr int ROWS = kWave / LANES;
-  constexpr int NS = NR + (REF ? 1 : 0);
-  constexpr int NRA = NR > 0 ? NR : 1;
-  constexpr int TILE = ROWS * TR;
-  constexpr int STEP = W * TILE;
-  constexpr int REC = 2 * D + 2;
-  static_assert(W >= NS, "one merging wave per loop slot");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane % LANES, r = lane / LANES;
-  const int split = blockIdx.x, bh = blockIdx.y;
-  const int t_begin = split * a.tps;
-  const int t_end = min(t_begin + a.tps, a.n_ctx);
-  const int G = D / a.group;
-  const int gshift = __builtin_ctz((unsigned)G);     // meta words per token = 2^gshift
-  const int k = j / (a.group / 8);
-
-  // Plane bases of this (batch, head): uniform, so they live in SGPRs and
-  // every load is base + 32-bit lane offset.
-  const size_t row0 = (size_t)bh * a.cap;
-  const uint16_t *kref = a.kref + row0 * D;
-  const uint16_t *vref = a.vref + row0 * D;
-  const uint8_t *kc[NRA], *vc[NRA];
-  const uint32_t *km[NRA], *vm[NRA];
-  const uint16_t *ka[NRA], *va[NRA];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int cb = ((B4 >> i) & 1) ? D / 2 : D / 4;
-    kc[i] = a.kc[i] + row0 * cb;
-    vc[i] = a.vc[i] + row0 * cb;
-    km[i] = a.km[i] + row0 * G;
-    vm[i] = a.vm[i] + row0 * G;
-    ka[i] = a.ka[i] + row0;
-    va[i] = a.va[i] + row0;
-  }
-
-  // ---- prologue: queries of every loop in the pass -------------------------
-  // Reference dots use the BF16 query pairs as stored; residual dots use
-  // q' = H_n q in FP32, each element pre-multiplied by 2^(24 - pos) for its
-  // code's position in code_halves.  Scores are scaled by sm_scale*log2(e)
-  // after the row sum.
-  uint32_t qb[NS][4];
-  float qr[NRA][8], sig[NRA];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
-    qb[s][0] = w.x; qb[s][1] = w.y; qb[s][2] = w.z; qb[s][3] = w.w;
-  }
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    float f[8];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(qb[i][p]); f[2 * p + 1] = bf16hi(qb[i][p]); }
-    if (a.rotate) wht8<D>(f, lane);
-    float tot = 0.0f;
-    const bool int4 = (B4 >> i) & 1;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const float v = f[p] * a.rot_c;
-      tot += v;
-      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
-      qr[i][p] = v * (float)(1 << (24 - pos));
-    }
-    sig[i] = tot;
-  }
-
-  // Softmax state: m per loop slot (uniform across a row); the running sum of
-  // loop slot own = j % 4 only, kept by the lanes that compute that slot's
-  // exponentials (lane j of a quad computes slot j's weight; the quad shares
-  // the four weights through DPP).
-  const int own = j & 3;
-  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    m[s] = -FLT_MAX;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < NRA; ++i) {
-    zacc[i] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
-  }
-
-  auto load = [&](Tile<TR, NRA> &T, int base) {
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      const uint32_t t = (uint32_t)min(base + u * ROWS + r, t_end - 1);
-      T.yk[u] = ldg<uint4>(kref, t * (2 * D) + 16 * j);
-      T.yv[u] = ldg<uint4>(vref, t * (2 * D) + 16 * j);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if ((B4 >> i) & 1) {
-          T.kc[u][i] = ldg<uint32_t>(kc[i], t * (D / 2) + 4 * j);
-          T.vc[u][i] = ldg<uint32_t>(vc[i], t * (D / 2) + 4 * j);
-        } else {
-          T.kc[u][i] = ldg<uint16_t>(kc[i], t * (D / 4) + 2 * j);
-          T.vc[u][i] = ldg<uint16_t>(vc[i], t * (D / 4) + 2 * j);
-        }
-        T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
-        T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
-        T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
-        T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
-      }
-    }
-  };
-
-  auto process = [&](const Tile<TR, NRA> &T, int base, auto full_tile) {
-    constexpr bool FULL = decltype(full_tile)::value;
-    // scores (log2 units)
-    float sc[TR][NS];
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      // Partial scores of this lane's 8 dims, in units of 1/qscale: the
-      // reference dots are exact BF16 products; the residual dots and their
-      // offset terms carry q' without the softmax scale, and the FP16 scale,
-      // zero and LS coefficient enter v_fma_mix_f32 as stored.
-      float part[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float dy = dot2bf0(qb[s][0], T.yk[u].x);
-        dy = dot2bf(qb[s][1], T.yk[u].y, dy);
-        dy = dot2bf(qb[s][2], T.yk[u].z, dy);
-        part[s] = dot2bf(qb[s][3], T.yk[u].w, dy);
-      }
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const float dc = ((B4 >> i) & 1) ? code_dot<true>(T.kc[u][i], qr[i], 0.0f)
-                                         : code_dot<false>(T.kc[u][i], qr[i], 0.0f);
-        const uint32_t mw = T.km[u][i];
-        const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
-        part[i] = __builtin_fmaf(h_lo(T.ka[u][i]), part[i], t);
-      }
-      const bool valid = FULL || base + u * ROWS + r < t_end;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
-        sc[u][s] = FULL ? tot : (valid ? tot : -INFINITY);
-      }
-    }
-
-    // online softmax; rescale only when the max grows by more than the slack
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      float mt = sc[0][s];
-#pragma unroll
-      for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u][s]);
-      if (mt > m[s] + kRescaleSlack) {
-        const float f = fexp2(m[s] - mt);
-        m[s] = mt;
-        if (own == s) l_own *= f;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) oref[s][p] *= f;
-        if (s < NR) {
-          zacc[s] *= f;
-#pragma unroll
-          for (int p = 0; p < 8; ++p) ores[s][p] *= f;
-        }
-      }
-    }
-
-    // values
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      const float y[8] = {bf16lo(T.yv[u].x), bf16hi(T.yv[u].x), bf16lo(T.yv[u].y), bf16hi(T.yv[u].y),
-                          bf16lo(T.yv[u].z), bf16hi(T.yv[u].z), bf16lo(T.yv[u].w), bf16hi(T.yv[u].w)};
-      // one exponential per lane (slot own), shared across the quad
-      float x = sc[u][0] - m[0];
-#pragma unroll
-      for (int s = 1; s < NS; ++s) {
-        const float xs = sc[u][s] - m[s];
-        x = own == s ? xs : x;
-      }
-      const float p_own = fexp2(x);
-      l_own += p_own;
-      float pq[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pq[s] = quad_bcast(p_own, s);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float pr = pq[s];
-        if (s < NR) {
-          const uint32_t mw = T.vm[u][s];
-          const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
-          const float wq = __builtin_fmaf(h_lo(mw), pr, 0.0f);
-          zacc[s] = __builtin_fmaf(h_hi(mw), pr, zacc[s]);
-#pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
-          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], wq, ores[s]);
-          else code_axpy<false>(T.vc[u][s], wq, ores[s]);
-        } else {
-#pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
-        }
-      }
-    }
-  };
-
-  // ---- token tiles: two tile buffers, the next one loading while the other
-  // is processed.  The next tile is always loaded (its token indices clamped
-  // into the split), so the loads are straight-line code and the wait before
-  // processing a tile covers only that tile's loads.
-  int base = t_begin + wave * TILE;
-  if (base < t_end) {
-    Tile<TR, NRA> ta, tb;
-    load(ta, base);
-    while (true) {
-      load(tb, base + STEP);
-      if (base + TILE <= t_end) process(ta, base, std::true_type{});
-      else process(ta, base, std::false_type{});
-      base += STEP;
-      if (base >= t_end) break;
-      load(ta, base + STEP);
-      if (base + TILE <= t_end) process(tb, base, std::true_type{});
-      else process(tb, base, std::false_type{});
-      base += STEP;
-      if (base >= t_end) break;
-    }
-  }
-
-  // undo the 2^(pos-24) factors of the value codes, add the offsets' share
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const bool int4 = (B4 >> i) & 1;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
-      ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - pos)), zacc[i]);
-    }
-  }
-
-  // ---- merge rows, then waves -----------------------------------------------
-  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l_own, own, oref, ores);
-
-  __shared__ float sm[W][NS][REC];
-  if (r == 0) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (j == 0) sm[wave][s][0] = m[s];
-      if (j == s) sm[wave][s][1] = l_own;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
-      if (s < NR) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
-      }
-    }
-  }
-  __syncthreads();
-  // wave s combines loop slot s over the W waves
-  if (wave < NS) {
-    const int s = wave;
-    const bool residual = s < NR;
-    float M = sm[0][s][0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w][s][0]);
-    float f[W];
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) { f[w] = fexp2(sm[w][s][0] - M); L = __builtin_fmaf(f[w], sm[w][s][1], L); }
-    constexpr int E = D / 64;
-    float o[E], q[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      o[e] = 0.0f; q[e] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        o[e] = __builtin_fmaf(f[w], sm[w][s][2 + lane + 64 * e], o[e]);
-        if (residual) q[e] = __builtin_fmaf(f[w], sm[w][s][2 + D + lane + 64 * e], q[e]);
-      }
-    }
-    if (a.n_splits == 1) {
-      finish_row<D>(a, bh, s, residual, lane, L, o, q);
-    } else {
-      float *rec = a.ws + (((size_t)split * kMaxSlots + s) * a.bh + bh) * REC;
-      if (lane == 0) { rec[0] = M; rec[1] = L; }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        rec[2 + lane + 64 * e] = o[e];
-        if (residual) rec[2 + D + lane + 64 * e] = q[e];
-      }
-    }
-  }
-}
-
 // Kernel M: one wave per (batch*head, loop slot): log-sum-exp over the
-// splits' records, then finish_row.
+// splits' records and, when there is one, the BF16 tail of the slot's loop
+// (walked token by token, original domain), then finish_row.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, int n_res) {
   constexpr int E = D / 64;
@@ -519,12 +22,42 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, in
   for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
   M = group_max<64>(M);
 
+  float mt = -FLT_MAX, lt = 0.0f, ot[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ot[e] = 0.0f;
+  if (a.n_tail > 0) {
+    const uint16_t *qrow = a.q + ((size_t)a.qloop[s] * a.bh + bh) * D;
+    const uint16_t *tk = a.tk[s] + (size_t)bh * a.tcap * D;
+    const uint16_t *tv = a.tv[s] + (size_t)bh * a.tcap * D;
+    float qv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[e] = bf16lo(qrow[lane + 64 * e]);
+    for (int t = 0; t < a.n_tail; ++t) {
+      float dp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dp = __builtin_fmaf(qv[e], bf16lo(tk[(size_t)t * D + lane + 64 * e]), dp);
+      const float sc = group_sum<64>(dp) * a.qscale;
+      if (sc > mt) {
+        const float f = fexp2(mt - sc);
+        lt *= f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) ot[e] *= f;
+        mt = sc;
+      }
+      const float p = fexp2(sc - mt);
+      lt += p;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ot[e] = __builtin_fmaf(p, bf16lo(tv[(size_t)t * D + lane + 64 * e]), ot[e]);
+    }
+  }
+  const float Mall = fmaxf(M, mt);
+
   float L = 0.0f, o[E], q[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) { o[e] = 0.0f; q[e] = 0.0f; }
   for (int sp = 0; sp < a.n_splits; ++sp) {
     const float *rec = rec0 + sp * stride;
-    const float f = fexp2(rec[0] - M);
+    const float f = fexp2(rec[0] - Mall);
     L = __builtin_fmaf(f, rec[1], L);
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(f, rec[2 + lane + 64 * e], o[e]);
@@ -533,67 +66,29 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, in
       for (int e = 0; e < E; ++e) q[e] = __builtin_fmaf(f, rec[2 + D + lane + 64 * e], q[e]);
     }
   }
-  finish_row<D>(a, bh, s, residual, lane, L, o, q);
+  const float ft = fexp2(mt - Mall);
+  L = __builtin_fmaf(ft, lt, L);
+#pragma unroll
+  for (int e = 0; e < E; ++e) ot[e] *= ft;
+  finish_row<D>(a, bh, s, residual, lane, L, o, q, ot);
 }
 
-// Tiles per wave iteration and waves per workgroup.  Four waves (the fewest
-// that give every loop slot its own merging wave) let two workgroups share a
-// compute unit, so one workgroup's merge overlaps the other's streaming.
-constexpr int kTilesPerIter = 2;
-constexpr int kWaves = 4;
-
-template <int D, int NR, bool REF, int B4>
-static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
-  const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, kTilesPerIter, kWaves>), grid, block, 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.bh, NR + (REF ? 1 : 0)), dim3(64), 0, st, a, NR);
+hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t st) {
+  const dim3 grid(a.bh, n_slots), block(64);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, st, a, n_res); break;
+    case 128: hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, st, a, n_res); break;
+    case 256: hipLaunchKernelGGL(decode_merge_kernel<256>, grid, block, 0, st, a, n_res); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
-}
-
-// Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
-template <int D, int NR, bool REF>
-static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
-  int b4 = 0;
-  for (int i = 0; i < NR; ++i) b4 |= (a.bits[i] == 4) << i;
-  switch (b4) {
-    case 0: return launch_kernel<D, NR, REF, 0>(a, st);
-    case 1: if constexpr (NR >= 1) return launch_kernel<D, NR, REF, 1>(a, st); break;
-    case 2: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 2>(a, st); break;
-    case 3: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 3>(a, st); break;
-    case 4: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 4>(a, st); break;
-    case 5: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 5>(a, st); break;
-    case 6: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 6>(a, st); break;
-    case 7: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 7>(a, st); break;
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int D>
-static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
-  if (ref) {
-    switch (n_res) {
-      case 0: return launch_bits<D, 0, true>(a, st);
-      case 1: return launch_bits<D, 1, true>(a, st);
-      case 2: return launch_bits<D, 2, true>(a, st);
-      case 3: return launch_bits<D, 3, true>(a, st);
-    }
-  } else {
-    switch (n_res) {
-      case 1: return launch_bits<D, 1, false>(a, st);
-      case 2: return launch_bits<D, 2, false>(a, st);
-      case 3: return launch_bits<D, 3, false>(a, st);
-    }
-  }
-  return hipErrorInvalidValue;
 }
 
 template <int D>
 static int blocks_per_cu_d() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves>, 64 * kWaves, 0) != hipSuccess)
+          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0>, 64 * kWaves, 0) != hipSuccess)
     return -1;
   return n;
 }
@@ -607,11 +102,14 @@ int decode_blocks_per_cu(int head_dim) {
   }
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
-  switch (head_dim) {
-    case 64: return launch_decode_d<64>(a, n_res, ref, st);
-    case 128: return launch_decode_d<128>(a, n_res, ref, st);
-    case 256: return launch_decode_d<256>(a, n_res, ref, st);
+template hipError_t launch_decode_aq<0>(const DecodeArgs &, int, int, bool, hipStream_t);
+
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
+                         hipStream_t st) {
+  switch (anchor_bits) {
+    case 0: return launch_decode_aq<0>(a, head_dim, n_res, ref, st);
+    case 2: return launch_decode_aq<2>(a, head_dim, n_res, ref, st);
+    case 4: return launch_decode_aq<4>(a, head_dim, n_res, ref, st);
     default: return hipErrorInvalidValue;
   }
 }

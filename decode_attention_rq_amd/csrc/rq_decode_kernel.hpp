@@ -1,0 +1,674 @@
+// rq_decode_kernel.hpp -- fused decode attention over a ResidualQuant cache
+// (gfx950): the kernel template, included by the files that instantiate it
+// for a BF16 reference (rq_decode.hip) and for quantized anchors.
+//
+// ResidualQuant page ("ResidualQuant: KV Cache Quantization for Looped
+// Transformers with 2-Bit Residuals"), Abstract: decode reads each loop's
+// compressed cache (BF16 reference + low-bit residual) and the smaller
+// traffic is what speeds it up.  For loop l and token t, with y the
+// reference vector and u = z + s*code the rotated, quantized residual:
+//   key    k_t = aK_t y_t + H_n u_t        value  v_t = aV_t y_t + H_n u'_t
+// Because H_n is symmetric and orthonormal the rotation is folded:
+//   q . k_t      = aK_t (q . y_t) + sum_k [ s_k (q'_k . code_k) + z_k sum(q'_k) ]
+//   sum_t p_t v_t = sum_t (p_t aV_t) y_t + H_n sum_t p_t u'_t
+// with q' = H_n q, so the per-token work is the reference dot product, the
+// code dot products and FMA accumulation; H_n is applied once per output.
+//
+// Kernel P, one launch per pass of up to three residual loops: a workgroup
+// of W waves per (token split, batch*head), each wave taking every W-th tile
+// of ROWS*TR tokens.  Lanes: D/8 lanes per token, 8 consecutive dims per
+// lane, ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane
+// reads ROWS consecutive reference rows, and every loop of the pass shares
+// that load.  Online softmax per (row, loop) in the exp2 domain; rows, then
+// waves (through LDS), are merged by log-sum-exp.  With one split the
+// workgroup finishes the output itself (un-rotation of the residual
+// accumulator, normalisation); with several it writes one record per (split,
+// loop, batch*head) to the workspace and kernel M merges the records.
+
+#pragma once
+
+#include <float.h>
+
+#include <type_traits>
+
+#include "rq_device.hpp"
+#include "rq_internal.hpp"
+
+namespace rq {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Value of x in lane 4*(lane/4) + S (DPP quad_perm broadcast).
+__device__ __forceinline__ float quad_bcast(float x, int s) {
+  switch (s) {
+    case 0: return dpp<0x00>(x);
+    case 1: return dpp<0x55>(x);
+    case 2: return dpp<0xAA>(x);
+    default: return dpp<0xFF>(x);
+  }
+}
+
+// First product of a dot chain: the three-operand v_dot2_f32_bf16 with an
+// inline zero accumulator (the builtin would zero a register first).
+__device__ __forceinline__ float dot2bf0(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+
+// Merge the online-softmax states of rows at lane distance MASK.  The lane's
+// running sum l_own belongs to loop slot `own` (lane index mod 4).
+template <int MASK, int NS, int NR>
+__device__ __forceinline__ void merge_rows(float (&m)[NS], float &l_own, int own, float (&oref)[NS][8],
+                                           float (&ores)[NR > 0 ? NR : 1][8]) {
+  const float lo = xor_lane<MASK>(l_own);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float mo = xor_lane<MASK>(m[s]);
+    const float M = fmaxf(m[s], mo);
+    const float fa = fexp2(m[s] - M), fb = fexp2(mo - M);
+    if (own == s) l_own = l_own * fa + lo * fb;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) oref[s][p] = oref[s][p] * fa + xor_lane<MASK>(oref[s][p]) * fb;
+    if (s < NR) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) ores[s][p] = ores[s][p] * fa + xor_lane<MASK>(ores[s][p]) * fb;
+    }
+    m[s] = M;
+  }
+}
+
+// Output row of one (loop slot, batch*head), lane holding dims lane + 64*e:
+// out = (o_ref + H_n o_res + t) / l, where o_ref accumulates the reference
+// (BF16 rows, or the anchor), o_res the residual codes and t the BF16 tail
+// rows.  When the anchor is itself rotated, o_ref joins o_res before the
+// un-rotation.  H_n runs as butterflies across lanes (distances 1..32) and
+// across the lane's E = D/64 elements.
+template <int D>
+__device__ __forceinline__ void finish_row(const DecodeArgs &a, int bh, int s, bool residual, int lane,
+                                           float L, float (&o)[D / 64], float (&w)[D / 64],
+                                           const float (&t)[D / 64]) {
+  constexpr int E = D / 64;
+  const bool ref_rot = a.ref_rotated != 0;
+  if (residual || ref_rot) {
+    if (ref_rot) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        w[e] = residual ? w[e] + o[e] : o[e];
+        o[e] = 0.0f;
+      }
+    }
+    if (a.rotate) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        w[e] = wht_stage<1>(w[e], lane);
+        w[e] = wht_stage<2>(w[e], lane);
+        w[e] = wht_stage<4>(w[e], lane);
+        w[e] = wht_stage<8>(w[e], lane);
+        w[e] = wht_stage<16>(w[e], lane);
+        w[e] = wht_stage<32>(w[e], lane);
+      }
+#pragma unroll
+      for (int h = 1; h < E; h *= 2) {
+#pragma unroll
+        for (int e0 = 0; e0 < E; e0 += 2 * h) {
+#pragma unroll
+          for (int e = e0; e < e0 + h; ++e) {
+            const float x = w[e], y = w[e + h];
+            w[e] = x + y;
+            w[e + h] = x - y;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[e] *= a.rot_c;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += w[e];
+  }
+  const float invL = 1.0f / L;
+  float *out = a.out + ((size_t)a.qloop[s] * a.bh + bh) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[lane + 64 * e] = (o[e] + t[e]) * invL;
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// fma(a, h, c) where h is one half of `w` read as an FP16 number (v_fma_mix_f32
+// takes the half directly, no conversion instruction).
+template <int HI>
+__device__ __forceinline__ float fma_half(float a, uint32_t w, float c) {
+  const half2_t h = __builtin_bit_cast(half2_t, w);
+  return __builtin_fmaf(a, (float)h[HI], c);
+}
+
+// The 8 codes of one lane as 8 FP16 halves, each holding one code in its
+// mantissa bits: a half whose bit pattern is c << b (b + width <= 10) is the
+// subnormal number c * 2^(b-24), exact.  Code p lands in half (p / 4) of word
+// w[p % 4] for INT2 and in half (p / 4) of word w[p % 4] for INT4 as well,
+// at mantissa bit position pos(p) (see code_pos).
+//   INT2 (16-bit word x, code p at bits 2p): bytes x0 = c0..c3, x1 = c4..c7 are
+//   spread to the two halves, then masked per code.
+//   INT4 (32-bit word x, code p at bits 4p): halves already hold c0..c3 and
+//   c4..c7; codes 2, 3 (6, 7) are shifted down by 8 bits first.
+template <bool INT4>
+__device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
+  if constexpr (INT4) {
+    const uint32_t y = x >> 8;
+    w[0] = x & 0x000F000Fu;
+    w[1] = x & 0x00F000F0u;
+    w[2] = y & 0x000F000Fu;
+    w[3] = y & 0x00F000F0u;
+  } else {
+    const uint32_t X = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [x.b0, 0, x.b1, 0]
+    w[0] = X & 0x00030003u;
+    w[1] = X & 0x000C000Cu;
+    w[2] = X & 0x00300030u;
+    w[3] = X & 0x00C000C0u;
+  }
+}
+
+// Mantissa bit position of code p in its half (so its half reads c * 2^(pos-24)).
+template <bool INT4>
+__host__ __device__ constexpr int code_pos(int p) {
+  return INT4 ? 4 * (p & 1) : 2 * (p & 3);
+}
+
+// Sum over the lane's 8 codes of coef[p] * half_p  (coef pre-multiplied by
+// 2^(24 - pos) makes this sum_p coef'[p] * c_p).
+template <bool INT4>
+__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fma_half<0>(coef[q], w[q], acc);
+    acc = fma_half<1>(coef[q + 4], w[q], acc);
+  }
+  return acc;
+}
+
+// acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
+template <bool INT4>
+__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = fma_half<0>(wgt, w[q], acc[q]);
+    acc[q + 4] = fma_half<1>(wgt, w[q], acc[q + 4]);
+  }
+}
+
+// The low / high FP16 half of a 32-bit word, for use as an fma operand
+// (v_fma_mix_f32 reads it in place).
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
+
+// Load from a uniform base plus a 32-bit byte offset (global_load with an
+// SGPR base and a 32-bit VGPR offset; no 64-bit address arithmetic per lane).
+template <typename T>
+__device__ __forceinline__ T ldg(const void *base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// Reference part of a token tile: BF16 rows (AQ = 0), or a quantized
+// anchor's code word and (scale, zero) word per lane (AQ = its bit width).
+template <int TR, int AQ>
+struct RefTile {
+  uint32_t ak[TR], av[TR], amk[TR], amv[TR];
+};
+template <int TR>
+struct RefTile<TR, 0> {
+  uint4 yk[TR], yv[TR];
+};
+
+template <int TR, int NRA, int AQ>
+struct Tile : RefTile<TR, AQ> {
+  uint32_t kc[TR][NRA], km[TR][NRA], ka[TR][NRA], vc[TR][NRA], vm[TR][NRA], va[TR][NRA];
+};
+
+// The lane's 8 anchor values z + s*code (FP32; the anchor's own domain,
+// rotated when the layout rotates) from its code word and (scale, zero) word.
+// Codes enter v_fma_mix_f32 as FP16 subnormals (see code_halves); the scale
+// carries the matching 2^(24 - pos).
+template <bool INT4>
+__device__ __forceinline__ void anchor_values(uint32_t x, uint32_t mw, float (&y)[8]) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+  const float s = h_lo(mw);
+  const float sc0 = s * 16777216.0f;                       // 2^24
+  const float sc1 = INT4 ? s * 1048576.0f : s * 4194304.0f; // 2^20 | 2^22
+  const float sc2 = s * 1048576.0f;                        // 2^20 (INT2)
+  const float sc3 = s * 262144.0f;                         // 2^18 (INT2)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float sq = INT4 ? ((q & 1) ? sc1 : sc0) : (q == 0 ? sc0 : q == 1 ? sc1 : q == 2 ? sc2 : sc3);
+    y[q] = __builtin_fmaf(h_lo(w[q]), sq, h_hi(mw));
+    y[q + 4] = __builtin_fmaf(h_hi(w[q]), sq, h_hi(mw));
+  }
+}
+
+// Scores above the running max by more than this (log2 units) trigger a
+// rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int NR, bool REF, int B4, int TR, int W, int AQ>
+__global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
+  constexpr int LANES = D / 8;
+  constexpr int ROWS = kWave / LANES;
+  constexpr int NS = NR + (REF ? 1 : 0);
+  constexpr int NRA = NR > 0 ? NR : 1;
+  constexpr int TILE = ROWS * TR;
+  constexpr int STEP = W * TILE;
+  constexpr int REC = 2 * D + 2;
+  static_assert(W >= NS, "one merging wave per loop slot");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LANES, r = lane / LANES;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int t_begin = split * a.tps;
+  const int t_end = min(t_begin + a.tps, a.n_ctx);
+  const int G = D / a.group;
+  const int gshift = __builtin_ctz((unsigned)G);     // meta words per token = 2^gshift
+  const int k = j / (a.group / 8);
+  constexpr bool AINT4 = AQ == 4;
+  const int ashift = __builtin_ctz((unsigned)(D / a.agroup));   // anchor meta words per token
+  const int ka_ = j / (a.agroup / 8);                           // this lane's anchor group
+
+  // Plane bases of this (batch, head): uniform, so they live in SGPRs and
+  // every load is base + 32-bit lane offset.
+  const size_t row0 = (size_t)bh * a.cap;
+  const uint16_t *kref = a.kref + row0 * D;
+  const uint16_t *vref = a.vref + row0 * D;
+  const uint8_t *kac = a.kac + row0 * (D * (AQ > 0 ? AQ : 1) / 8);
+  const uint8_t *vac = a.vac + row0 * (D * (AQ > 0 ? AQ : 1) / 8);
+  const uint32_t *kam = a.kam + (row0 << ashift);
+  const uint32_t *vam = a.vam + (row0 << ashift);
+  const uint8_t *kc[NRA], *vc[NRA];
+  const uint32_t *km[NRA], *vm[NRA];
+  const uint16_t *ka[NRA], *va[NRA];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int cb = ((B4 >> i) & 1) ? D / 2 : D / 4;
+    kc[i] = a.kc[i] + row0 * cb;
+    vc[i] = a.vc[i] + row0 * cb;
+    km[i] = a.km[i] + row0 * G;
+    vm[i] = a.vm[i] + row0 * G;
+    ka[i] = a.ka[i] + row0;
+    va[i] = a.va[i] + row0;
+  }
+
+  // ---- prologue: queries of every loop in the pass -------------------------
+  // BF16 reference: its dots use the BF16 query pairs as stored (qb).
+  // Quantized anchor: its dots use q' (= H_n q when rotated) in FP32 (qf).
+  // Residual dots use q' in FP32, each element pre-multiplied by 2^(24 - pos)
+  // for its code's position in code_halves (qr).  Scores are scaled by
+  // sm_scale*log2(e) after the row sum.
+  constexpr int NQB = AQ ? 1 : NS;
+  constexpr int NQF = AQ ? NS : 1;
+  uint32_t qb[NQB][4];
+  float qf[NQF][8];
+  float qr[NRA][8], sig[NRA];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+    const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (!AQ) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) qb[s][p] = wq[p];
+    }
+    if (AQ || s < NR) {
+      float f[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(wq[p]); f[2 * p + 1] = bf16hi(wq[p]); }
+      if (a.rotate) wht8<D>(f, lane);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) f[p] = f[p] * a.rot_c;
+      if constexpr (AQ > 0) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) qf[s < NQF ? s : 0][p] = f[p];
+      }
+      if (s < NR) {
+        const int i = s < NRA ? s : 0;
+        float tot = 0.0f;
+        const bool int4 = (B4 >> i) & 1;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          tot += f[p];
+          const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
+          qr[i][p] = f[p] * (float)(1 << (24 - pos));
+        }
+        sig[i] = tot;
+      }
+    }
+  }
+
+  // Softmax state: m per loop slot (uniform across a row); the running sum of
+  // loop slot own = j % 4 only, kept by the lanes that compute that slot's
+  // exponentials (lane j of a quad computes slot j's weight; the quad shares
+  // the four weights through DPP).
+  const int own = j & 3;
+  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    m[s] = -FLT_MAX;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NRA; ++i) {
+    zacc[i] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
+  }
+
+  auto load = [&](Tile<TR, NRA, AQ> &T, int base) {
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      const uint32_t t = (uint32_t)min(base + u * ROWS + r, t_end - 1);
+      if constexpr (AQ == 0) {
+        T.yk[u] = ldg<uint4>(kref, t * (2 * D) + 16 * j);
+        T.yv[u] = ldg<uint4>(vref, t * (2 * D) + 16 * j);
+      } else {
+        if constexpr (AINT4) {
+          T.ak[u] = ldg<uint32_t>(kac, t * (D / 2) + 4 * j);
+          T.av[u] = ldg<uint32_t>(vac, t * (D / 2) + 4 * j);
+        } else {
+          T.ak[u] = ldg<uint16_t>(kac, t * (D / 4) + 2 * j);
+          T.av[u] = ldg<uint16_t>(vac, t * (D / 4) + 2 * j);
+        }
+        T.amk[u] = ldg<uint32_t>(kam, ((t << ashift) + ka_) * 4);
+        T.amv[u] = ldg<uint32_t>(vam, ((t << ashift) + ka_) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if ((B4 >> i) & 1) {
+          T.kc[u][i] = ldg<uint32_t>(kc[i], t * (D / 2) + 4 * j);
+          T.vc[u][i] = ldg<uint32_t>(vc[i], t * (D / 2) + 4 * j);
+        } else {
+          T.kc[u][i] = ldg<uint16_t>(kc[i], t * (D / 4) + 2 * j);
+          T.vc[u][i] = ldg<uint16_t>(vc[i], t * (D / 4) + 2 * j);
+        }
+        T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
+        T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
+        T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
+        T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
+      }
+    }
+  };
+
+  auto process = [&](const Tile<TR, NRA, AQ> &T, int base, auto full_tile) {
+    constexpr bool FULL = decltype(full_tile)::value;
+    // scores (log2 units)
+    float sc[TR][NS];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      // Partial scores of this lane's 8 dims, in units of 1/qscale: the
+      // reference dots are exact BF16 products; the residual dots and their
+      // offset terms carry q' without the softmax scale, and the FP16 scale,
+      // zero and LS coefficient enter v_fma_mix_f32 as stored.
+      float part[NS];
+      if constexpr (AQ == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float dy = dot2bf0(qb[s][0], T.yk[u].x);
+          dy = dot2bf(qb[s][1], T.yk[u].y, dy);
+          dy = dot2bf(qb[s][2], T.yk[u].z, dy);
+          part[s] = dot2bf(qb[s][3], T.yk[u].w, dy);
+        }
+      } else {
+        float yk[8];
+        anchor_values<AINT4>(T.ak[u], T.amk[u], yk);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float dy = qf[s][0] * yk[0];
+#pragma unroll
+          for (int p = 1; p < 8; ++p) dy = __builtin_fmaf(qf[s][p], yk[p], dy);
+          part[s] = dy;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float dc = ((B4 >> i) & 1) ? code_dot<true>(T.kc[u][i], qr[i], 0.0f)
+                                         : code_dot<false>(T.kc[u][i], qr[i], 0.0f);
+        const uint32_t mw = T.km[u][i];
+        const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
+        part[i] = __builtin_fmaf(h_lo(T.ka[u][i]), part[i], t);
+      }
+      const bool valid = FULL || base + u * ROWS + r < t_end;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
+        sc[u][s] = FULL ? tot : (valid ? tot : -INFINITY);
+      }
+    }
+
+    // online softmax; rescale only when the max grows by more than the slack
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float mt = sc[0][s];
+#pragma unroll
+      for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u][s]);
+      if (mt > m[s] + kRescaleSlack) {
+        const float f = fexp2(m[s] - mt);
+        m[s] = mt;
+        if (own == s) l_own *= f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+        if (s < NR) {
+          zacc[s] *= f;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+        }
+      }
+    }
+
+    // values
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      float y[8];
+      if constexpr (AQ == 0) {
+        y[0] = bf16lo(T.yv[u].x); y[1] = bf16hi(T.yv[u].x);
+        y[2] = bf16lo(T.yv[u].y); y[3] = bf16hi(T.yv[u].y);
+        y[4] = bf16lo(T.yv[u].z); y[5] = bf16hi(T.yv[u].z);
+        y[6] = bf16lo(T.yv[u].w); y[7] = bf16hi(T.yv[u].w);
+      } else {
+        anchor_values<AINT4>(T.av[u], T.amv[u], y);
+      }
+      // one exponential per lane (slot own), shared across the quad
+      float x = sc[u][0] - m[0];
+#pragma unroll
+      for (int s = 1; s < NS; ++s) {
+        const float xs = sc[u][s] - m[s];
+        x = own == s ? xs : x;
+      }
+      const float p_own = fexp2(x);
+      l_own += p_own;
+      float pq[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pq[s] = quad_bcast(p_own, s);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float pr = pq[s];
+        if (s < NR) {
+          const uint32_t mw = T.vm[u][s];
+          const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
+          const float wq = __builtin_fmaf(h_lo(mw), pr, 0.0f);
+          zacc[s] = __builtin_fmaf(h_hi(mw), pr, zacc[s]);
+#pragma unroll
+          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
+          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], wq, ores[s]);
+          else code_axpy<false>(T.vc[u][s], wq, ores[s]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
+        }
+      }
+    }
+  };
+
+  // ---- token tiles: two tile buffers, the next one loading while the other
+  // is processed.  The next tile is always loaded (its token indices clamped
+  // into the split), so the loads are straight-line code and the wait before
+  // processing a tile covers only that tile's loads.
+  int base = t_begin + wave * TILE;
+  if (base < t_end) {
+    Tile<TR, NRA, AQ> ta, tb;
+    load(ta, base);
+    while (true) {
+      load(tb, base + STEP);
+      if (base + TILE <= t_end) process(ta, base, std::true_type{});
+      else process(ta, base, std::false_type{});
+      base += STEP;
+      if (base >= t_end) break;
+      load(ta, base + STEP);
+      if (base + TILE <= t_end) process(tb, base, std::true_type{});
+      else process(tb, base, std::false_type{});
+      base += STEP;
+      if (base >= t_end) break;
+    }
+  }
+
+  // undo the 2^(pos-24) factors of the value codes, add the offsets' share
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const bool int4 = (B4 >> i) & 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
+      ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - pos)), zacc[i]);
+    }
+  }
+
+  // ---- merge rows, then waves -----------------------------------------------
+  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l_own, own, oref, ores);
+
+  __shared__ float sm[W][NS][REC];
+  if (r == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (j == 0) sm[wave][s][0] = m[s];
+      if (j == s) sm[wave][s][1] = l_own;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
+      if (s < NR) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
+      }
+    }
+  }
+  __syncthreads();
+  // wave s combines loop slot s over the W waves
+  if (wave < NS) {
+    const int s = wave;
+    const bool residual = s < NR;
+    float M = sm[0][s][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w][s][0]);
+    float f[W];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) { f[w] = fexp2(sm[w][s][0] - M); L = __builtin_fmaf(f[w], sm[w][s][1], L); }
+    constexpr int E = D / 64;
+    float o[E], q[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      o[e] = 0.0f; q[e] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        o[e] = __builtin_fmaf(f[w], sm[w][s][2 + lane + 64 * e], o[e]);
+        if (residual) q[e] = __builtin_fmaf(f[w], sm[w][s][2 + D + lane + 64 * e], q[e]);
+      }
+    }
+    if (!a.records) {
+      float none[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) none[e] = 0.0f;
+      finish_row<D>(a, bh, s, residual, lane, L, o, q, none);
+    } else {
+      float *rec = a.ws + (((size_t)split * kMaxSlots + s) * a.bh + bh) * REC;
+      if (lane == 0) { rec[0] = M; rec[1] = L; }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        rec[2 + lane + 64 * e] = o[e];
+        if (residual) rec[2 + D + lane + 64 * e] = q[e];
+      }
+    }
+  }
+}
+
+
+// Tiles per wave iteration and waves per workgroup.  Four waves (the fewest
+// that give every loop slot its own merging wave) let two workgroups share a
+// compute unit, so one workgroup's merge overlaps the other's streaming.
+constexpr int kTilesPerIter = 2;
+constexpr int kWaves = 4;
+
+template <int D, int NR, bool REF, int B4, int AQ>
+static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
+  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, kTilesPerIter, kWaves, AQ>), grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.records) return e;
+  return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);
+}
+
+// Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
+template <int D, int NR, bool REF, int AQ>
+static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
+  int b4 = 0;
+  for (int i = 0; i < NR; ++i) b4 |= (a.bits[i] == 4) << i;
+  switch (b4) {
+    case 0: return launch_kernel<D, NR, REF, 0, AQ>(a, st);
+    case 1: if constexpr (NR >= 1) return launch_kernel<D, NR, REF, 1, AQ>(a, st); break;
+    case 2: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 2, AQ>(a, st); break;
+    case 3: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 3, AQ>(a, st); break;
+    case 4: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 4, AQ>(a, st); break;
+    case 5: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 5, AQ>(a, st); break;
+    case 6: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 6, AQ>(a, st); break;
+    case 7: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 7, AQ>(a, st); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, int AQ>
+static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
+  if (ref) {
+    switch (n_res) {
+      case 0: return launch_bits<D, 0, true, AQ>(a, st);
+      case 1: return launch_bits<D, 1, true, AQ>(a, st);
+      case 2: return launch_bits<D, 2, true, AQ>(a, st);
+      case 3: return launch_bits<D, 3, true, AQ>(a, st);
+    }
+  } else {
+    switch (n_res) {
+      case 1: return launch_bits<D, 1, false, AQ>(a, st);
+      case 2: return launch_bits<D, 2, false, AQ>(a, st);
+      case 3: return launch_bits<D, 3, false, AQ>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits).
+template <int AQ>
+hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_decode_d<64, AQ>(a, n_res, ref, st);
+    case 128: return launch_decode_d<128, AQ>(a, n_res, ref, st);
+    case 256: return launch_decode_d<256, AQ>(a, n_res, ref, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rq

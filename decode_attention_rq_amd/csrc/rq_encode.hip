@@ -4,6 +4,9 @@
 // Transformers with 2-Bit Residuals"), Fig. 1 steps 2-5: every earlier loop's
 // K/V vector becomes a least-squares-scaled residual against the final loop,
 // is rotated, and is quantized per group of g dims at that loop's bit width.
+// With a quantized anchor (Fig. 3 caption, "Ascending [2,2,2,4]"; Table 8
+// caption) the final loop is first quantized the same way (no LS
+// coefficient) and the residuals are taken against its dequantized value.
 //
 // Mapping: one head_dim vector per D/8 consecutive lanes, 8 consecutive dims
 // per lane (one 128-bit load), 64/(D/8) tokens per wave.  A wave handles all
@@ -43,6 +46,49 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 w, float (&f)[8]) {
   f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
 }
 
+// Group quantization of the lane's 8 values (already rotated if the layout
+// rotates): canonicalise -0 to +0, group min/max over the gl lanes of the
+// group, FP16 scale and offset, codes by round-half-even of (u - z) * (1/s)
+// clamped to the grid.  Returns the packed code word (code p at bits
+// [bits*p, +bits)); q receives the codes as floats.
+__device__ __forceinline__ uint32_t quantize8(float (&u)[8], int bits, int gl, uint32_t &s16,
+                                              uint32_t &z16, float (&q)[8]) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) u[p] = u[p] + 0.0f;   // -0 -> +0
+  float mn = u[0], mx = u[0];
+#pragma unroll
+  for (int p = 1; p < 8; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
+  if (gl == 4) { mn = group_min<4>(mn); mx = group_max<4>(mx); }
+  else         { mn = group_min<2>(mn); mx = group_max<2>(mx); }
+  const float levels = (float)((1 << bits) - 1);
+  s16 = f32_to_f16_sat((mx - mn) / levels);
+  z16 = f32_to_f16_sat(mn);
+  const float s = f16_to_f32(s16);
+  const float z = f16_to_f32(z16);
+  uint32_t word = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) q[p] = 0.0f;
+  if (s != 0.0f) {
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      float c = __builtin_rintf((u[p] - z) * inv);
+      c = fminf(fmaxf(c, 0.0f), levels);
+      q[p] = c;
+      word |= (uint32_t)c << (bits * p);
+    }
+  }
+  return word;
+}
+
+template <int D>
+__device__ __forceinline__ void store_codes(uint8_t *plane, size_t slot, int j, int bits, uint32_t word) {
+  if (bits == 2)
+    reinterpret_cast<uint16_t *>(plane + slot * (D / 4))[j] = (uint16_t)word;
+  else
+    reinterpret_cast<uint32_t *>(plane + slot * (D / 2))[j] = word;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   constexpr int LANES = D / 8;
@@ -64,10 +110,39 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   const int gl = a.group / 8;                        // lanes per group
 
   float y[8];
-  unpack_bf16x8(*reinterpret_cast<const uint4 *>(S.ref + slot * D + 8 * j), y);
+  if (a.abits == 0) {
+    unpack_bf16x8(*reinterpret_cast<const uint4 *>(S.ref + slot * D + 8 * j), y);
+  } else {
+    // the anchor: loop L-1 of the input, quantized like a residual (groups of
+    // agroup, no LS coefficient); y becomes its dequantized value
+    const uint16_t *yp = S.xin + (((size_t)a.n_res * a.bh + bh) * a.n + tlc) * D + 8 * j;
+    unpack_bf16x8(*reinterpret_cast<const uint4 *>(yp), y);
+    if (a.rotate) {
+      wht8<D>(y, lane);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) y[p] = y[p] * a.rot_c;
+    }
+    uint32_t s16, z16;
+    float q[8];
+    const int agl = a.agroup / 8;
+    const uint32_t word = quantize8(y, a.abits, agl, s16, z16, q);
+    if (valid) {
+      const size_t oslot = (size_t)bh * a.cap + (size_t)(a.t0 + tl);
+      store_codes<D>(S.codes[a.n_res], oslot, j, a.abits, word);
+      if (j % agl == 0) S.meta[a.n_res][oslot * (D / a.agroup) + j / agl] = s16 | (z16 << 16);
+    }
+    const float s = f16_to_f32(s16), z = f16_to_f32(z16);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) y[p] = __builtin_fmaf(q[p], s, z);
+    if (a.rotate) {
+      wht8<D>(y, lane);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) y[p] = y[p] * a.rot_c;
+    }
+  }
   float t[8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) t[p] = y[p] * y[p];    // exact: bf16 * bf16
+  for (int p = 0; p < 8; ++p) t[p] = y[p] * y[p];    // exact for a BF16 y
   const float den = dot_sum<LANES>(t);
 
   for (int l = 0; l < a.n_res; ++l) {
@@ -89,37 +164,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 #pragma unroll
       for (int p = 0; p < 8; ++p) u[p] = u[p] * a.rot_c;
     }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) u[p] = u[p] + 0.0f;   // -0 -> +0
-
-    float mn = u[0], mx = u[0];
-#pragma unroll
-    for (int p = 1; p < 8; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
-    if (gl == 4) { mn = group_min<4>(mn); mx = group_max<4>(mx); }
-    else         { mn = group_min<2>(mn); mx = group_max<2>(mx); }
-
     const int bits = a.bits[l];
-    const float levels = (float)((1 << bits) - 1);
-    const uint32_t s16 = f32_to_f16_sat((mx - mn) / levels);
-    const uint32_t z16 = f32_to_f16_sat(mn);
-    const float s = f16_to_f32(s16);
-    const float z = f16_to_f32(z16);
-    uint32_t word = 0;
-    if (s != 0.0f) {
-      const float inv = 1.0f / s;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        float q = __builtin_rintf((u[p] - z) * inv);
-        q = fminf(fmaxf(q, 0.0f), levels);
-        word |= (uint32_t)q << (bits * p);
-      }
-    }
+    uint32_t s16, z16;
+    float q[8];
+    const uint32_t word = quantize8(u, bits, gl, s16, z16, q);
     if (valid) {
       const size_t oslot = (size_t)bh * a.cap + (size_t)(a.t0 + tl);
-      if (bits == 2)
-        reinterpret_cast<uint16_t *>(S.codes[l] + oslot * (D / 4))[j] = (uint16_t)word;
-      else
-        reinterpret_cast<uint32_t *>(S.codes[l] + oslot * (D / 2))[j] = word;
+      store_codes<D>(S.codes[l], oslot, j, bits, word);
       if (j % gl == 0) S.meta[l][oslot * G + j / gl] = s16 | (z16 << 16);
       if (j == 0) S.alpha[l][oslot] = (uint16_t)a16;
     }

@@ -11,10 +11,10 @@ namespace rq {
 
 // Kernel argument blocks.  Plane pointers are per residual loop.
 struct EncodeSide {
-  const uint16_t *ref;               // bf16 [BH][cap][D]
-  const uint16_t *xin;               // bf16 [L-1][BH][n][D]
-  uint8_t *codes[RQ_MAX_LOOPS];
-  uint32_t *meta[RQ_MAX_LOOPS];      // (scale | zero << 16) per group
+  const uint16_t *ref;               // bf16 [BH][cap][D] (BF16 reference)
+  const uint16_t *xin;               // bf16 [L-1][BH][n][D]; [L][BH][n][D] with an anchor
+  uint8_t *codes[RQ_MAX_LOOPS];      // [L-1]: the anchor's codes
+  uint32_t *meta[RQ_MAX_LOOPS];      // (scale | zero << 16) per group; [L-1]: the anchor's
   uint16_t *alpha[RQ_MAX_LOOPS];
 };
 
@@ -29,32 +29,44 @@ struct EncodeArgs {
   float rot_c;                       // fp32(1/sqrt(D))
   int32_t chunks;                    // ceil(n / vectors per wave)
   int32_t tasks_per_side;            // bh * chunks
+  int32_t abits;                     // 0: BF16 reference; 2, 4: quantized anchor
+  int32_t agroup;                    // the anchor's group size
 };
 
 struct ReconArgs {
-  const uint16_t *ref;
-  const uint8_t *codes;
+  const uint16_t *ref;               // BF16 reference (abits == 0)
+  const uint8_t *acodes;             // quantized anchor (abits > 0)
+  const uint32_t *ameta;
+  const uint8_t *codes;              // the loop's planes (NULL: the anchor itself)
   const uint32_t *meta;
   const uint16_t *alpha;
   float *out;                        // f32 [BH][n][D]
   int32_t bits, bh, cap, t0, n, group, rotate;
   float rot_c;
   int32_t chunks;
+  int32_t abits, agroup;
 };
 
 constexpr int kMaxRes = 3;           // residual loops per decode pass
 constexpr int kMaxSlots = 4;         // residual loops + the reference loop
 
 struct DecodeArgs {
-  const uint16_t *kref, *vref;       // bf16 [BH][cap][D]
+  const uint16_t *kref, *vref;       // bf16 [BH][cap][D] (BF16 reference)
+  const uint8_t *kac, *vac;          // quantized anchor codes [BH][cap][D*abits/8]
+  const uint32_t *kam, *vam;         // and (scale | zero << 16) [BH][cap][D/agroup]
+  int32_t agroup;
+  int32_t ref_rotated;               // the anchor is stored rotated (anchor and rotate)
   const uint8_t *kc[kMaxRes], *vc[kMaxRes];
   const uint32_t *km[kMaxRes], *vm[kMaxRes];
   const uint16_t *ka[kMaxRes], *va[kMaxRes];
   int32_t bits[kMaxRes];
   const uint16_t *q;                 // bf16 [L][BH][D]
   int32_t qloop[kMaxSlots];          // slot -> loop index (residual slots first)
-  float *ws;                         // f32 [S][kMaxSlots][BH][2D+2] split records (S > 1)
+  float *ws;                         // f32 [S][kMaxSlots][BH][2D+2] split records
   float *out;                        // f32 [L][BH][D]
+  const uint16_t *tk[kMaxSlots], *tv[kMaxSlots];   // BF16 tail rows per slot [BH][tcap][D]
+  int32_t tcap, n_tail;
+  int32_t records;                   // write split records and merge (S > 1 or a tail)
   int32_t bh, cap, n_ctx, n_splits, tps;
   int32_t group, rotate;
   float qscale;                      // sm_scale * log2(e)
@@ -63,7 +75,15 @@ struct DecodeArgs {
 
 hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
+// One decode pass of n_res residual loops (+ the reference loop if ref);
+// anchor_bits 0 for a BF16 reference.  Launches the merge kernel too when
+// a.records is set.
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
+                         hipStream_t s);
+template <int AQ>
+hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
+// The split/tail merge for n_slots loop slots, the first n_res of them residual.
+hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t s);
 // Decode workgroups of this head_dim resident per compute unit at once (the
 // occupancy of the main decode kernel), or <= 0 on a HIP error.
 int decode_blocks_per_cu(int head_dim);

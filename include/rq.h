@@ -13,8 +13,18 @@
  * every loop, over that loop's cache reconstructed from the reference and its
  * residual (Abstract: the smaller cache is read with less memory traffic).
  *
+ * The reference may instead be stored as a quantized anchor: the pages' final
+ * configuration keeps the last loop at INT4 too ("Ascending [2,2,2,4]", Fig. 3
+ * caption; one INT4 anchor per loop group, Table 8 caption; INT4 anchor at
+ * g=32 with INT2 residuals at g=16, Fig. 6 caption).  The earlier loops' residuals
+ * are then taken against the dequantized anchor.  Recent tokens whose
+ * earlier-loop K/V cannot be encoded yet (their final loop has not run) can be
+ * attended from BF16 rows (a "tail", Table 10: recent BF16 tokens), see
+ * rq_decode_attn_tail.
+ *
  * Conventions for every entry point:
- *   - Loops are numbered 0 .. n_loops-1; loop n_loops-1 is the BF16 reference.
+ *   - Loops are numbered 0 .. n_loops-1; loop n_loops-1 is the reference (BF16,
+ *     or the quantized anchor when layout.ref_bits > 0).
  *   - All data pointers are DEVICE pointers on the current HIP device, except
  *     the rq_layout / rq_cache structs themselves, which are host memory and
  *     are only read during the call.
@@ -32,6 +42,8 @@
  *              bits [bits*(i % (8/bits)), +bits) of byte i*bits/8
  *       meta   f16  [batch][heads][cap][head_dim/group][2]   (scale, zero)
  *       alpha  f16  [batch][heads][cap]
+ *     A quantized anchor uses codes[L-1] and meta[L-1] (its own bits and group)
+ *     and has no alpha plane and no ref plane.
  *   - Non-finite inputs are not supported (results unspecified, no fault).
  */
 #ifndef RQ_H_
@@ -66,14 +78,22 @@ typedef struct {
     int32_t capacity;            /* token slots per (batch, head) in every plane, >= 1 */
     int32_t rotate;              /* 1: normalized Hadamard rotation of residuals; 0: none */
     int32_t bits[RQ_MAX_LOOPS];  /* bits[l] in {2, 4} for l < L-1 (entry L-1 unused)  */
+    int32_t ref_bits;            /* 0: loop L-1 is the BF16 ref plane; 2 or 4: loop L-1
+                                    is a quantized anchor in codes[L-1] / meta[L-1]  */
+    int32_t ref_group;           /* the anchor's group size, 16 or 32 (0 = group);
+                                    ignored when ref_bits == 0                        */
 } rq_layout;
 
 /* One side (K or V) of one layer's cache: caller-owned device planes.
- * Entries l >= L-1 of the arrays are ignored. */
+ * Entries l >= L-1 of the arrays are ignored, except codes[L-1] and meta[L-1]
+ * with a quantized anchor. */
 typedef struct {
-    void *ref;                   /* bf16 [B][H][cap][d], written by the caller      */
-    void *codes[RQ_MAX_LOOPS];   /* u8   [B][H][cap][d*bits[l]/8]                  */
-    void *meta[RQ_MAX_LOOPS];    /* f16  [B][H][cap][d/g][2]                       */
+    void *ref;                   /* bf16 [B][H][cap][d], written by the caller;
+                                    unused (may be NULL) with a quantized anchor   */
+    void *codes[RQ_MAX_LOOPS];   /* u8   [B][H][cap][d*bits[l]/8]; [L-1]: anchor
+                                    codes [B][H][cap][d*ref_bits/8]                */
+    void *meta[RQ_MAX_LOOPS];    /* f16  [B][H][cap][d/g][2]; [L-1]: anchor
+                                    [B][H][cap][d/ref_group][2]                    */
     void *alpha[RQ_MAX_LOOPS];   /* f16  [B][H][cap]                               */
 } rq_cache;
 
@@ -98,11 +118,23 @@ typedef struct {
  *     (u canonicalized to +0 where it is -0; all codes 0 if s = 0)
  * The result is bit-identical to that FP32 definition.
  *
- *   k, v    caches; their ref planes must already hold tokens [t0, t0+n)
- *   k_in    bf16 [L-1][B][H][n][d] contiguous: the new K vectors of loops 0..L-2
+ * With a quantized anchor (ref_bits > 0) the reference vector y (the BF16
+ * input of loop L-1) is first quantized the same way -- rotated if rotate,
+ * groups of ref_group, ref_bits codes, no alpha -- and the residual loops use
+ * its dequantized value instead of y:
+ *   y_hat = fp32(1/sqrt(d)) * H_d u_hat (or u_hat without rotation), with
+ *   u_hat = fma(code, s, z) per element (FP32, s and z as stored)
+ * (the dot products then sum rounded FP32 products).
+ *
+ *   k, v    caches; with a BF16 reference their ref planes must already hold
+ *           tokens [t0, t0+n)
+ *   k_in    bf16 [L-1][B][H][n][d] contiguous: the new K vectors of loops 0..L-2;
+ *           with a quantized anchor [L][B][H][n][d], loop L-1 (the anchor's
+ *           input) last
  *   v_in    same for V
  *   t0, n   0 <= t0, 0 <= n, t0 + n <= capacity (n = 0 is a no-op)
- * Writes codes/meta/alpha of loops 0..L-2 at slots [t0, t0+n); nothing else.
+ * Writes codes/meta/alpha of loops 0..L-2 (and the anchor's codes/meta) at
+ * slots [t0, t0+n); nothing else.
  */
 rq_status rq_encode(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
                     const void *k_in, const void *v_in, int32_t t0, int32_t n,
@@ -111,7 +143,8 @@ rq_status rq_encode(const rq_layout *layout, const rq_cache *k, const rq_cache *
 /*
  * rq_decode_workspace_bytes -- bytes of scratch rq_decode_attn needs for
  * `n_ctx` tokens and `n_splits` token splits (0 = the split count the library
- * would choose, see rq_decode_splits).  Returns 0 for an invalid layout.
+ * would choose, see rq_decode_splits); also enough for rq_decode_attn_tail.
+ * 0 <= n_ctx <= capacity.  Returns 0 for an invalid layout.
  */
 size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_ctx, int32_t n_splits);
 
@@ -126,7 +159,8 @@ int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
  *   out[l][b][h] = softmax(sm_scale * q[l][b][h] . K_l^T) V_l
  * over tokens [0, n_ctx), where K_l, V_l are loop l's keys and values
  * reconstructed as alpha*y + H_n (z + s*code) (the reference itself for loop
- * L-1).  ResidualQuant page, Abstract: decode attention over every loop's
+ * L-1; with a quantized anchor y is the dequantized anchor, and loop L-1
+ * attends over it).  ResidualQuant page, Abstract: decode attention over every loop's
  * compressed cache.  The rotation is applied to the query and to the
  * accumulated output instead of to every key and value (H_n is symmetric and
  * orthonormal), and the reference is read once for all loops in the mask.
@@ -148,11 +182,41 @@ rq_status rq_decode_attn(const rq_layout *layout, const rq_cache *k, const rq_ca
                          int32_t n_splits, float *out, void *workspace,
                          size_t workspace_bytes, void *hip_stream);
 
+/* Recent tokens kept in BF16, per loop (host struct, read-only).  Loop l's
+ * rows are its own K and V, not residuals. */
+typedef struct {
+    const void *k[RQ_MAX_LOOPS]; /* bf16 [B][H][capacity][d]; NULL for loops not in the mask */
+    const void *v[RQ_MAX_LOOPS]; /* same for V                                          */
+    int32_t capacity;            /* token slots per (batch, head) of every tail plane   */
+    int32_t n;                   /* tail tokens [0, n) attended, 0 <= n <= capacity      */
+} rq_tail;
+
+/*
+ * rq_decode_attn_tail -- rq_decode_attn over the n_ctx cached tokens followed
+ * by tail->n BF16 tokens: for every loop l in the mask and every (b, h),
+ *   out[l][b][h] = softmax(sm_scale * q . [K_l ; Kt_l]^T) [V_l ; Vt_l]
+ * with Kt_l, Vt_l the tail rows tail->k[l][b][h][0 .. n).  This is the
+ * per-loop decode of a looped model: a token's earlier loops run before its
+ * final loop, so its own K/V (and those of recent tokens) are not encoded yet
+ * and are attended in BF16 (ResidualQuant page, Table 10: recent tokens kept
+ * in BF16).  Arguments as for rq_decode_attn, except:
+ *   tail       NULL or a tail; tail->n == 0 makes this call rq_decode_attn
+ *   n_ctx      0 <= n_ctx <= capacity, n_ctx + tail->n >= 1 (n_ctx = 0: the
+ *              tail alone; no cache plane is read)
+ * The tail is meant for tens of tokens: one wave per (row) walks it.
+ */
+rq_status rq_decode_attn_tail(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
+                              const rq_tail *tail, const void *q, uint32_t loop_mask,
+                              int32_t n_ctx, float sm_scale, int32_t n_splits, float *out,
+                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /*
  * rq_reconstruct -- dequantize loop `loop` (< L-1) for tokens [t0, t0+n):
  *   out[b][h][t - t0] = alpha*y + H_n (z + s*code)          (FP32)
  * ResidualQuant page, Abstract (the residual form keeps reconstruction
  * cheap).  out is f32 [B][H][n][d]; 0 <= t0, 1 <= n, t0 + n <= capacity.
+ * With a quantized anchor y is the dequantized anchor, and loop = L-1 is
+ * allowed: it returns the dequantized anchor itself.
  */
 rq_status rq_reconstruct(const rq_layout *layout, const rq_cache *c, int32_t loop,
                          int32_t t0, int32_t n, float *out, void *hip_stream);

@@ -41,12 +41,14 @@ class Workload:
     layers: int = 1
     steps: int = 0                  # append-decode steps after the prefill
     seed: int = 0
+    ref_bits: int = 0               # 0: BF16 reference; 2/4: quantized anchor
+    ref_group: int = 0              # the anchor's group size (0: g)
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads: a tiny CPU-checkable case, the 8k-context INT2 decode,
-# mixed precision with appends, 32k context over 24 layers, and the 8k
-# peak-batch sweep.
+# The workloads: a tiny CPU-checkable case, the 8k-context INT2 decode,
+# mixed precision with appends, 32k context over 24 layers, the 8k
+# peak-batch sweep, and per-loop decode with a quantized anchor.
 WORKLOADS = {
     "tiny": Workload("tiny", n_loops=2, batch=1, heads=1, d=64, g=32, n_ctx=128,
                      bits=[2], c=[0.9], sigma=[0.1], rotate=0, seed=0),
@@ -62,6 +64,13 @@ WORKLOADS = {
     "peak-batch-8k": Workload("peak-batch-8k", n_loops=4, batch=0, heads=16, d=128, g=32,
                               n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
                               sigma=[0.15, 0.12, 0.1], rotate=1, layers=24, seed=4),
+    # The pages' final configuration: [2,2,2,4] with an INT4 anchor at g=32 and
+    # INT2 residuals at g=16, decoded loop by loop as a looped model runs,
+    # with the 64 most recent tokens in BF16.
+    "anchor-8k-perloop": Workload("anchor-8k-perloop", n_loops=4, batch=16, heads=16, d=128, g=16,
+                                  n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
+                                  sigma=[0.15, 0.12, 0.1], rotate=1, seed=5, ref_bits=4,
+                                  ref_group=32, extra={"tail": 64}),
 }
 
 
@@ -115,6 +124,21 @@ def draw_layer(w: Workload, seed: Optional[int] = None, batch: Optional[int] = N
     q = draw_queries(gen, w.n_loops, B, w.heads, w.d)
     return dict(k_ref=k_ref, k_loops=k_loops, v_ref=v_ref, v_loops=v_loops, q=q,
                 k_std=k_std, v_std=v_std)
+
+
+def draw_tail(w: Workload, seed: int, batch: Optional[int] = None, n: int = 64,
+              device: str = "cpu") -> dict:
+    """Recent tokens kept in BF16: every loop's own K and V for n tokens,
+    drawn like the cache (loop l = c_l * final loop + noise).  Returns
+    dict(k, v), each bf16 [L, B, H, n, d] with the final loop last."""
+    gen = generator(seed, device)
+    B = w.batch if batch is None else batch
+    out = {}
+    for side in ("k", "v"):
+        std = channel_std(gen, w.heads, w.d)
+        ref, loops = draw_kv(gen, w.n_loops, B, w.heads, n, w.d, w.c, w.sigma, std)
+        out[side] = torch.cat([loops, ref.unsqueeze(0)]).contiguous()
+    return out
 
 
 def bf16_bits(t: torch.Tensor):

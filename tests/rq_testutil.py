@@ -20,13 +20,22 @@ def tol_rel_row(got: np.ndarray, want: np.ndarray) -> np.ndarray:
 
 def oracle_layout(w: synth.Workload, batch: int, cap: int) -> dict:
     return dict(n_loops=w.n_loops, batch=batch, heads=w.heads, d=w.d, g=w.g, cap=cap,
-                rotate=w.rotate, bits=list(w.bits))
+                rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits, ref_group=w.ref_group)
 
 
 def gpu_layout(w: synth.Workload, batch: int, cap: int):
     import decode_attention_rq_amd as rq
     return rq.Layout(n_loops=w.n_loops, batch=batch, n_heads=w.heads, head_dim=w.d, group=w.g,
-                     capacity=cap, rotate=w.rotate, bits=list(w.bits))
+                     capacity=cap, rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits,
+                     ref_group=w.ref_group)
+
+
+def encoder_input(w: synth.Workload, loops: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
+    """rq_encode's input: the residual loops, plus the anchor's own input
+    last when the reference is a quantized anchor."""
+    if w.ref_bits:
+        return torch.cat([loops, ref.unsqueeze(0)])
+    return loops
 
 
 class Case:
@@ -43,11 +52,12 @@ class Case:
         self.lay = gpu_layout(w, self.B, self.cap)
         self.k = rq.Cache(self.lay, device)
         self.v = rq.Cache(self.lay, device)
-        self.k.ref[:, :, :n] = self.data["k_ref"].to(device)
-        self.v.ref[:, :, :n] = self.data["v_ref"].to(device)
+        if not w.ref_bits:
+            self.k.ref[:, :, :n] = self.data["k_ref"].to(device)
+            self.v.ref[:, :, :n] = self.data["v_ref"].to(device)
         self.q = self.data["q"].to(device).contiguous()
-        kin = self.data["k_loops"].to(device)
-        vin = self.data["v_loops"].to(device)
+        kin = encoder_input(w, self.data["k_loops"], self.data["k_ref"]).to(device)
+        vin = encoder_input(w, self.data["v_loops"], self.data["v_ref"]).to(device)
         chunks = t_chunks or [(0, n)]
         for t0, cnt in chunks:
             rq.rq_encode(self.lay, self.k, self.v, kin[:, :, :, t0:t0 + cnt].contiguous(),
@@ -75,8 +85,8 @@ class Case:
                 idx[ax + 1] = hi
                 return t[tuple(idx)].unsqueeze(ax + 1)
         lay = oracle_layout(w, B, n)
-        kp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits)
-        vp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits)
+        kp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None)
+        vp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None)
         if bh_list is None:
             kr, vr, kl, vl, q = (self.data["k_ref"], self.data["v_ref"], self.data["k_loops"],
                                  self.data["v_loops"], self.data["q"])
@@ -85,10 +95,14 @@ class Case:
             kl, vl = sel(self.data["k_loops"], 1).cpu(), sel(self.data["v_loops"], 1).cpu()
             q = sel(self.data["q"], 1).cpu()
         lay["heads"] = H
-        kp.ref[:] = bf16_bits(kr)
-        vp.ref[:] = bf16_bits(vr)
-        oracle.encode(lay, kp, bf16_bits(kl), 0, n)
-        oracle.encode(lay, vp, bf16_bits(vl), 0, n)
+        if w.ref_bits:
+            oracle.encode(lay, kp, bf16_bits(encoder_input(w, kl, kr)), 0, n)
+            oracle.encode(lay, vp, bf16_bits(encoder_input(w, vl, vr)), 0, n)
+        else:
+            kp.ref[:] = bf16_bits(kr)
+            vp.ref[:] = bf16_bits(vr)
+            oracle.encode(lay, kp, bf16_bits(kl), 0, n)
+            oracle.encode(lay, vp, bf16_bits(vl), 0, n)
         return lay, kp, vp, bf16_bits(q)
 
 

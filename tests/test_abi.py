@@ -27,8 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["rq_encode", "rq_decode_workspace_bytes", "rq_decode_splits",
-                            "rq_decode_attn", "rq_reconstruct", "rq_status_string",
-                            "rq_bf16_decode_attn"])
+                            "rq_decode_attn", "rq_decode_attn_tail", "rq_reconstruct",
+                            "rq_status_string", "rq_bf16_decode_attn"])
 
 
 def test_library_exports_every_declared_symbol(rq):
@@ -168,8 +168,10 @@ def test_workspace_size_formula(rq):
     assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 2) == 2 * 4 * 4 * 258 * 4
     # more splits than tokens are clamped to one token per split
     assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 3, 8) == 3 * 4 * 4 * 258 * 4
-    # one split needs no records (a token 256 bytes)
-    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 1) == 256
+    # one split still has room for its records (written when a BF16 tail follows)
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 32, 1) == 1 * 4 * 4 * 258 * 4
+    # no cached tokens (a tail alone): one split's worth
+    assert rq._lib.rq_decode_workspace_bytes(C.byref(lay), 0, 1) == 1 * 4 * 4 * 258 * 4
 
 
 @pytest.mark.parametrize("loop,t0,n", [(-1, 0, 4), (3, 0, 4), (0, -1, 4), (0, 0, 0), (0, 62, 4)])
@@ -191,3 +193,79 @@ def test_bf16_baseline_validation(rq):
     assert f(C.byref(lay), planes, planes, FAKE, 1, 65, 0.1, 2, FAKE, FAKE, 1 << 30, None) == INVALID
     # loop 1's null plane is not looked at when loop 1 is not in the mask
     assert f(C.byref(lay), planes, bad, FAKE, 0b1101, 32, 0.1, 2, FAKE, FAKE, 1, None) == WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# quantized anchor and BF16 tail
+# ---------------------------------------------------------------------------
+
+def _anchor_cache(rq, n_loops=4, bad=None):
+    c = _cache(rq, n_loops, bad=bad)
+    if not bad or bad[0] != "ref":
+        c.ref = 0                       # unused with a quantized anchor
+    if not (bad and bad[1] == n_loops - 1):
+        c.codes[n_loops - 1] = FAKE + 0x7000
+        c.meta[n_loops - 1] = FAKE + 0x700000
+    return c
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ref_bits=3), UNSUPPORTED), (dict(ref_bits=8), UNSUPPORTED), (dict(ref_bits=-1), UNSUPPORTED),
+    (dict(ref_bits=4, ref_group=8), UNSUPPORTED), (dict(ref_bits=4, ref_group=64), UNSUPPORTED),
+])
+def test_anchor_layout_validation(rq, kw, code):
+    lay = _layout(rq, **kw)
+    assert _encode(rq, lay, k=_anchor_cache(rq), v=_anchor_cache(rq)) == code
+    assert _decode(rq, lay, k=_anchor_cache(rq), v=_anchor_cache(rq)) == code
+
+
+@pytest.mark.parametrize("bad", [("codes", 3, 0), ("meta", 3, FAKE + 4), ("codes", 0, 0)])
+def test_anchor_planes_are_checked(rq, bad):
+    lay = _layout(rq, ref_bits=4, ref_group=32)
+    assert _encode(rq, lay, k=_anchor_cache(rq, bad=bad)) == INVALID
+    assert _decode(rq, lay, v=_anchor_cache(rq, bad=bad), k=_anchor_cache(rq)) == INVALID
+
+
+def test_anchor_needs_no_ref_plane(rq):
+    lay = _layout(rq, ref_bits=4, ref_group=32)
+    k, v = _anchor_cache(rq), _anchor_cache(rq)
+    assert k.ref is None or k.ref == 0
+    # everything else valid: the too-small workspace is the first complaint
+    assert _decode(rq, lay, k=k, v=v, ws_bytes=1) == WORKSPACE
+    # the anchor loop itself reconstructs with an anchor, never with BF16
+    L = lay.c()
+    assert rq._lib.rq_reconstruct(C.byref(L), C.byref(k), 3, 0, 4, FAKE + 8, None) == INVALID
+    assert rq._lib.rq_reconstruct(C.byref(L), C.byref(k), 4, 0, 4, FAKE, None) == INVALID
+
+
+def _tail(rq, n=4, cap=8, bad_loop=None):
+    t = rq.rq_tail()
+    for l in range(4):
+        t.k[l] = 0 if l == bad_loop else FAKE + 0x200 * (l + 1)
+        t.v[l] = FAKE + 0x400 * (l + 1)
+    t.capacity, t.n = cap, n
+    return t
+
+
+def _decode_tail(rq, lay, tail, mask=0b1111, n_ctx=32, splits=2, ws_bytes=1 << 30):
+    L = lay.c()
+    k, v = _cache(rq, lay.n_loops), _cache(rq, lay.n_loops)
+    return rq._lib.rq_decode_attn_tail(C.byref(L), C.byref(k), C.byref(v),
+                                       C.byref(tail) if tail is not None else None, FAKE, mask,
+                                       n_ctx, 0.1, splits, FAKE, FAKE, ws_bytes, None)
+
+
+def test_tail_validation(rq):
+    lay = _layout(rq)
+    assert _decode_tail(rq, lay, _tail(rq, n=-1)) == INVALID
+    assert _decode_tail(rq, lay, _tail(rq, n=9, cap=8)) == INVALID
+    assert _decode_tail(rq, lay, _tail(rq, bad_loop=2)) == INVALID
+    # a masked-out loop's tail rows are not looked at
+    assert _decode_tail(rq, lay, _tail(rq, bad_loop=2), mask=0b1011, ws_bytes=1) == WORKSPACE
+    # nothing to attend
+    assert _decode_tail(rq, lay, _tail(rq, n=0), n_ctx=0) == INVALID
+    assert _decode_tail(rq, lay, None, n_ctx=0) == INVALID
+    # the tail alone is valid (no split count is needed); the workspace still is
+    assert _decode_tail(rq, lay, _tail(rq), n_ctx=0, splits=0, ws_bytes=1) == WORKSPACE
+    # plain rq_decode_attn still needs a cached token
+    assert _decode(rq, lay, n_ctx=0) == INVALID
