@@ -46,12 +46,27 @@ def parse():
     return a
 
 
+def layout_bytes_per_token(n_loops: int, bits, g: int, d: int, ref_bits: int = 0,
+                           ref_group: int = 0) -> int:
+    """Bytes per (batch, head, token), K plus V, of the cache layout in
+    include/rq.h: the reference (BF16 rows, or anchor codes plus an FP16
+    scale and zero per group of ref_group) and, per residual loop, its codes,
+    an FP16 scale and zero per group of g and an FP16 LS coefficient."""
+    ref = 2 * d if not ref_bits else d * ref_bits // 8 + 4 * (d // (ref_group or g))
+    return 2 * (ref + sum(d * bits[l] // 8 + 4 * (d // g) + 2 for l in range(n_loops - 1)))
+
+
+def loop_read_bytes_per_token(bits: int, g: int, d: int, ref_bits: int = 0, ref_group: int = 0) -> int:
+    """Bytes per (batch, head, token), K plus V, that attending over ONE
+    residual loop on its own reads: the reference and that loop's planes."""
+    ref = 2 * d if not ref_bits else d * ref_bits // 8 + 4 * (d // (ref_group or g))
+    return 2 * (ref + d * bits // 8 + 4 * (d // g) + 2)
+
+
 def algorithmic_bytes_per_token(w) -> int:
-    """Bytes one decode step must read per (batch, head, token): the BF16
-    reference K and V once, and for each residual loop its codes, FP16
-    scale/zero per group and FP16 LS coefficient, for K and for V."""
-    from oracle.storage import layout_bytes_per_token
-    return layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
+    """Bytes one fused decode step must read per (batch, head, token): the
+    reference K and V once, and every residual loop's planes."""
+    return layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d, w.ref_bits, w.ref_group)
 
 
 def kernel_source_hash() -> str:
@@ -196,7 +211,6 @@ def append_bench(args, w):
     import torch
     import decode_attention_rq_amd as rq
     import synth
-    from oracle.storage import layout_bytes_per_token
 
     dev = "cuda"
     n0, steps = w.n_ctx, w.steps
@@ -278,7 +292,6 @@ def layers_bench(args, w):
     import torch
     import decode_attention_rq_amd as rq
     import synth
-    from oracle.storage import layout_bytes_per_token
 
     dev, n = "cuda", w.n_ctx
     lay = layout_of(w, w.batch, n)
@@ -349,7 +362,6 @@ def peak_batch_bench(args, w, budget=250e9):
     import torch
     import decode_attention_rq_amd as rq
     import synth
-    from oracle.storage import layout_bytes_per_token
 
     dev, n, L = "cuda", w.n_ctx, w.layers
     rq_per_b = L * w.heads * n * layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
@@ -440,6 +452,119 @@ def peak_batch_bench(args, w, budget=250e9):
     return res
 
 
+def anchor_bench(args, w):
+    """Per-loop decode with a quantized anchor (the pages' [2,2,2,4]: INT4
+    anchor at g=32, INT2 residuals at g=16) and the most recent tokens in
+    BF16.  A looped model runs its loops in sequence, so one decode step of a
+    layer is one attention call per loop, in loop order, each over the cached
+    tokens plus the tail: rq_decode_attn_tail with one loop in the mask.
+    Compared with BF16 per-loop decode over the same tokens (each loop's own
+    BF16 K and V), and with the fused call over all four loops."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+
+    dev, n, T, L = "cuda", w.n_ctx, w.extra["tail"], w.n_loops
+    B, H, d = w.batch, w.heads, w.d
+    lay = rq.Layout(L, B, H, d, w.g, n, w.rotate, w.bits, ref_bits=w.ref_bits, ref_group=w.ref_group)
+    scale = 1.0 / np.sqrt(d)
+    reps = []
+    for r in range(args.replicas):
+        dl = synth.draw_layer(w, seed=w.seed + 17 * r, device=dev)
+        k, v = rq.Cache(lay, dev, zero=False), rq.Cache(lay, dev, zero=False)
+        rq.rq_encode(lay, k, v, torch.cat([dl["k_loops"], dl["k_ref"][None]]),
+                     torch.cat([dl["v_loops"], dl["v_ref"][None]]), 0, n)
+        tl = synth.draw_tail(w, seed=w.seed + 17 * r + 1, n=T, device=dev)
+        tail = rq.Tail([tl["k"][l].contiguous() for l in range(L)], [tl["v"][l].contiguous() for l in range(L)], T)
+        reps.append((k, v, tail, dl["q"].contiguous()))
+        del dl, tl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    splits = args.splits or rq.rq_decode_splits(lay, n)
+    ws = rq.workspace_for(lay, n, splits, dev)
+    out = torch.empty(L, B, H, d, device=dev)
+
+    def step(i):
+        k, v, tail, q = reps[i % len(reps)]
+        for l in range(L):
+            rq.rq_decode_attn_tail(lay, k, v, tail, q, 1 << l, n, scale, out, ws, splits)
+
+    steps = args.steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # per-call events: the residual-loop calls are the dominant kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(steps)]
+    for i in range(steps):
+        k, v, tail, q = reps[i % len(reps)]
+        ev[i][0].record()
+        for l in range(L):
+            rq.rq_decode_attn_tail(lay, k, v, tail, q, 1 << l, n, scale, out, ws, splits)
+            ev[i][l + 1].record()
+    torch.cuda.synchronize()
+    call_ms = np.array([[ev[i][l].elapsed_time(ev[i][l + 1]) for l in range(L)] for i in range(steps)])
+    span_ms = ev[0][0].elapsed_time(ev[-1][L])
+    ms = span_ms / steps
+    tail_bytes = B * H * T * 2 * d * 2
+    res_call = B * H * n * loop_read_bytes_per_token(w.bits[0], w.g, d, w.ref_bits, w.ref_group) \
+        + tail_bytes + B * H * d * 2 + B * H * d * 4
+    anchor_call = B * H * n * 2 * (d * w.ref_bits // 8 + 4 * (d // w.ref_group)) + tail_bytes \
+        + B * H * d * 2 + B * H * d * 4
+    step_bytes = (L - 1) * res_call + anchor_call
+    res_us = float(call_ms[:, :L - 1].mean()) * 1e3
+    roof = {"bound": "hbm", "achieved": round(res_call / (res_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(res_call / (res_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "one residual loop's call: decode_kernel (1 residual loop, INT4 anchor) + merge with "
+                      "the BF16 tail",
+            "algorithmic_bytes_per_launch": res_call, "launch_us_mean": round(res_us, 2),
+            "anchor_loop_call_us_mean": round(float(call_ms[:, L - 1].mean()) * 1e3, 2)}
+    res = {"metric": "per-loop decode tokens/s, [2,2,2,4] INT4 anchor + INT2 residuals g=16, 8k ctx + 64 BF16 tail",
+           "value": round(B / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: 1 layer, batch {B}, {H} heads, head_dim {d}, {L} loops "
+                                  f"(INT{w.ref_bits} anchor g={w.ref_group}, residual bits {w.bits} g={w.g}), "
+                                  f"{n} cached tokens + {T} BF16 tail tokens, one call per loop",
+                      "splits": splits, "replicas": args.replicas},
+           "bytes_per_step": step_bytes, "hbm_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+           "frac_of_peak": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof}
+    # all four loops in one call (when every loop's query is known at once)
+    def fstep(i):
+        k, v, tail, q = reps[i % len(reps)]
+        rq.rq_decode_attn_tail(lay, k, v, tail, q, (1 << L) - 1, n, scale, out, ws, splits)
+    fms = timed(fstep, steps, 3)
+    fbytes = B * H * n * layout_bytes_per_token(L, w.bits, w.g, d, w.ref_bits, w.ref_group) + L * tail_bytes
+    res["fused_all_loops"] = {"ms_per_step": round(fms, 4), "tokens_per_s": round(B / (fms / 1e3), 1),
+                              "hbm_gbs": round(fbytes / (fms / 1e3) / 1e9, 1), "bytes_per_step": fbytes}
+    del reps
+    torch.cuda.empty_cache()
+    if not args.no_bf16_baseline:
+        nb = n + T
+        blay = layout_of(w, B, nb)
+        dl = synth.draw_layer(w, seed=w.seed + 999, n=nb, device=dev)
+        ks = [dl["k_loops"][l].clone() for l in range(L - 1)] + [dl["k_ref"]]
+        vs = [dl["v_loops"][l].clone() for l in range(L - 1)] + [dl["v_ref"]]
+        q = dl["q"].contiguous()
+        del dl
+        torch.cuda.empty_cache()
+        bsplits = rq.rq_decode_splits(blay, nb)
+        bws = rq.workspace_for(blay, nb, bsplits, dev)
+
+        def bstep(i):
+            for l in range(L):
+                rq.rq_bf16_decode_attn(blay, ks, vs, q, 1 << l, nb, scale, out, bws, bsplits)
+        bms = timed(bstep, steps, 3)
+        bbytes = L * B * H * nb * 2 * d * 2
+        res["bf16_baseline"] = {"value": round(B / (bms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(bms, 4),
+                                "hbm_gbs": round(bbytes / (bms / 1e3) / 1e9, 1), "bytes_per_step": bbytes,
+                                "kernel": "rq_bf16_decode_attn, one call per loop over its own BF16 K/V"}
+        res["speedup_vs_bf16"] = round(bms / ms, 3)
+        res["kv_bytes_ratio_vs_bf16"] = round(2 * L * d * 2 / layout_bytes_per_token(
+            L, w.bits, w.g, d, w.ref_bits, w.ref_group), 3)
+    return res
+
+
 def main():
     args = parse()
     if args.mode == "copy":
@@ -465,6 +590,9 @@ def main():
         return
     if args.workload == "peak-batch-8k":
         print(json.dumps(peak_batch_bench(args, w)), flush=True)
+        return
+    if args.workload == "anchor-8k-perloop":
+        print(json.dumps(anchor_bench(args, w)), flush=True)
         return
     dev = "cuda"
     lay = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, w.n_ctx, w.rotate, w.bits)

@@ -6,21 +6,21 @@
 
 namespace rq {
 
-// Kernel M: one wave per (batch*head, loop slot): log-sum-exp over the
-// splits' records and, when there is one, the BF16 tail of the slot's loop
-// (walked token by token, original domain), then finish_row.
+// Kernel M: one workgroup per (batch*head, loop slot).  Its waves share the
+// BF16 tail of the slot's loop (original domain): each wave takes batches of
+// kTailBatch tokens (loads issued together, reductions interleaved) with its
+// own online softmax; the waves' states meet in LDS.  Wave 0 then merges the
+// splits' records with the tail state by log-sum-exp and finishes the row.
+constexpr int kTailBatch = 8;
+constexpr int kMergeWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, int n_res) {
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const DecodeArgs a, int n_res) {
   constexpr int E = D / 64;
   constexpr int REC = 2 * D + 2;
-  const int bh = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int bh = blockIdx.x, s = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const bool residual = s < n_res;
-  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
-  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
-
-  float M = -FLT_MAX;
-  for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
-  M = group_max<64>(M);
 
   float mt = -FLT_MAX, lt = 0.0f, ot[E];
 #pragma unroll
@@ -32,24 +32,73 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, in
     float qv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) qv[e] = bf16lo(qrow[lane + 64 * e]);
-    for (int t = 0; t < a.n_tail; ++t) {
-      float dp = 0.0f;
+    for (int t0 = wave * kTailBatch; t0 < a.n_tail; t0 += nw * kTailBatch) {
+      float kk[kTailBatch][E], vv[kTailBatch][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) dp = __builtin_fmaf(qv[e], bf16lo(tk[(size_t)t * D + lane + 64 * e]), dp);
-      const float sc = group_sum<64>(dp) * a.qscale;
-      if (sc > mt) {
-        const float f = fexp2(mt - sc);
+      for (int i = 0; i < kTailBatch; ++i) {
+        const size_t row = (size_t)min(t0 + i, a.n_tail - 1) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kk[i][e] = bf16lo(tk[row + lane + 64 * e]);
+          vv[i][e] = bf16lo(tv[row + lane + 64 * e]);
+        }
+      }
+      float sc[kTailBatch];
+#pragma unroll
+      for (int i = 0; i < kTailBatch; ++i) {
+        float dp = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dp = __builtin_fmaf(qv[e], kk[i][e], dp);
+        sc[i] = group_sum<64>(dp) * a.qscale;
+      }
+      float mb = -FLT_MAX;
+#pragma unroll
+      for (int i = 0; i < kTailBatch; ++i) {
+        if (t0 + i >= a.n_tail) sc[i] = -INFINITY;
+        mb = fmaxf(mb, sc[i]);
+      }
+      if (mb > mt) {
+        const float f = fexp2(mt - mb);
         lt *= f;
 #pragma unroll
         for (int e = 0; e < E; ++e) ot[e] *= f;
-        mt = sc;
+        mt = mb;
       }
-      const float p = fexp2(sc - mt);
-      lt += p;
 #pragma unroll
-      for (int e = 0; e < E; ++e) ot[e] = __builtin_fmaf(p, bf16lo(tv[(size_t)t * D + lane + 64 * e]), ot[e]);
+      for (int i = 0; i < kTailBatch; ++i) {
+        const float p = fexp2(sc[i] - mt);
+        lt += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) ot[e] = __builtin_fmaf(p, vv[i][e], ot[e]);
+      }
     }
   }
+  __shared__ float sm[kMergeWaves][2 + D];
+  if (nw > 1) {
+    if (lane == 0) { sm[wave][0] = mt; sm[wave][1] = lt; }
+#pragma unroll
+    for (int e = 0; e < E; ++e) sm[wave][2 + lane + 64 * e] = ot[e];
+    __syncthreads();
+    if (wave != 0) return;
+    mt = sm[0][0];
+    for (int w = 1; w < nw; ++w) mt = fmaxf(mt, sm[w][0]);
+    lt = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ot[e] = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+      const float f = fexp2(sm[w][0] - mt);
+      lt = __builtin_fmaf(f, sm[w][1], lt);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ot[e] = __builtin_fmaf(f, sm[w][2 + lane + 64 * e], ot[e]);
+    }
+  }
+
+  // split records of this (slot, batch*head)
+  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
+  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
+  float M = -FLT_MAX;
+  for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
+  M = group_max<64>(M);
   const float Mall = fmaxf(M, mt);
 
   float L = 0.0f, o[E], q[E];
@@ -74,7 +123,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a, in
 }
 
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t st) {
-  const dim3 grid(a.bh, n_slots), block(64);
+  // one wave unless there is a tail to share out
+  const dim3 grid(a.bh, n_slots), block(a.n_tail > 0 ? 64 * kMergeWaves : 64);
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, st, a, n_res); break;
     case 128: hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, st, a, n_res); break;

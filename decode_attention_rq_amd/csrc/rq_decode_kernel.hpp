@@ -611,13 +611,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 // Tiles per wave iteration and waves per workgroup.  Four waves (the fewest
 // that give every loop slot its own merging wave) let two workgroups share a
 // compute unit, so one workgroup's merge overlaps the other's streaming.
+// A single-slot pass (one loop alone) moves few bytes per token, so its waves
+// keep four tiles in flight instead of two.
 constexpr int kTilesPerIter = 2;
 constexpr int kWaves = 4;
+template <int NS>
+constexpr int tiles_per_iter() { return NS == 1 ? 4 : kTilesPerIter; }
 
 template <int D, int NR, bool REF, int B4, int AQ>
 static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, kTilesPerIter, kWaves, AQ>), grid, block, 0, st, a);
+  constexpr int TR = tiles_per_iter<NR + (REF ? 1 : 0)>();
+  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
   return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);

@@ -61,3 +61,22 @@ def test_anchored_layout():
     assert storage.loop_read_bytes_per_token(2, 32, 128, ref_bits=4, ref_group=32) == 2 * (80 + 50)
     # with the BF16 reference, one loop alone reads more than its BF16 K and V
     assert storage.loop_read_bytes_per_token(2, 32, 128) == 2 * (256 + 50) > 512
+
+
+def test_bench_byte_accounting_matches():
+    """bench.py keeps its own byte accounting (it may not import the oracle
+    outside its CPU-baseline leg); it must agree with this module."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for args in [(4, [2, 2, 2], 32, 128), (4, [4, 2, 2], 32, 128), (2, [2], 32, 64), (6, [2, 4, 2, 2, 4], 16, 256)]:
+        assert bench.layout_bytes_per_token(*args) == storage.layout_bytes_per_token(*args)
+        for rb, rg in [(4, 32), (2, 16), (4, 16)]:
+            assert (bench.layout_bytes_per_token(*args, ref_bits=rb, ref_group=rg)
+                    == storage.layout_bytes_per_token(*args, ref_bits=rb, ref_group=rg))
+    for b, g, d in [(2, 16, 128), (4, 32, 128), (2, 32, 64)]:
+        assert bench.loop_read_bytes_per_token(b, g, d) == storage.loop_read_bytes_per_token(b, g, d)
+        assert (bench.loop_read_bytes_per_token(b, g, d, 4, 32)
+                == storage.loop_read_bytes_per_token(b, g, d, 4, 32))
