@@ -66,7 +66,9 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 
 // Merge the online-softmax states of rows at lane distance MASK.  The lane's
 // running sum l_own belongs to loop slot `own` (lane index mod 4).
-template <int MASK, int NS, int NR>
+// Slots below OREF_FROM carry no reference accumulator (with a quantized
+// anchor the residual slots fold the anchor into their residual one).
+template <int MASK, int NS, int NR, int OREF_FROM>
 __device__ __forceinline__ void merge_rows(float (&m)[NS], float &l_own, int own, float (&oref)[NS][8],
                                            float (&ores)[NR > 0 ? NR : 1][8]) {
   const float lo = xor_lane<MASK>(l_own);
@@ -76,8 +78,10 @@ __device__ __forceinline__ void merge_rows(float (&m)[NS], float &l_own, int own
     const float M = fmaxf(m[s], mo);
     const float fa = fexp2(m[s] - M), fb = fexp2(mo - M);
     if (own == s) l_own = l_own * fa + lo * fb;
+    if (s >= OREF_FROM) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) oref[s][p] = oref[s][p] * fa + xor_lane<MASK>(oref[s][p]) * fb;
+      for (int p = 0; p < 8; ++p) oref[s][p] = oref[s][p] * fa + xor_lane<MASK>(oref[s][p]) * fb;
+    }
     if (s < NR) {
 #pragma unroll
       for (int p = 0; p < 8; ++p) ores[s][p] = ores[s][p] * fa + xor_lane<MASK>(ores[s][p]) * fb;
@@ -153,20 +157,19 @@ __device__ __forceinline__ float fma_half(float a, uint32_t w, float c) {
 // The 8 codes of one lane as 8 FP16 halves, each holding one code in its
 // mantissa bits: a half whose bit pattern is c << b (b + width <= 10) is the
 // subnormal number c * 2^(b-24), exact.  Code p lands in half (p / 4) of word
-// w[p % 4] for INT2 and in half (p / 4) of word w[p % 4] for INT4 as well,
-// at mantissa bit position pos(p) (see code_pos).
+// w[p % 4] at mantissa bit position pos(p) = 2 * (p % 4), for INT2 and INT4
+// alike, so one set of 2^(24 - pos) factors serves every loop:
 //   INT2 (16-bit word x, code p at bits 2p): bytes x0 = c0..c3, x1 = c4..c7 are
 //   spread to the two halves, then masked per code.
-//   INT4 (32-bit word x, code p at bits 4p): halves already hold c0..c3 and
-//   c4..c7; codes 2, 3 (6, 7) are shifted down by 8 bits first.
+//   INT4 (32-bit word x, code p at bits 4p): the halves already hold c0..c3
+//   and c4..c7; code q of each half is shifted down by 2q bits, then masked.
 template <bool INT4>
 __device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
   if constexpr (INT4) {
-    const uint32_t y = x >> 8;
     w[0] = x & 0x000F000Fu;
-    w[1] = x & 0x00F000F0u;
-    w[2] = y & 0x000F000Fu;
-    w[3] = y & 0x00F000F0u;
+    w[1] = (x >> 2) & 0x003C003Cu;
+    w[2] = (x >> 4) & 0x00F000F0u;
+    w[3] = (x >> 6) & 0x03C003C0u;
   } else {
     const uint32_t X = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [x.b0, 0, x.b1, 0]
     w[0] = X & 0x00030003u;
@@ -177,17 +180,11 @@ __device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
 }
 
 // Mantissa bit position of code p in its half (so its half reads c * 2^(pos-24)).
-template <bool INT4>
-__host__ __device__ constexpr int code_pos(int p) {
-  return INT4 ? 4 * (p & 1) : 2 * (p & 3);
-}
+__host__ __device__ constexpr int code_pos(int p) { return 2 * (p & 3); }
 
-// Sum over the lane's 8 codes of coef[p] * half_p  (coef pre-multiplied by
-// 2^(24 - pos) makes this sum_p coef'[p] * c_p).
-template <bool INT4>
-__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
+// Sum over the lane's 8 codes (as halves w) of coef[p] * half_p (coef
+// pre-multiplied by 2^(24 - pos) makes this sum_p coef'[p] * c_p).
+__device__ __forceinline__ float code_dot_h(const uint32_t (&w)[4], const float (&coef)[8], float acc) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     acc = fma_half<0>(coef[q], w[q], acc);
@@ -196,16 +193,27 @@ __device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], fl
   return acc;
 }
 
-// acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
 template <bool INT4>
-__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
+__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
   uint32_t w[4];
   code_halves<INT4>(x, w);
+  return code_dot_h(w, coef, acc);
+}
+
+// acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
+__device__ __forceinline__ void code_axpy_h(const uint32_t (&w)[4], float wgt, float (&acc)[8]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     acc[q] = fma_half<0>(wgt, w[q], acc[q]);
     acc[q + 4] = fma_half<1>(wgt, w[q], acc[q + 4]);
   }
+}
+
+template <bool INT4>
+__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
+  uint32_t w[4];
+  code_halves<INT4>(x, w);
+  code_axpy_h(w, wgt, acc);
 }
 
 // The low / high FP16 half of a 32-bit word, for use as an fma operand
@@ -235,27 +243,6 @@ template <int TR, int NRA, int AQ>
 struct Tile : RefTile<TR, AQ> {
   uint32_t kc[TR][NRA], km[TR][NRA], ka[TR][NRA], vc[TR][NRA], vm[TR][NRA], va[TR][NRA];
 };
-
-// The lane's 8 anchor values z + s*code (FP32; the anchor's own domain,
-// rotated when the layout rotates) from its code word and (scale, zero) word.
-// Codes enter v_fma_mix_f32 as FP16 subnormals (see code_halves); the scale
-// carries the matching 2^(24 - pos).
-template <bool INT4>
-__device__ __forceinline__ void anchor_values(uint32_t x, uint32_t mw, float (&y)[8]) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
-  const float s = h_lo(mw);
-  const float sc0 = s * 16777216.0f;                       // 2^24
-  const float sc1 = INT4 ? s * 1048576.0f : s * 4194304.0f; // 2^20 | 2^22
-  const float sc2 = s * 1048576.0f;                        // 2^20 (INT2)
-  const float sc3 = s * 262144.0f;                         // 2^18 (INT2)
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float sq = INT4 ? ((q & 1) ? sc1 : sc0) : (q == 0 ? sc0 : q == 1 ? sc1 : q == 2 ? sc2 : sc3);
-    y[q] = __builtin_fmaf(h_lo(w[q]), sq, h_hi(mw));
-    y[q + 4] = __builtin_fmaf(h_hi(w[q]), sq, h_hi(mw));
-  }
-}
 
 // Scores above the running max by more than this (log2 units) trigger a
 // rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
@@ -308,15 +295,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 
   // ---- prologue: queries of every loop in the pass -------------------------
   // BF16 reference: its dots use the BF16 query pairs as stored (qb).
-  // Quantized anchor: its dots use q' (= H_n q when rotated) in FP32 (qf).
-  // Residual dots use q' in FP32, each element pre-multiplied by 2^(24 - pos)
-  // for its code's position in code_halves (qr).  Scores are scaled by
+  // Code dots (residual loops, and with a quantized anchor the anchor too)
+  // use q' = H_n q in FP32 (just q without rotation), each element
+  // pre-multiplied by 2^(24 - pos) for its code's position in code_halves
+  // (qr); sig is the lane's sum of q' for the offsets.  Scores are scaled by
   // sm_scale*log2(e) after the row sum.
   constexpr int NQB = AQ ? 1 : NS;
-  constexpr int NQF = AQ ? NS : 1;
+  constexpr int NQR = AQ ? NS : NRA;
   uint32_t qb[NQB][4];
-  float qf[NQF][8];
-  float qr[NRA][8], sig[NRA];
+  float qr[NQR][8], sig[NQR];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
@@ -326,28 +313,19 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       for (int p = 0; p < 4; ++p) qb[s][p] = wq[p];
     }
     if (AQ || s < NR) {
+      const int i = s < NQR ? s : 0;
       float f[8];
 #pragma unroll
       for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(wq[p]); f[2 * p + 1] = bf16hi(wq[p]); }
       if (a.rotate) wht8<D>(f, lane);
+      float tot = 0.0f;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) f[p] = f[p] * a.rot_c;
-      if constexpr (AQ > 0) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) qf[s < NQF ? s : 0][p] = f[p];
+      for (int p = 0; p < 8; ++p) {
+        const float v = f[p] * a.rot_c;
+        tot += v;
+        qr[i][p] = v * (float)(1 << (24 - code_pos(p)));
       }
-      if (s < NR) {
-        const int i = s < NRA ? s : 0;
-        float tot = 0.0f;
-        const bool int4 = (B4 >> i) & 1;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          tot += f[p];
-          const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
-          qr[i][p] = f[p] * (float)(1 << (24 - pos));
-        }
-        sig[i] = tot;
-      }
+      sig[i] = tot;
     }
   }
 
@@ -356,7 +334,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // exponentials (lane j of a quad computes slot j's weight; the quad shares
   // the four weights through DPP).
   const int own = j & 3;
-  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA];
+  // With a quantized anchor the residual slots fold the anchor's values into
+  // their residual accumulator (both are code sums in the same domain), so
+  // only the anchor's own slot keeps a reference accumulator (with offset
+  // share zref).
+  constexpr int OREF_FROM = AQ ? NR : 0;
+  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA], zref = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     m[s] = -FLT_MAX;
@@ -425,14 +408,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           part[s] = dot2bf(qb[s][3], T.yk[u].w, dy);
         }
       } else {
-        float yk[8];
-        anchor_values<AINT4>(T.ak[u], T.amk[u], yk);
+        // anchor dot per slot: s_a (q' . code) + z_a sum(q'), codes as halves
+        uint32_t hk[4];
+        code_halves<AINT4>(T.ak[u], hk);
+        const uint32_t mw = T.amk[u];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          float dy = qf[s][0] * yk[0];
-#pragma unroll
-          for (int p = 1; p < 8; ++p) dy = __builtin_fmaf(qf[s][p], yk[p], dy);
-          part[s] = dy;
+          const float dc = code_dot_h(hk, qr[s], 0.0f);
+          part[s] = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[s], 0.0f));
         }
       }
 #pragma unroll
@@ -461,8 +444,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         const float f = fexp2(m[s] - mt);
         m[s] = mt;
         if (own == s) l_own *= f;
+        if (s >= OREF_FROM) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+          for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+          if (AQ) zref *= f;
+        }
         if (s < NR) {
           zacc[s] *= f;
 #pragma unroll
@@ -475,13 +461,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
       float y[8];
+      uint32_t hv[4];
       if constexpr (AQ == 0) {
         y[0] = bf16lo(T.yv[u].x); y[1] = bf16hi(T.yv[u].x);
         y[2] = bf16lo(T.yv[u].y); y[3] = bf16hi(T.yv[u].y);
         y[4] = bf16lo(T.yv[u].z); y[5] = bf16hi(T.yv[u].z);
         y[6] = bf16lo(T.yv[u].w); y[7] = bf16hi(T.yv[u].w);
       } else {
-        anchor_values<AINT4>(T.av[u], T.amv[u], y);
+        code_halves<AINT4>(T.av[u], hv);
       }
       // one exponential per lane (slot own), shared across the quad
       float x = sc[u][0] - m[0];
@@ -503,13 +490,24 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
           const float wq = __builtin_fmaf(h_lo(mw), pr, 0.0f);
           zacc[s] = __builtin_fmaf(h_hi(mw), pr, zacc[s]);
+          if constexpr (AQ == 0) {
 #pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
+            for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
+          } else {
+            // alpha_V p (s_a code + z_a), into the residual accumulator
+            const uint32_t am = T.amv[u];
+            zacc[s] = __builtin_fmaf(h_hi(am), wr, zacc[s]);
+            code_axpy_h(hv, __builtin_fmaf(h_lo(am), wr, 0.0f), ores[s]);
+          }
           if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], wq, ores[s]);
           else code_axpy<false>(T.vc[u][s], wq, ores[s]);
-        } else {
+        } else if constexpr (AQ == 0) {
 #pragma unroll
           for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
+        } else {
+          const uint32_t am = T.amv[u];
+          zref = __builtin_fmaf(h_hi(am), pr, zref);
+          code_axpy_h(hv, __builtin_fmaf(h_lo(am), pr, 0.0f), oref[s]);
         }
       }
     }
@@ -540,18 +538,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // undo the 2^(pos-24) factors of the value codes, add the offsets' share
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const bool int4 = (B4 >> i) & 1;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int pos = int4 ? code_pos<true>(p) : code_pos<false>(p);
-      ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - pos)), zacc[i]);
-    }
+    for (int p = 0; p < 8; ++p) ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - code_pos(p))), zacc[i]);
+  }
+  if constexpr (AQ > 0 && REF) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) oref[NR][p] = __builtin_fmaf(oref[NR][p], (float)(1 << (24 - code_pos(p))), zref);
   }
 
   // ---- merge rows, then waves -----------------------------------------------
-  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
 
   __shared__ float sm[W][NS][REC];
   if (r == 0) {
@@ -560,7 +558,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       if (j == 0) sm[wave][s][0] = m[s];
       if (j == s) sm[wave][s][1] = l_own;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = oref[s][p];
+      for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = s >= OREF_FROM ? oref[s][p] : 0.0f;
       if (s < NR) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
