@@ -71,6 +71,17 @@ WORKLOADS = {
                                   n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
                                   sigma=[0.15, 0.12, 0.1], rotate=1, seed=5, ref_bits=4,
                                   ref_group=32, extra={"tail": 64}),
+    # The pages' throughput grid (Fig. 4: g=32 everywhere; Fig. 6: INT2
+    # residuals at g=16): 24 layers, contexts 2k-16k, power-of-two batches up
+    # to a 250 GB KV budget, per-loop decode, against BF16 per-loop decode.
+    "grid-g16": Workload("grid-g16", n_loops=4, batch=0, heads=16, d=128, g=16, n_ctx=0,
+                         bits=[2, 2, 2], c=[0.8, 0.85, 0.9], sigma=[0.15, 0.12, 0.1], rotate=1,
+                         layers=24, seed=6, ref_bits=4, ref_group=32,
+                         extra={"tail": 64, "contexts": [2048, 4096, 8192, 16384]}),
+    "grid-g32": Workload("grid-g32", n_loops=4, batch=0, heads=16, d=128, g=32, n_ctx=0,
+                         bits=[2, 2, 2], c=[0.8, 0.85, 0.9], sigma=[0.15, 0.12, 0.1], rotate=1,
+                         layers=24, seed=7, ref_bits=4, ref_group=32,
+                         extra={"tail": 64, "contexts": [2048, 4096, 8192, 16384]}),
 }
 
 
