@@ -29,9 +29,12 @@ rq_status check_layout(const rq_layout *L) {
   if (L->group != 16 && L->group != 32) return RQ_ERR_UNSUPPORTED;
   if (L->head_dim % L->group != 0) return RQ_ERR_UNSUPPORTED;
   if (L->rotate != 0 && L->rotate != 1) return RQ_ERR_INVALID_ARG;
-  for (int l = 0; l < L->n_loops - 1; ++l)
-    if (L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
+  const int G = L->group_loops ? L->group_loops : L->n_loops;
+  if (G < 2 || G > L->n_loops || L->n_loops % G != 0) return RQ_ERR_UNSUPPORTED;
+  for (int l = 0; l < L->n_loops; ++l)
+    if ((l + 1) % G != 0 && L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
   if (L->ref_bits != 0 && L->ref_bits != 2 && L->ref_bits != 4) return RQ_ERR_UNSUPPORTED;
+  if (G < L->n_loops && L->ref_bits == 0) return RQ_ERR_UNSUPPORTED;   // one BF16 ref plane only
   if (L->ref_bits != 0) {
     const int ga = L->ref_group ? L->ref_group : L->group;
     if (ga != 16 && ga != 32) return RQ_ERR_UNSUPPORTED;
@@ -43,17 +46,28 @@ rq_status check_layout(const rq_layout *L) {
 
 int anchor_group(const rq_layout *L) { return L->ref_group ? L->ref_group : L->group; }
 
-// The reference planes: the BF16 ref plane, or the anchor's codes and meta.
-bool ref_planes_ok(const rq_layout *L, const rq_cache *c) {
+// Loops per anchor group, the anchor (reference) loop of loop l's group, and
+// whether l is an anchor.
+int group_len(const rq_layout *L) { return L->group_loops ? L->group_loops : L->n_loops; }
+int anchor_of(const rq_layout *L, int l) { const int G = group_len(L); return (l / G) * G + G - 1; }
+bool is_anchor(const rq_layout *L, int l) { return (l + 1) % group_len(L) == 0; }
+
+// The reference planes of the group whose anchor is loop a: the BF16 ref
+// plane, or the anchor's codes and meta.
+bool ref_planes_ok(const rq_layout *L, const rq_cache *c, int a) {
   if (L->ref_bits == 0) return aligned16(c->ref);
-  return aligned16(c->codes[L->n_loops - 1]) && aligned16(c->meta[L->n_loops - 1]);
+  return aligned16(c->codes[a]) && aligned16(c->meta[a]);
+}
+
+bool residual_planes_ok(const rq_cache *c, int l) {
+  return aligned16(c->codes[l]) && aligned16(c->meta[l]) && aligned16(c->alpha[l]);
 }
 
 rq_status check_cache(const rq_layout *L, const rq_cache *c) {
-  if (c == nullptr || !ref_planes_ok(L, c)) return RQ_ERR_INVALID_ARG;
-  for (int l = 0; l < L->n_loops - 1; ++l)
-    if (!aligned16(c->codes[l]) || !aligned16(c->meta[l]) || !aligned16(c->alpha[l]))
-      return RQ_ERR_INVALID_ARG;
+  if (c == nullptr) return RQ_ERR_INVALID_ARG;
+  for (int l = 0; l < L->n_loops; ++l) {
+    if (is_anchor(L, l) ? !ref_planes_ok(L, c, l) : !residual_planes_ok(c, l)) return RQ_ERR_INVALID_ARG;
+  }
   return RQ_OK;
 }
 
@@ -153,41 +167,50 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
   if (t0 < 0 || n < 0 || (int64_t)t0 + n > L->capacity) return RQ_ERR_INVALID_ARG;
   if (n == 0) return RQ_OK;
 
-  rq::EncodeArgs a;
-  std::memset(&a, 0, sizeof a);
+  const int G = group_len(L);
+  const int64_t bh = (int64_t)L->batch * L->n_heads;
+  const int vpw = 64 / (L->head_dim / 8);
+  const int chunks = (n + vpw - 1) / vpw;
+  if (bh * chunks * 2 > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
   const rq_cache *sides[2] = {k, v};
   const void *ins[2] = {k_in, v_in};
-  for (int s = 0; s < 2; ++s) {
-    a.side[s].ref = static_cast<const uint16_t *>(sides[s]->ref);
-    a.side[s].xin = static_cast<const uint16_t *>(ins[s]);
-    for (int l = 0; l < L->n_loops - 1; ++l) {
-      a.side[s].codes[l] = static_cast<uint8_t *>(sides[s]->codes[l]);
-      a.side[s].meta[l] = static_cast<uint32_t *>(sides[s]->meta[l]);
-      a.side[s].alpha[l] = static_cast<uint16_t *>(sides[s]->alpha[l]);
-    }
-    if (L->ref_bits) {
-      a.side[s].codes[L->n_loops - 1] = static_cast<uint8_t *>(sides[s]->codes[L->n_loops - 1]);
-      a.side[s].meta[L->n_loops - 1] = static_cast<uint32_t *>(sides[s]->meta[L->n_loops - 1]);
-    }
-  }
-  a.abits = L->ref_bits;
-  a.agroup = anchor_group(L);
-  for (int l = 0; l < L->n_loops - 1; ++l) a.bits[l] = L->bits[l];
-  a.n_res = L->n_loops - 1;
-  a.bh = L->batch * L->n_heads;
-  a.cap = L->capacity;
-  a.t0 = t0;
-  a.n = n;
-  a.group = L->group;
-  a.rotate = L->rotate;
-  a.rot_c = rot_const(L->head_dim);
-  const int vpw = 64 / (L->head_dim / 8);
-  a.chunks = (n + vpw - 1) / vpw;
-  if ((int64_t)a.bh * a.chunks * 2 > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
-  a.tasks_per_side = a.bh * a.chunks;
+  // the inputs of one group: G loops (the anchor's included when quantized)
+  const int in_loops = L->ref_bits ? G : G - 1;
+  const size_t loop_elems = (size_t)bh * n * L->head_dim;
   (void)hipGetLastError();
-  return rq::launch_encode(a, L->head_dim, static_cast<hipStream_t>(hip_stream)) == hipSuccess
-             ? RQ_OK : RQ_ERR_DEVICE;
+  for (int g0 = 0; g0 < L->n_loops; g0 += G) {
+    rq::EncodeArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int s = 0; s < 2; ++s) {
+      a.side[s].ref = static_cast<const uint16_t *>(sides[s]->ref);
+      a.side[s].xin = static_cast<const uint16_t *>(ins[s]) + (size_t)(g0 / G) * in_loops * loop_elems;
+      for (int l = 0; l < G - 1; ++l) {
+        a.side[s].codes[l] = static_cast<uint8_t *>(sides[s]->codes[g0 + l]);
+        a.side[s].meta[l] = static_cast<uint32_t *>(sides[s]->meta[g0 + l]);
+        a.side[s].alpha[l] = static_cast<uint16_t *>(sides[s]->alpha[g0 + l]);
+      }
+      if (L->ref_bits) {
+        a.side[s].codes[G - 1] = static_cast<uint8_t *>(sides[s]->codes[g0 + G - 1]);
+        a.side[s].meta[G - 1] = static_cast<uint32_t *>(sides[s]->meta[g0 + G - 1]);
+      }
+    }
+    for (int l = 0; l < G - 1; ++l) a.bits[l] = L->bits[g0 + l];
+    a.abits = L->ref_bits;
+    a.agroup = anchor_group(L);
+    a.n_res = G - 1;
+    a.bh = (int32_t)bh;
+    a.cap = L->capacity;
+    a.t0 = t0;
+    a.n = n;
+    a.group = L->group;
+    a.rotate = L->rotate;
+    a.rot_c = rot_const(L->head_dim);
+    a.chunks = chunks;
+    a.tasks_per_side = (int32_t)(bh * chunks);
+    if (rq::launch_encode(a, L->head_dim, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+      return RQ_ERR_DEVICE;
+  }
+  return RQ_OK;
 }
 
 int32_t rq_decode_splits(const rq_layout *L, int32_t n_ctx) {
@@ -229,15 +252,14 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   if (n_tail > 0 && (int64_t)L->batch * L->n_heads * tail->capacity > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
   if (n_splits < 0 || (n_ctx > 0 && n_splits > n_ctx)) return RQ_ERR_INVALID_ARG;
-  const int ref_loop = L->n_loops - 1;
-  if (n_ctx > 0 && !ref_planes_ok(L, k)) return RQ_ERR_INVALID_ARG;
-  if (n_ctx > 0 && !ref_planes_ok(L, v)) return RQ_ERR_INVALID_ARG;
   for (int l = 0; l < L->n_loops; ++l) {
     if (!((loop_mask >> l) & 1u)) continue;
-    if (n_ctx > 0 && l < ref_loop &&
-        (!aligned16(k->codes[l]) || !aligned16(k->meta[l]) || !aligned16(k->alpha[l]) ||
-         !aligned16(v->codes[l]) || !aligned16(v->meta[l]) || !aligned16(v->alpha[l])))
-      return RQ_ERR_INVALID_ARG;
+    if (n_ctx > 0) {
+      const int an = anchor_of(L, l);
+      if (!ref_planes_ok(L, k, an) || !ref_planes_ok(L, v, an)) return RQ_ERR_INVALID_ARG;
+      if (!is_anchor(L, l) && (!residual_planes_ok(k, l) || !residual_planes_ok(v, l)))
+        return RQ_ERR_INVALID_ARG;
+    }
     if (n_tail > 0 && (!aligned16(tail->k[l]) || !aligned16(tail->v[l]))) return RQ_ERR_INVALID_ARG;
   }
   int S = 0, tps = 0;
@@ -259,10 +281,6 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
     a.kref = static_cast<const uint16_t *>(k->ref);
     a.vref = static_cast<const uint16_t *>(v->ref);
   } else {
-    a.kac = static_cast<const uint8_t *>(k->codes[ref_loop]);
-    a.vac = static_cast<const uint8_t *>(v->codes[ref_loop]);
-    a.kam = static_cast<const uint32_t *>(k->meta[ref_loop]);
-    a.vam = static_cast<const uint32_t *>(v->meta[ref_loop]);
     a.ref_rotated = L->rotate;
   }
   a.agroup = anchor_group(L);
@@ -282,49 +300,60 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
   a.rot_c = L->rotate ? rot_const(L->head_dim) : 1.0f;
 
-  int res[RQ_MAX_LOOPS], nres = 0;
-  for (int l = 0; l < ref_loop; ++l)
-    if ((loop_mask >> l) & 1u) res[nres++] = l;
-  bool want_ref = (loop_mask >> ref_loop) & 1u;
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const int G = group_len(L);
   (void)hipGetLastError();
-  // Passes of at most kMaxRes residual loops; the first also computes the
-  // reference loop.  Each pass reads the reference once.
-  int done = 0;
-  do {
-    const int cnt = (nres - done) < rq::kMaxRes ? (nres - done) : rq::kMaxRes;
-    for (int i = 0; i < rq::kMaxSlots; ++i) a.tk[i] = a.tv[i] = nullptr;
-    for (int i = 0; i < cnt; ++i) {
-      const int l = res[done + i];
-      a.kc[i] = static_cast<const uint8_t *>(k->codes[l]);
-      a.vc[i] = static_cast<const uint8_t *>(v->codes[l]);
-      a.km[i] = static_cast<const uint32_t *>(k->meta[l]);
-      a.vm[i] = static_cast<const uint32_t *>(v->meta[l]);
-      a.ka[i] = static_cast<const uint16_t *>(k->alpha[l]);
-      a.va[i] = static_cast<const uint16_t *>(v->alpha[l]);
-      a.bits[i] = L->bits[l];
-      a.qloop[i] = l;
-      if (n_tail > 0) {
-        a.tk[i] = static_cast<const uint16_t *>(tail->k[l]);
-        a.tv[i] = static_cast<const uint16_t *>(tail->v[l]);
-      }
+  for (int g0 = 0; g0 < L->n_loops; g0 += G) {
+    const int ref_loop = g0 + G - 1;          // this group's reference / anchor
+    int res[RQ_MAX_LOOPS], nres = 0;
+    for (int l = g0; l < ref_loop; ++l)
+      if ((loop_mask >> l) & 1u) res[nres++] = l;
+    bool want_ref = (loop_mask >> ref_loop) & 1u;
+    if (nres == 0 && !want_ref) continue;
+    if (L->ref_bits) {
+      a.kac = static_cast<const uint8_t *>(k->codes[ref_loop]);
+      a.vac = static_cast<const uint8_t *>(v->codes[ref_loop]);
+      a.kam = static_cast<const uint32_t *>(k->meta[ref_loop]);
+      a.vam = static_cast<const uint32_t *>(v->meta[ref_loop]);
     }
-    if (want_ref) {
-      a.qloop[cnt] = ref_loop;
-      if (n_tail > 0) {
-        a.tk[cnt] = static_cast<const uint16_t *>(tail->k[ref_loop]);
-        a.tv[cnt] = static_cast<const uint16_t *>(tail->v[ref_loop]);
+    // Passes of at most kMaxRes residual loops; the first also computes the
+    // reference loop.  Each pass reads the reference once.
+    int done = 0;
+    do {
+      const int cnt = (nres - done) < rq::kMaxRes ? (nres - done) : rq::kMaxRes;
+      for (int i = 0; i < rq::kMaxSlots; ++i) a.tk[i] = a.tv[i] = nullptr;
+      for (int i = 0; i < cnt; ++i) {
+        const int l = res[done + i];
+        a.kc[i] = static_cast<const uint8_t *>(k->codes[l]);
+        a.vc[i] = static_cast<const uint8_t *>(v->codes[l]);
+        a.km[i] = static_cast<const uint32_t *>(k->meta[l]);
+        a.vm[i] = static_cast<const uint32_t *>(v->meta[l]);
+        a.ka[i] = static_cast<const uint16_t *>(k->alpha[l]);
+        a.va[i] = static_cast<const uint16_t *>(v->alpha[l]);
+        a.bits[i] = L->bits[l];
+        a.qloop[i] = l;
+        if (n_tail > 0) {
+          a.tk[i] = static_cast<const uint16_t *>(tail->k[l]);
+          a.tv[i] = static_cast<const uint16_t *>(tail->v[l]);
+        }
       }
-    }
-    hipError_t e;
-    if (n_ctx > 0)
-      e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, stream);
-    else   // the tail alone: the merge kernel attends over it, no split records
-      e = rq::launch_merge(a, L->head_dim, cnt, cnt + (want_ref ? 1 : 0), stream);
-    if (e != hipSuccess) return RQ_ERR_DEVICE;
-    want_ref = false;
-    done += cnt;
-  } while (done < nres);
+      if (want_ref) {
+        a.qloop[cnt] = ref_loop;
+        if (n_tail > 0) {
+          a.tk[cnt] = static_cast<const uint16_t *>(tail->k[ref_loop]);
+          a.tv[cnt] = static_cast<const uint16_t *>(tail->v[ref_loop]);
+        }
+      }
+      hipError_t e;
+      if (n_ctx > 0)
+        e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, stream);
+      else   // the tail alone: the merge kernel attends over it, no split records
+        e = rq::launch_merge(a, L->head_dim, cnt, cnt + (want_ref ? 1 : 0), stream);
+      if (e != hipSuccess) return RQ_ERR_DEVICE;
+      want_ref = false;
+      done += cnt;
+    } while (done < nres);
+  }
   return RQ_OK;
 }
 
@@ -404,13 +433,12 @@ rq_status rq_reconstruct(const rq_layout *L, const rq_cache *c, int32_t loop, in
                          float *out, void *hip_stream) {
   rq_status st = check_layout(L);
   if (st != RQ_OK) return st;
-  const int ref_loop = L->n_loops - 1;
-  const bool anchor_loop = L->ref_bits != 0 && loop == ref_loop;
-  if (loop < 0 || loop > ref_loop || (loop == ref_loop && !anchor_loop)) return RQ_ERR_INVALID_ARG;
-  if (c == nullptr || !ref_planes_ok(L, c) || !aligned16(out)) return RQ_ERR_INVALID_ARG;
-  if (!anchor_loop &&
-      (!aligned16(c->codes[loop]) || !aligned16(c->meta[loop]) || !aligned16(c->alpha[loop])))
-    return RQ_ERR_INVALID_ARG;
+  if (loop < 0 || loop >= L->n_loops) return RQ_ERR_INVALID_ARG;
+  const int ref_loop = anchor_of(L, loop);
+  const bool anchor_loop = loop == ref_loop;
+  if (anchor_loop && L->ref_bits == 0) return RQ_ERR_INVALID_ARG;   // the BF16 reference itself
+  if (c == nullptr || !ref_planes_ok(L, c, ref_loop) || !aligned16(out)) return RQ_ERR_INVALID_ARG;
+  if (!anchor_loop && !residual_planes_ok(c, loop)) return RQ_ERR_INVALID_ARG;
   if (t0 < 0 || n < 1 || (int64_t)t0 + n > L->capacity) return RQ_ERR_INVALID_ARG;
   rq::ReconArgs a;
   std::memset(&a, 0, sizeof a);

@@ -82,11 +82,18 @@ typedef struct {
                                     is a quantized anchor in codes[L-1] / meta[L-1]  */
     int32_t ref_group;           /* the anchor's group size, 16 or 32 (0 = group);
                                     ignored when ref_bits == 0                        */
+    int32_t group_loops;         /* loops per anchor group (0 = n_loops: one group).
+                                    Loops [k*G, (k+1)*G) form group k; its last loop
+                                    is the group's quantized anchor and the others
+                                    are residuals against it (Table 8: one INT4
+                                    anchor per group of loops).  G >= 2 divides
+                                    n_loops; G < n_loops needs ref_bits > 0         */
 } rq_layout;
 
 /* One side (K or V) of one layer's cache: caller-owned device planes.
  * Entries l >= L-1 of the arrays are ignored, except codes[L-1] and meta[L-1]
- * with a quantized anchor. */
+ * with a quantized anchor.  With several anchor groups, every group's anchor
+ * loop a has codes[a] / meta[a] in the anchor format and no alpha[a]. */
 typedef struct {
     void *ref;                   /* bf16 [B][H][cap][d], written by the caller;
                                     unused (may be NULL) with a quantized anchor   */

@@ -235,24 +235,40 @@ def ref_group(layout: dict) -> int:
     return int(layout.get("ref_group") or layout["g"])
 
 
+def group_len(layout: dict) -> int:
+    """Loops per anchor group (Table 8 caption: each group of loops ends in one
+    INT4 anchor); the whole schedule is one group unless group_loops is set."""
+    return int(layout.get("group_loops") or layout["n_loops"])
+
+
 class Planes:
     """One cache side (K or V), as numpy arrays in the contract layout: the
     BF16 reference and each residual loop's codes / meta / alpha planes; with
     a quantized anchor (ref_bits > 0) no reference plane, and codes / meta
     lists one longer, the anchor's planes last."""
 
-    def __init__(self, n_loops, batch, heads, d, g, cap, bits, ref_bits=0, ref_group=None):
+    def __init__(self, n_loops, batch, heads, d, g, cap, bits, ref_bits=0, ref_group=None,
+                 group_loops=0):
         ga = ref_group or g
-        self.ref = None if ref_bits else np.zeros((batch, heads, cap, d), dtype=np.uint16)
-        self.codes = [np.zeros((batch, heads, cap, d * bits[l] // 8), dtype=np.uint8)
-                      for l in range(n_loops - 1)]
-        self.meta = [np.zeros((batch, heads, cap, d // g, 2), dtype=np.uint16)
-                     for l in range(n_loops - 1)]
-        self.alpha = [np.zeros((batch, heads, cap), dtype=np.uint16)
-                      for l in range(n_loops - 1)]
-        if ref_bits:
-            self.codes.append(np.zeros((batch, heads, cap, d * ref_bits // 8), dtype=np.uint8))
-            self.meta.append(np.zeros((batch, heads, cap, d // ga, 2), dtype=np.uint16))
+        G = group_loops or n_loops
+        shape = (batch, heads, cap)
+        if not ref_bits:
+            self.ref = np.zeros(shape + (d,), dtype=np.uint16)
+            self.codes = [np.zeros(shape + (d * bits[l] // 8,), dtype=np.uint8) for l in range(n_loops - 1)]
+            self.meta = [np.zeros(shape + (d // g, 2), dtype=np.uint16) for l in range(n_loops - 1)]
+            self.alpha = [np.zeros(shape, dtype=np.uint16) for l in range(n_loops - 1)]
+            return
+        self.ref = None
+        self.codes, self.meta, self.alpha = [], [], []
+        for l in range(n_loops):
+            if (l + 1) % G == 0:                 # the group's anchor
+                self.codes.append(np.zeros(shape + (d * ref_bits // 8,), dtype=np.uint8))
+                self.meta.append(np.zeros(shape + (d // ga, 2), dtype=np.uint16))
+                self.alpha.append(None)
+            else:
+                self.codes.append(np.zeros(shape + (d * bits[l] // 8,), dtype=np.uint8))
+                self.meta.append(np.zeros(shape + (d // g, 2), dtype=np.uint16))
+                self.alpha.append(np.zeros(shape, dtype=np.uint16))
 
 
 def _ptrs(arrs):
@@ -269,14 +285,19 @@ def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) ->
     d, g, cap = layout["d"], layout["g"], layout["cap"]
     bits = np.ascontiguousarray(layout["bits"][:L - 1], dtype=np.int32)
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
-    cp, mp, ap = _ptrs(planes.codes), _ptrs(planes.meta), _ptrs(planes.alpha)
     if anchored(layout):
         assert x.shape == (L, B, H, n, d)
-        lib().rqo_encode_anchored(L, B, H, d, g, ref_group(layout), int(layout["ref_bits"]), cap,
-                                  int(layout["rotate"]), bits, x, t0, n,
-                                  C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p),
-                                  C.cast(ap, C.c_void_p))
+        G = group_len(layout)
+        for g0 in range(0, L, G):             # every group on its own
+            cp, mp = _ptrs(planes.codes[g0:g0 + G]), _ptrs(planes.meta[g0:g0 + G])
+            ap = _ptrs(planes.alpha[g0:g0 + G - 1])
+            gbits = np.ascontiguousarray(layout["bits"][g0:g0 + G - 1], dtype=np.int32)
+            lib().rqo_encode_anchored(G, B, H, d, g, ref_group(layout), int(layout["ref_bits"]), cap,
+                                      int(layout["rotate"]), gbits, np.ascontiguousarray(x[g0:g0 + G]),
+                                      t0, n, C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p),
+                                      C.cast(ap, C.c_void_p))
         return
+    cp, mp, ap = _ptrs(planes.codes), _ptrs(planes.meta), _ptrs(planes.alpha)
     assert x.shape == (L - 1, B, H, n, d)
     lib().rqo_encode(L, B, H, d, g, cap, int(layout["rotate"]), bits,
                      np.ascontiguousarray(planes.ref), x, t0, n,
@@ -294,12 +315,14 @@ def reconstruct(layout: dict, planes: Planes, loop: int, t0: int, n: int) -> np.
     L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
     out = np.zeros((B, H, n, d), dtype=np.float64)
     if anchored(layout):
-        anchor = loop == L - 1
-        li = 0 if anchor else loop
+        G = group_len(layout)
+        an = (loop // G) * G + G - 1         # the loop's anchor
+        anchor = loop == an
+        li = an - 1 if anchor else loop      # stand-in residual planes (unread for the anchor)
         lib().rqo_reconstruct_anchored(B, H, d, layout["g"], ref_group(layout),
                                        int(layout["ref_bits"]), layout["cap"],
                                        int(layout["rotate"]), int(layout["bits"][li]),
-                                       planes.codes[L - 1], planes.meta[L - 1],
+                                       planes.codes[an], planes.meta[an],
                                        planes.codes[li].ctypes.data, planes.meta[li].ctypes.data,
                                        planes.alpha[li].ctypes.data, -1 if anchor else loop,
                                        t0, n, out)
@@ -326,10 +349,16 @@ def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: i
     the n_ctx cached tokens and then the tail rows (bf16 bits [T, d] of this
     (loop, b, h)), if given."""
     L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
-    # The final loop attends over the reference alone; its residual plane
-    # arguments are ignored by the C side, so loop 0's planes stand in.
-    li = 0 if loop == L - 1 else loop
+    # One anchor group at a time: the C side sees the group's loops as a
+    # schedule of G loops whose last is the reference.
+    G = group_len(layout) if anchored(layout) else L
+    g0 = (loop // G) * G
+    an = g0 + G - 1
+    # The reference loop attends over the reference alone; its residual plane
+    # arguments are ignored by the C side, so the group's first planes stand in.
+    li = g0 if loop == an else loop
     bits = int(layout["bits"][li])
+    q_grp = np.ascontiguousarray(np.asarray(q_bits, dtype=np.uint16)[g0:g0 + G])
     out = np.zeros(d, dtype=np.float64)
     ptr = lambda a: None if a is None else np.ascontiguousarray(a).ctypes.data
     keep = []
@@ -344,18 +373,17 @@ def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: i
     n_tail = 0 if tail_k is None else int(np.asarray(tail_k).shape[0])
     if anchored(layout):
         abits, ga = int(layout["ref_bits"]), ref_group(layout)
-        anc = (kp.codes[L - 1], kp.meta[L - 1], vp.codes[L - 1], vp.meta[L - 1])
+        anc = (kp.codes[an], kp.meta[an], vp.codes[an], vp.meta[an])
         kref = vref = None
     else:
         abits, ga = 0, layout["g"]
         anc = (None, None, None, None)
         kref, vref = kp.ref, vp.ref
-    lib().rqo_decode_row_ex(L, B, H, d, layout["g"], layout["cap"], int(layout["rotate"]), bits,
+    lib().rqo_decode_row_ex(G, B, H, d, layout["g"], layout["cap"], int(layout["rotate"]), bits,
                             ptr(kref), ptr(kp.codes[li]), ptr(kp.meta[li]), ptr(kp.alpha[li]),
                             ptr(vref), ptr(vp.codes[li]), ptr(vp.meta[li]), ptr(vp.alpha[li]),
                             ga, abits, *[ptr(x) for x in anc], tk, tv, n_tail,
-                            np.ascontiguousarray(q_bits, dtype=np.uint16), loop, b, h, n_ctx,
-                            float(scale), out)
+                            q_grp, loop - g0, b, h, n_ctx, float(scale), out)
     return out
 
 

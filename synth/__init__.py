@@ -43,6 +43,7 @@ class Workload:
     seed: int = 0
     ref_bits: int = 0               # 0: BF16 reference; 2/4: quantized anchor
     ref_group: int = 0              # the anchor's group size (0: g)
+    group_loops: int = 0            # loops per anchor group (0: one group)
     extra: dict = field(default_factory=dict)
 
 

@@ -20,14 +20,15 @@ def tol_rel_row(got: np.ndarray, want: np.ndarray) -> np.ndarray:
 
 def oracle_layout(w: synth.Workload, batch: int, cap: int) -> dict:
     return dict(n_loops=w.n_loops, batch=batch, heads=w.heads, d=w.d, g=w.g, cap=cap,
-                rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits, ref_group=w.ref_group)
+                rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits, ref_group=w.ref_group,
+                group_loops=w.group_loops)
 
 
 def gpu_layout(w: synth.Workload, batch: int, cap: int):
     import decode_attention_rq_amd as rq
     return rq.Layout(n_loops=w.n_loops, batch=batch, n_heads=w.heads, head_dim=w.d, group=w.g,
                      capacity=cap, rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits,
-                     ref_group=w.ref_group)
+                     ref_group=w.ref_group, group_loops=w.group_loops)
 
 
 def encoder_input(w: synth.Workload, loops: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
@@ -85,8 +86,10 @@ class Case:
                 idx[ax + 1] = hi
                 return t[tuple(idx)].unsqueeze(ax + 1)
         lay = oracle_layout(w, B, n)
-        kp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None)
-        vp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None)
+        kp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None,
+                           w.group_loops)
+        vp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None,
+                           w.group_loops)
         if bh_list is None:
             kr, vr, kl, vl, q = (self.data["k_ref"], self.data["v_ref"], self.data["k_loops"],
                                  self.data["v_loops"], self.data["q"])

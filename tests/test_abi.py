@@ -269,3 +269,26 @@ def test_tail_validation(rq):
     assert _decode_tail(rq, lay, _tail(rq), n_ctx=0, splits=0, ws_bytes=1) == WORKSPACE
     # plain rq_decode_attn still needs a cached token
     assert _decode(rq, lay, n_ctx=0) == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group_loops=3), UNSUPPORTED), (dict(group_loops=1), UNSUPPORTED), (dict(group_loops=5), UNSUPPORTED),
+    (dict(group_loops=2), UNSUPPORTED),                       # several groups need quantized anchors
+])
+def test_anchor_group_validation(rq, kw, code):
+    lay = _layout(rq, **kw)
+    assert _encode(rq, lay) == code
+    assert _decode(rq, lay) == code
+
+
+def test_anchor_groups_check_every_anchor(rq):
+    lay = _layout(rq, ref_bits=4, ref_group=32, group_loops=2)
+    k = _anchor_cache(rq)
+    k.codes[1], k.meta[1] = FAKE + 0x9000, FAKE + 0x900000      # anchor of group 0
+    v = _anchor_cache(rq)
+    v.codes[1], v.meta[1] = FAKE + 0x9000, FAKE + 0x900000
+    assert _decode(rq, lay, k=k, v=v, ws_bytes=1) == WORKSPACE
+    k.meta[1] = 0
+    assert _decode(rq, lay, k=k, v=v, mask=0b0001) == INVALID     # loop 0 needs its group's anchor
+    assert _decode(rq, lay, k=k, v=v, mask=0b1100, ws_bytes=1) == WORKSPACE   # group 1 does not
+    assert _encode(rq, lay, k=k, v=v) == INVALID

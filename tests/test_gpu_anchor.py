@@ -226,3 +226,50 @@ def test_anchor_perloop_full_size(oracle):
                                      bf16_bits(tail["k"][l, b, h]), bf16_bits(tail["v"][l, b, h]))
             rel = float(tol_rel_row(got[l, b, h], want))
             assert rel <= ATT_TOL, (l, b, h, rel)
+
+
+# --------------------------------------------------------------------------
+# several anchor groups (Table 8: one INT4 anchor per group of loops)
+# --------------------------------------------------------------------------
+
+def _wg(L, G, bits, g=16, B=2, H=2, seed=61):
+    return synth.Workload("grp", n_loops=L, batch=B, heads=H, d=128, g=g, n_ctx=0, bits=list(bits),
+                          c=[0.85] * (L - 1), sigma=[0.12] * (L - 1), rotate=1, seed=seed, ref_bits=4,
+                          ref_group=32, group_loops=G)
+
+
+GROUP_CASES = {
+    "2x[2,4,2,4]": _wg(8, 4, [2, 4, 2, 0, 2, 2, 4]),
+    "2x[2^7,4]": _wg(16, 8, [2, 2, 2, 2, 2, 2, 2, 0, 2, 2, 2, 2, 2, 2, 2], g=32),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_CASES))
+def test_anchor_groups_encode_reconstruct_decode(oracle, name):
+    import decode_attention_rq_amd as rq
+    w = GROUP_CASES[name]
+    n = 150
+    case = Case(w, n, cap=160, t_chunks=[(0, 99), (99, 51)])
+    lay, kp, vp, qb = case.oracle_planes(oracle)
+    for side, planes in (("k", kp), ("v", vp)):
+        gc = getattr(case, side)
+        for l in range(w.n_loops):
+            assert np.array_equal(plane_bits(gc.codes[l])[:, :, :n], planes.codes[l][:, :, :n]), (side, l)
+            assert np.array_equal(plane_bits(gc.meta[l])[:, :, :n], planes.meta[l][:, :, :n]), (side, l)
+            if planes.alpha[l] is not None:
+                assert np.array_equal(plane_bits(gc.alpha[l])[:, :, :n], planes.alpha[l][:, :, :n]), (side, l)
+    for l in (0, w.group_loops - 1, w.group_loops, w.n_loops - 1):
+        out = torch.empty(case.B, w.heads, 40, w.d, dtype=torch.float32, device="cuda")
+        rq.rq_reconstruct(case.lay, case.k, l, 7, 40, out)
+        torch.cuda.synchronize()
+        want = oracle.reconstruct(lay, kp, l, 7, 40)
+        an = (l // w.group_loops + 1) * w.group_loops - 1
+        sa = plane_bits(case.k.meta[an])[:, :, 7:47, :, 0].view(np.float16).astype(np.float64).max(-1)
+        sr = plane_bits(case.k.meta[l])[:, :, 7:47, :, 0].view(np.float16).astype(np.float64).max(-1)
+        err = np.abs(out.cpu().double().numpy() - want).max(-1)
+        assert np.all(err <= REC_TOL * np.maximum(sa, sr)), l
+    tk, tv = _tail(w, case.B, 4)
+    full = (1 << w.n_loops) - 1
+    for mask, splits in ((full, 0), (full, 3), (0b1 | (1 << (w.n_loops - 1)), 1)):
+        got = _run(case, mask, n, tk, tv, 4, splits=splits)
+        _check(oracle, case, got, mask, n, tk, tv)

@@ -230,3 +230,35 @@ def test_tail_is_attended_after_the_cache(oracle, anchor):
     want1 = _sdpa(_f32(q[0, 0, 0]).astype(np.float64), np.concatenate([kh, _f32(tk)]),
                   np.concatenate([vh, _f32(tv)]), 0.2)
     assert np.allclose(got1, want1, rtol=1e-12, atol=1e-12)
+
+
+def test_anchor_groups_are_independent_schedules(oracle):
+    """Table 8 caption: with several anchor groups each group of loops ends in
+    its own INT4 anchor.  An 8-loop 2 x [2,2,2,4] layout encodes, reconstructs
+    and decodes exactly as its two 4-loop halves do on their own."""
+    rng = np.random.default_rng(88)
+    L, G, B, H, d, g, n = 8, 4, 1, 2, 64, 16, 12
+    bits = [2, 4, 2, 0, 2, 2, 4, 0]
+    lay = dict(n_loops=L, batch=B, heads=H, d=d, g=g, cap=n, rotate=1, bits=bits, ref_bits=4,
+               ref_group=32, group_loops=G)
+    x = _bf16(rng.standard_normal((L, B, H, n, d)))
+    whole = oracle.Planes(L, B, H, d, g, n, bits, 4, 32, group_loops=G)
+    oracle.encode(lay, whole, x, 0, n)
+    q = _bf16(rng.standard_normal((L, B, H, d)))
+    tk = _bf16(rng.standard_normal((L, B, H, 3, d)))
+    tv = _bf16(rng.standard_normal((L, B, H, 3, d)))
+    for g0 in (0, G):
+        sub = dict(lay, n_loops=G, bits=bits[g0:g0 + G], group_loops=0)
+        part = oracle.Planes(G, B, H, d, g, n, bits[g0:g0 + G], 4, 32)
+        oracle.encode(sub, part, x[g0:g0 + G], 0, n)
+        for l in range(G):
+            assert np.array_equal(whole.codes[g0 + l], part.codes[l])
+            assert np.array_equal(whole.meta[g0 + l], part.meta[l])
+            if l < G - 1:
+                assert np.array_equal(whole.alpha[g0 + l], part.alpha[l])
+            assert np.array_equal(oracle.reconstruct(lay, whole, g0 + l, 0, n),
+                                  oracle.reconstruct(sub, part, l, 0, n))
+            got = oracle.decode_row(lay, whole, whole, q, g0 + l, 0, 1, n, 0.3, tk[g0 + l, 0, 1], tv[g0 + l, 0, 1])
+            want = oracle.decode_row(sub, part, part, q[g0:g0 + G], l, 0, 1, n, 0.3, tk[g0 + l, 0, 1],
+                                     tv[g0 + l, 0, 1])
+            assert np.array_equal(got, want)
