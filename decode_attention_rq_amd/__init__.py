@@ -28,7 +28,8 @@ class rq_layout(C.Structure):
     _fields_ = [("n_loops", C.c_int32), ("batch", C.c_int32), ("n_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("group", C.c_int32), ("capacity", C.c_int32),
                 ("rotate", C.c_int32), ("bits", C.c_int32 * RQ_MAX_LOOPS),
-                ("ref_bits", C.c_int32), ("ref_group", C.c_int32), ("group_loops", C.c_int32)]
+                ("ref_bits", C.c_int32), ("ref_group", C.c_int32), ("group_loops", C.c_int32),
+                ("ref_first", C.c_int32), ("alpha_mode", C.c_int32)]
 
 
 class rq_cache(C.Structure):
@@ -100,14 +101,17 @@ class Layout:
     ref_bits: int = 0        # 0: BF16 reference; 2 or 4: quantized anchor
     ref_group: int = 0       # the anchor's group size (0: group)
     group_loops: int = 0     # loops per anchor group (0: all loops, one group)
+    ref_first: int = 0       # 1: each group's first loop is its reference
+    alpha_mode: int = 0      # 0 least squares, 1 alpha = 1, 2 norm ratio
 
     @property
     def anchor_group(self) -> int:
         return self.ref_group or self.group
 
     def is_anchor(self, l: int) -> bool:
-        """Loop l is its group's reference (the last loop of every group)."""
-        return (l + 1) % (self.group_loops or self.n_loops) == 0
+        """Loop l is its group's reference (its first or last loop)."""
+        G = self.group_loops or self.n_loops
+        return l % G == (0 if self.ref_first else G - 1)
 
     def c(self) -> rq_layout:
         s = rq_layout(self.n_loops, self.batch, self.n_heads, self.head_dim, self.group,
@@ -117,6 +121,8 @@ class Layout:
         s.ref_bits = int(self.ref_bits)
         s.ref_group = int(self.ref_group)
         s.group_loops = int(self.group_loops)
+        s.ref_first = int(self.ref_first)
+        s.alpha_mode = int(self.alpha_mode)
         return s
 
 
@@ -124,8 +130,9 @@ class Cache:
     """One side (K or V) of a layer's cache: torch tensors in the plane layout
     of include/rq.h (the library reads and writes them in place).  codes /
     meta / alpha are indexed by loop.  With a BF16 reference, `ref` holds it and
-    the lists stop before loop L-1.  With quantized anchors there is no `ref`
-    (None); every anchor loop has anchor-format codes / meta and alpha None."""
+    the reference loop's entries are None.  With quantized anchors there is no
+    `ref` (None); every anchor loop has anchor-format codes / meta and alpha
+    None."""
 
     def __init__(self, layout: Layout, device="cuda", ref: Optional[torch.Tensor] = None,
                  zero: bool = True):
@@ -152,17 +159,22 @@ class Cache:
                     self.alpha.append(new(B, H, cap, dtype=torch.float16, device=device))
         else:
             self.ref = ref if ref is not None else new(B, H, cap, d, dtype=torch.bfloat16, device=device)
-            self.codes = [new(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device)
-                          for l in range(L - 1)]
-            self.meta = [new(B, H, cap, d // g, 2, dtype=torch.float16, device=device) for _ in range(L - 1)]
-            self.alpha = [new(B, H, cap, dtype=torch.float16, device=device) for _ in range(L - 1)]
+            for l in range(L):
+                if layout.is_anchor(l):
+                    self.codes.append(None)
+                    self.meta.append(None)
+                    self.alpha.append(None)
+                else:
+                    self.codes.append(new(B, H, cap, d * layout.bits[l] // 8, dtype=torch.uint8, device=device))
+                    self.meta.append(new(B, H, cap, d // g, 2, dtype=torch.float16, device=device))
+                    self.alpha.append(new(B, H, cap, dtype=torch.float16, device=device))
 
     def c(self) -> rq_cache:
         s = rq_cache()
         s.ref = _ptr(self.ref)
         for l in range(len(self.codes)):
-            s.codes[l] = self.codes[l].data_ptr()
-            s.meta[l] = self.meta[l].data_ptr()
+            s.codes[l] = _ptr(self.codes[l])
+            s.meta[l] = _ptr(self.meta[l])
         for l in range(len(self.alpha)):
             s.alpha[l] = _ptr(self.alpha[l])
         return s
@@ -174,8 +186,8 @@ class Cache:
         v = Cache.__new__(Cache)
         v.layout = layout
         v.ref = None if self.ref is None else self.ref[b0:b1]
-        v.codes = [t[b0:b1] for t in self.codes]
-        v.meta = [t[b0:b1] for t in self.meta]
+        v.codes = [None if t is None else t[b0:b1] for t in self.codes]
+        v.meta = [None if t is None else t[b0:b1] for t in self.meta]
         v.alpha = [None if t is None else t[b0:b1] for t in self.alpha]
         return v
 
@@ -196,8 +208,9 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 def rq_encode(layout: Layout, k: Cache, v: Cache, k_in: torch.Tensor, v_in: torch.Tensor,
               t0: int, n: int, stream=None) -> None:
-    """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous; with quantized anchors
-    [L, B, H, n, d] (every loop, anchors included, in loop order)."""
+    """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous, the loops other than
+    the BF16 reference in loop order; with quantized anchors [L, B, H, n, d]
+    (every loop, anchors included, in loop order)."""
     lay, kc, vc = layout.c(), k.c(), v.c()
     _check(_lib.rq_encode(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(k_in), _ptr(v_in),
                           int(t0), int(n), _stream(stream)))

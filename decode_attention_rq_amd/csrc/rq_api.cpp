@@ -31,8 +31,11 @@ rq_status check_layout(const rq_layout *L) {
   if (L->rotate != 0 && L->rotate != 1) return RQ_ERR_INVALID_ARG;
   const int G = L->group_loops ? L->group_loops : L->n_loops;
   if (G < 2 || G > L->n_loops || L->n_loops % G != 0) return RQ_ERR_UNSUPPORTED;
+  if (L->ref_first != 0 && L->ref_first != 1) return RQ_ERR_INVALID_ARG;
+  if (L->alpha_mode < 0 || L->alpha_mode > 2) return RQ_ERR_UNSUPPORTED;
+  const int aof = L->ref_first ? 0 : G - 1;         // the anchor's place in its group
   for (int l = 0; l < L->n_loops; ++l)
-    if ((l + 1) % G != 0 && L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
+    if (l % G != aof && L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
   if (L->ref_bits != 0 && L->ref_bits != 2 && L->ref_bits != 4) return RQ_ERR_UNSUPPORTED;
   if (G < L->n_loops && L->ref_bits == 0) return RQ_ERR_UNSUPPORTED;   // one BF16 ref plane only
   if (L->ref_bits != 0) {
@@ -49,8 +52,11 @@ int anchor_group(const rq_layout *L) { return L->ref_group ? L->ref_group : L->g
 // Loops per anchor group, the anchor (reference) loop of loop l's group, and
 // whether l is an anchor.
 int group_len(const rq_layout *L) { return L->group_loops ? L->group_loops : L->n_loops; }
-int anchor_of(const rq_layout *L, int l) { const int G = group_len(L); return (l / G) * G + G - 1; }
-bool is_anchor(const rq_layout *L, int l) { return (l + 1) % group_len(L) == 0; }
+int anchor_of(const rq_layout *L, int l) {
+  const int G = group_len(L);
+  return (l / G) * G + (L->ref_first ? 0 : G - 1);
+}
+bool is_anchor(const rq_layout *L, int l) { return anchor_of(L, l) == l; }
 
 // The reference planes of the group whose anchor is loop a: the BF16 ref
 // plane, or the anchor's codes and meta.
@@ -174,29 +180,39 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
   if (bh * chunks * 2 > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
   const rq_cache *sides[2] = {k, v};
   const void *ins[2] = {k_in, v_in};
-  // the inputs of one group: G loops (the anchor's included when quantized)
-  const int in_loops = L->ref_bits ? G : G - 1;
+  // Inputs: with a BF16 reference the non-reference loops in loop order; with
+  // quantized anchors every loop in loop order.
   const size_t loop_elems = (size_t)bh * n * L->head_dim;
   (void)hipGetLastError();
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
+    const int an = anchor_of(L, g0);
+    int res[RQ_MAX_LOOPS], nres = 0;                 // this group's residual loops
+    for (int l = g0; l < g0 + G; ++l)
+      if (l != an) res[nres++] = l;
+    // input index of loop l
+    auto in_index = [&](int l) { return L->ref_bits ? l : (l < an ? l : l - 1); };
     rq::EncodeArgs a;
     std::memset(&a, 0, sizeof a);
     for (int s = 0; s < 2; ++s) {
+      const uint16_t *base = static_cast<const uint16_t *>(ins[s]);
       a.side[s].ref = static_cast<const uint16_t *>(sides[s]->ref);
-      a.side[s].xin = static_cast<const uint16_t *>(ins[s]) + (size_t)(g0 / G) * in_loops * loop_elems;
-      for (int l = 0; l < G - 1; ++l) {
-        a.side[s].codes[l] = static_cast<uint8_t *>(sides[s]->codes[g0 + l]);
-        a.side[s].meta[l] = static_cast<uint32_t *>(sides[s]->meta[g0 + l]);
-        a.side[s].alpha[l] = static_cast<uint16_t *>(sides[s]->alpha[g0 + l]);
+      for (int i = 0; i < nres; ++i) {
+        const int l = res[i];
+        a.side[s].xin[i] = base + (size_t)in_index(l) * loop_elems;
+        a.side[s].codes[i] = static_cast<uint8_t *>(sides[s]->codes[l]);
+        a.side[s].meta[i] = static_cast<uint32_t *>(sides[s]->meta[l]);
+        a.side[s].alpha[i] = static_cast<uint16_t *>(sides[s]->alpha[l]);
       }
       if (L->ref_bits) {
-        a.side[s].codes[G - 1] = static_cast<uint8_t *>(sides[s]->codes[g0 + G - 1]);
-        a.side[s].meta[G - 1] = static_cast<uint32_t *>(sides[s]->meta[g0 + G - 1]);
+        a.side[s].xin[nres] = base + (size_t)in_index(an) * loop_elems;
+        a.side[s].codes[nres] = static_cast<uint8_t *>(sides[s]->codes[an]);
+        a.side[s].meta[nres] = static_cast<uint32_t *>(sides[s]->meta[an]);
       }
     }
-    for (int l = 0; l < G - 1; ++l) a.bits[l] = L->bits[g0 + l];
+    for (int i = 0; i < nres; ++i) a.bits[i] = L->bits[res[i]];
     a.abits = L->ref_bits;
     a.agroup = anchor_group(L);
+    a.alpha_mode = L->alpha_mode;
     a.n_res = G - 1;
     a.bh = (int32_t)bh;
     a.cap = L->capacity;
@@ -304,10 +320,10 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   const int G = group_len(L);
   (void)hipGetLastError();
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
-    const int ref_loop = g0 + G - 1;          // this group's reference / anchor
+    const int ref_loop = anchor_of(L, g0);    // this group's reference / anchor
     int res[RQ_MAX_LOOPS], nres = 0;
-    for (int l = g0; l < ref_loop; ++l)
-      if ((loop_mask >> l) & 1u) res[nres++] = l;
+    for (int l = g0; l < g0 + G; ++l)
+      if (l != ref_loop && ((loop_mask >> l) & 1u)) res[nres++] = l;
     bool want_ref = (loop_mask >> ref_loop) & 1u;
     if (nres == 0 && !want_ref) continue;
     if (L->ref_bits) {

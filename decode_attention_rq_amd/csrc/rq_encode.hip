@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   } else {
     // the anchor: loop L-1 of the input, quantized like a residual (groups of
     // agroup, no LS coefficient); y becomes its dequantized value
-    const uint16_t *yp = S.xin + (((size_t)a.n_res * a.bh + bh) * a.n + tlc) * D + 8 * j;
+    const uint16_t *yp = S.xin[a.n_res] + ((size_t)bh * a.n + tlc) * D + 8 * j;
     unpack_bf16x8(*reinterpret_cast<const uint4 *>(yp), y);
     if (a.rotate) {
       wht8<D>(y, lane);
@@ -146,13 +146,23 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   const float den = dot_sum<LANES>(t);
 
   for (int l = 0; l < a.n_res; ++l) {
-    const uint16_t *xp = S.xin + (((size_t)l * a.bh + bh) * a.n + tlc) * D + 8 * j;
+    const uint16_t *xp = S.xin[l] + ((size_t)bh * a.n + tlc) * D + 8 * j;
     float x[8];
     unpack_bf16x8(*reinterpret_cast<const uint4 *>(xp), x);
+    float alpha32;
+    if (a.alpha_mode == 1) {
+      alpha32 = 1.0f;
+    } else if (a.alpha_mode == 2) {                    // ||x|| / ||y||
 #pragma unroll
-    for (int p = 0; p < 8; ++p) t[p] = x[p] * y[p];
-    const float num = dot_sum<LANES>(t);
-    const float alpha32 = den > 0.0f ? num / den : 0.0f;
+      for (int p = 0; p < 8; ++p) t[p] = x[p] * x[p];
+      const float nx = dot_sum<LANES>(t);
+      alpha32 = den > 0.0f ? __builtin_sqrtf(nx) / __builtin_sqrtf(den) : 0.0f;
+    } else {                                           // <x,y> / <y,y>
+#pragma unroll
+      for (int p = 0; p < 8; ++p) t[p] = x[p] * y[p];
+      const float num = dot_sum<LANES>(t);
+      alpha32 = den > 0.0f ? num / den : 0.0f;
+    }
     const uint32_t a16 = f32_to_f16_sat(alpha32);
     const float af = f16_to_f32(a16);
 

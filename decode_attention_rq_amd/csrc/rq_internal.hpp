@@ -10,11 +10,13 @@
 namespace rq {
 
 // Kernel argument blocks.  Plane pointers are per residual loop.
+// One encode launch covers one anchor group: residual loops 0..n_res-1 of the
+// launch and, with a quantized anchor, the anchor at index n_res.
 struct EncodeSide {
   const uint16_t *ref;               // bf16 [BH][cap][D] (BF16 reference)
-  const uint16_t *xin;               // bf16 [L-1][BH][n][D]; [L][BH][n][D] with an anchor
-  uint8_t *codes[RQ_MAX_LOOPS];      // [L-1]: the anchor's codes
-  uint32_t *meta[RQ_MAX_LOOPS];      // (scale | zero << 16) per group; [L-1]: the anchor's
+  const uint16_t *xin[RQ_MAX_LOOPS]; // bf16 [BH][n][D] input of residual i; [n_res]: the anchor's
+  uint8_t *codes[RQ_MAX_LOOPS];      // [n_res]: the anchor's codes
+  uint32_t *meta[RQ_MAX_LOOPS];      // (scale | zero << 16) per group; [n_res]: the anchor's
   uint16_t *alpha[RQ_MAX_LOOPS];
 };
 
@@ -31,6 +33,7 @@ struct EncodeArgs {
   int32_t tasks_per_side;            // bh * chunks
   int32_t abits;                     // 0: BF16 reference; 2, 4: quantized anchor
   int32_t agroup;                    // the anchor's group size
+  int32_t alpha_mode;                // 0 least squares, 1 alpha = 1, 2 norm ratio
 };
 
 struct ReconArgs {

@@ -88,6 +88,12 @@ typedef struct {
                                     are residuals against it (Table 8: one INT4
                                     anchor per group of loops).  G >= 2 divides
                                     n_loops; G < n_loops needs ref_bits > 0         */
+    int32_t ref_first;           /* 0: each group's LAST loop is its reference (the
+                                    Last-loop policy); 1: its FIRST loop (First-loop
+                                    policy; Table 1, Table 9)                       */
+    int32_t alpha_mode;          /* residual scaling (Table 9 columns): 0 least
+                                    squares <x,y>/<y,y>; 1 none (alpha = 1);
+                                    2 norm ratio ||x|| / ||y||                      */
 } rq_layout;
 
 /* One side (K or V) of one layer's cache: caller-owned device planes.
@@ -112,7 +118,9 @@ typedef struct {
  * quantization with a per-loop bit width (steps 1 and 5; Table 5).  For each
  * (loop l < L-1, batch b, head h, token t) and separately for K and V, with
  * x the loop-l vector and y = ref[b][h][t] (both BF16, widened exactly):
- *   alpha = fp16(<x,y> / <y,y>)   (0 if <y,y> = 0; each dot product sums
+ *   alpha = fp16(<x,y> / <y,y>)   (alpha_mode 0; 0 if <y,y> = 0; alpha_mode 1:
+ *                                   1; alpha_mode 2: sqrt(<x,x>) / sqrt(<y,y>),
+ *                                   0 if <y,y> = 0; each dot product sums
  *                                   its FP32 terms in blocks of 8 by pairwise
  *                                   halving, then the block sums by pairwise
  *                                   halving; FP16 stores round to nearest
@@ -135,9 +143,9 @@ typedef struct {
  *
  *   k, v    caches; with a BF16 reference their ref planes must already hold
  *           tokens [t0, t0+n)
- *   k_in    bf16 [L-1][B][H][n][d] contiguous: the new K vectors of loops 0..L-2;
- *           with a quantized anchor [L][B][H][n][d], loop L-1 (the anchor's
- *           input) last
+ *   k_in    bf16 [L-1][B][H][n][d] contiguous: the new K vectors of the loops
+ *           other than the reference, in loop order; with quantized anchors
+ *           [L][B][H][n][d], every loop in loop order (anchors included)
  *   v_in    same for V
  *   t0, n   0 <= t0, 0 <= n, t0 + n <= capacity (n = 0 is a no-op)
  * Writes codes/meta/alpha of loops 0..L-2 (and the anchor's codes/meta) at

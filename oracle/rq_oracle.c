@@ -184,6 +184,30 @@ float rqo_alpha_f32(const uint16_t *x, const uint16_t *y, int d)
     return rqo_alpha_f32_y(x, yf, d);
 }
 
+/* The scaling coefficients the pages compare (Table 9 columns "Residual",
+ * "Norm-ratio", "LS scaling"; Fig. 3 right: alpha = 1 without LS):
+ *   mode 0: least squares <x,y>/<y,y>
+ *   mode 1: no scaling, alpha = 1
+ *   mode 2: norm ratio ||x|| / ||y|| = sqrt(<x,x>) / sqrt(<y,y>)  (0 if y = 0)
+ * Dot products sum in the contract order; sqrt and division round to
+ * nearest (IEEE). */
+float rqo_alpha_mode_f32_y(const uint16_t *x, const float *y, int d, int mode)
+{
+    if (mode == 1)
+        return 1.0f;
+    if (mode == 0)
+        return rqo_alpha_f32_y(x, y, d);
+    float xx[RQO_MAX_D], yy[RQO_MAX_D];
+    for (int i = 0; i < d; ++i) {
+        float xf = rqo_bf16_to_f32(x[i]);
+        xx[i] = xf * xf;
+        yy[i] = y[i] * y[i];
+    }
+    float nx = rqo_dot_sum(xx, d);
+    float ny = rqo_dot_sum(yy, d);
+    return ny > 0.0f ? sqrtf(nx) / sqrtf(ny) : 0.0f;
+}
+
 /* Stored coefficient: one FP16 value per (loop, batch, head, token), for K and
  * V separately.  Reading of the pages' effective-bitwidth accounting, which
  * counts LS coefficients and adds 0.1 bit per value for residual loops over
@@ -281,17 +305,25 @@ static void rqo_quantize_vector(float *u, int d, int g, int bits, int rotate,
 
 /* Encode one head_dim vector x of a residual loop against an FP32 reference y
  * (the BF16 final loop, or the dequantized anchor). */
-void rqo_encode_vector_y(const uint16_t *x, const float *y, int d, int g,
-                         int bits, int rotate, uint8_t *packed, uint16_t *meta,
-                         uint16_t *alpha)
+void rqo_encode_vector_ym(const uint16_t *x, const float *y, int d, int g,
+                          int bits, int rotate, int alpha_mode, uint8_t *packed,
+                          uint16_t *meta, uint16_t *alpha)
 {
     float u[RQO_MAX_D];
     uint8_t codes[RQO_MAX_D];
-    *alpha = rqo_f32_to_f16_sat(rqo_alpha_f32_y(x, y, d));
+    *alpha = rqo_f32_to_f16_sat(rqo_alpha_mode_f32_y(x, y, d, alpha_mode));
     float a = rqo_f16_to_f32(*alpha);          /* the stored value is what decode sees */
     for (int i = 0; i < d; ++i)
         u[i] = fmaf(-a, y[i], rqo_bf16_to_f32(x[i]));
     rqo_quantize_vector(u, d, g, bits, rotate, codes, packed, meta);
+}
+
+/* The same with least-squares scaling. */
+void rqo_encode_vector_y(const uint16_t *x, const float *y, int d, int g,
+                         int bits, int rotate, uint8_t *packed, uint16_t *meta,
+                         uint16_t *alpha)
+{
+    rqo_encode_vector_ym(x, y, d, g, bits, rotate, 0, packed, meta, alpha);
 }
 
 /* Encode one head_dim vector x of a residual loop against the BF16 reference y. */
@@ -341,8 +373,10 @@ void rqo_anchor_vector(const uint16_t *y, int d, int g, int bits, int rotate,
  *   codes[l], meta[l], alpha[l]:  planes of loop l (layouts at the top)  */
 void rqo_encode(int L, int B, int H, int d, int g, int cap, int rotate,
                 const int *bits, const uint16_t *ref, const uint16_t *xin,
-                int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha)
+                int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha,
+                int alpha_mode)
 {
+    float yf[RQO_MAX_D];
     int G = d / g;
     for (int l = 0; l < L - 1; ++l) {
         int nb = d * bits[l] / 8;
@@ -353,9 +387,11 @@ void rqo_encode(int L, int B, int H, int d, int g, int cap, int rotate,
                     size_t slot = bh * cap + (size_t)(t0 + t);
                     const uint16_t *x = xin + ((((size_t)l * B + b) * H + h) * n + t) * d;
                     const uint16_t *y = ref + slot * d;
-                    rqo_encode_vector(x, y, d, g, bits[l], rotate,
-                                      codes[l] + slot * nb, meta[l] + slot * 2 * G,
-                                      alpha[l] + slot);
+                    for (int i = 0; i < d; ++i)
+                        yf[i] = rqo_bf16_to_f32(y[i]);
+                    rqo_encode_vector_ym(x, yf, d, g, bits[l], rotate, alpha_mode,
+                                         codes[l] + slot * nb, meta[l] + slot * 2 * G,
+                                         alpha[l] + slot);
                 }
     }
 }
@@ -367,7 +403,8 @@ void rqo_encode(int L, int B, int H, int d, int g, int cap, int rotate,
  *   first and its dequantized value is every residual loop's reference. */
 void rqo_encode_anchored(int L, int B, int H, int d, int g, int ga, int abits,
                          int cap, int rotate, const int *bits, const uint16_t *xin,
-                         int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha)
+                         int t0, int n, uint8_t **codes, uint16_t **meta, uint16_t **alpha,
+                         int alpha_mode)
 {
     int G = d / g, Ga = d / ga, nba = d * abits / 8;
     float yhat[RQO_MAX_D];
@@ -382,8 +419,9 @@ void rqo_encode_anchored(int L, int B, int H, int d, int g, int ga, int abits,
                 for (int l = 0; l < L - 1; ++l) {
                     int nb = d * bits[l] / 8;
                     const uint16_t *x = xin + ((((size_t)l * B + b) * H + h) * n + t) * d;
-                    rqo_encode_vector_y(x, yhat, d, g, bits[l], rotate, codes[l] + slot * nb,
-                                        meta[l] + slot * 2 * G, alpha[l] + slot);
+                    rqo_encode_vector_ym(x, yhat, d, g, bits[l], rotate, alpha_mode,
+                                         codes[l] + slot * nb, meta[l] + slot * 2 * G,
+                                         alpha[l] + slot);
                 }
             }
 }

@@ -64,7 +64,7 @@ def lib():
                                         _u8p, _u16p, C.POINTER(C.c_uint16)]
         L.rqo_encode.restype = None
         L.rqo_encode.argtypes = [C.c_int] * 7 + [_i32p, _u16p, _u16p, C.c_int, C.c_int,
-                                                 C.c_void_p, C.c_void_p, C.c_void_p]
+                                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_int]
         L.rqo_reconstruct_vector.restype = None
         L.rqo_reconstruct_vector.argtypes = [_u8p, _u16p, C.c_uint16, _u16p, C.c_int,
                                              C.c_int, C.c_int, C.c_int, _f64p]
@@ -88,7 +88,9 @@ def lib():
                                         _f32p]
         L.rqo_encode_anchored.restype = None
         L.rqo_encode_anchored.argtypes = [C.c_int] * 9 + [_i32p, _u16p, C.c_int, C.c_int,
-                                                          C.c_void_p, C.c_void_p, C.c_void_p]
+                                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_int]
+        L.rqo_alpha_mode_f32_y.restype = C.c_float
+        L.rqo_alpha_mode_f32_y.argtypes = [_u16p, _f32p, C.c_int, C.c_int]
         L.rqo_dequant_f64.restype = None
         L.rqo_dequant_f64.argtypes = [_u8p, _u16p, C.c_int, C.c_int, C.c_int, C.c_int, _f64p]
         L.rqo_reconstruct_anchored.restype = None
@@ -235,35 +237,67 @@ def ref_group(layout: dict) -> int:
     return int(layout.get("ref_group") or layout["g"])
 
 
+def alpha_mode(layout: dict) -> int:
+    """0: least squares, 1: alpha = 1, 2: norm ratio (Table 9's columns)."""
+    return int(layout.get("alpha_mode", 0))
+
+
+def alpha_mode_f32(x_bits, y_f32, mode: int) -> float:
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    y = np.ascontiguousarray(y_f32, dtype=np.float32)
+    return float(lib().rqo_alpha_mode_f32_y(x, y, x.size, int(mode)))
+
+
 def group_len(layout: dict) -> int:
     """Loops per anchor group (Table 8 caption: each group of loops ends in one
     INT4 anchor); the whole schedule is one group unless group_loops is set."""
     return int(layout.get("group_loops") or layout["n_loops"])
 
 
+def ref_first(layout: dict) -> bool:
+    """First-loop reference policy (the pages' Table 1 / Table 9): each group's
+    first loop is its reference instead of its last."""
+    return bool(layout.get("ref_first", 0))
+
+
+def anchor_loop(layout: dict, l: int) -> int:
+    """The reference loop of loop l's group."""
+    G = group_len(layout) if anchored(layout) else layout["n_loops"]
+    g0 = (l // G) * G
+    return g0 if ref_first(layout) else g0 + G - 1
+
+
+def group_order(layout: dict, l: int):
+    """The loops of loop l's group as the C side takes them: the group's
+    residual loops in loop order, then its reference."""
+    G = group_len(layout) if anchored(layout) else layout["n_loops"]
+    g0 = (l // G) * G
+    an = anchor_loop(layout, g0)
+    return [l for l in range(g0, g0 + G) if l != an] + [an]
+
+
 class Planes:
-    """One cache side (K or V), as numpy arrays in the contract layout: the
-    BF16 reference and each residual loop's codes / meta / alpha planes; with
-    a quantized anchor (ref_bits > 0) no reference plane, and codes / meta
-    lists one longer, the anchor's planes last."""
+    """One cache side (K or V), as numpy arrays in the contract layout, lists
+    indexed by loop.  BF16 reference: `ref` holds it and its loop's entries are
+    None.  Quantized anchors: no `ref`; an anchor loop's codes / meta are in
+    the anchor format and its alpha is None."""
 
     def __init__(self, n_loops, batch, heads, d, g, cap, bits, ref_bits=0, ref_group=None,
-                 group_loops=0):
+                 group_loops=0, ref_first=0):
         ga = ref_group or g
-        G = group_loops or n_loops
+        G = (group_loops or n_loops) if ref_bits else n_loops
         shape = (batch, heads, cap)
-        if not ref_bits:
-            self.ref = np.zeros(shape + (d,), dtype=np.uint16)
-            self.codes = [np.zeros(shape + (d * bits[l] // 8,), dtype=np.uint8) for l in range(n_loops - 1)]
-            self.meta = [np.zeros(shape + (d // g, 2), dtype=np.uint16) for l in range(n_loops - 1)]
-            self.alpha = [np.zeros(shape, dtype=np.uint16) for l in range(n_loops - 1)]
-            return
-        self.ref = None
+        self.ref = None if ref_bits else np.zeros(shape + (d,), dtype=np.uint16)
         self.codes, self.meta, self.alpha = [], [], []
         for l in range(n_loops):
-            if (l + 1) % G == 0:                 # the group's anchor
-                self.codes.append(np.zeros(shape + (d * ref_bits // 8,), dtype=np.uint8))
-                self.meta.append(np.zeros(shape + (d // ga, 2), dtype=np.uint16))
+            g0 = (l // G) * G
+            if l == (g0 if ref_first else g0 + G - 1):          # a reference loop
+                if ref_bits:
+                    self.codes.append(np.zeros(shape + (d * ref_bits // 8,), dtype=np.uint8))
+                    self.meta.append(np.zeros(shape + (d // ga, 2), dtype=np.uint16))
+                else:
+                    self.codes.append(None)
+                    self.meta.append(None)
                 self.alpha.append(None)
             else:
                 self.codes.append(np.zeros(shape + (d * bits[l] // 8,), dtype=np.uint8))
@@ -278,30 +312,37 @@ def _ptrs(arrs):
 def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) -> None:
     """Encode tokens [t0, t0+n) into `planes` (in place).
     layout: dict(n_loops, batch, heads, d, g, cap, rotate, bits[, ref_bits,
-    ref_group]).  BF16 reference: x_bits is bf16 bits [L-1, B, H, n, d] and
-    planes.ref already holds the reference.  Quantized anchor: x_bits is
-    [L, B, H, n, d], the anchor's input last."""
+    ref_group, group_loops, ref_first, alpha_mode]).  BF16 reference: x_bits
+    is bf16 bits [L-1, B, H, n, d], the non-reference loops in loop order, and
+    planes.ref already holds the reference.  Quantized anchors: x_bits is
+    [L, B, H, n, d], every loop in loop order."""
     L, B, H = layout["n_loops"], layout["batch"], layout["heads"]
     d, g, cap = layout["d"], layout["g"], layout["cap"]
-    bits = np.ascontiguousarray(layout["bits"][:L - 1], dtype=np.int32)
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if anchored(layout):
         assert x.shape == (L, B, H, n, d)
         G = group_len(layout)
         for g0 in range(0, L, G):             # every group on its own
-            cp, mp = _ptrs(planes.codes[g0:g0 + G]), _ptrs(planes.meta[g0:g0 + G])
-            ap = _ptrs(planes.alpha[g0:g0 + G - 1])
-            gbits = np.ascontiguousarray(layout["bits"][g0:g0 + G - 1], dtype=np.int32)
+            order = group_order(layout, g0)
+            res = order[:-1]
+            cp, mp = _ptrs([planes.codes[l] for l in order]), _ptrs([planes.meta[l] for l in order])
+            ap = _ptrs([planes.alpha[l] for l in res])
+            gbits = np.ascontiguousarray([layout["bits"][l] for l in res], dtype=np.int32)
             lib().rqo_encode_anchored(G, B, H, d, g, ref_group(layout), int(layout["ref_bits"]), cap,
-                                      int(layout["rotate"]), gbits, np.ascontiguousarray(x[g0:g0 + G]),
+                                      int(layout["rotate"]), gbits, np.ascontiguousarray(x[order]),
                                       t0, n, C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p),
-                                      C.cast(ap, C.c_void_p))
+                                      C.cast(ap, C.c_void_p), alpha_mode(layout))
         return
-    cp, mp, ap = _ptrs(planes.codes), _ptrs(planes.meta), _ptrs(planes.alpha)
     assert x.shape == (L - 1, B, H, n, d)
+    res = group_order(layout, 0)[:-1]
+    bits = np.ascontiguousarray([layout["bits"][l] for l in res], dtype=np.int32)
+    cp = _ptrs([planes.codes[l] for l in res])
+    mp = _ptrs([planes.meta[l] for l in res])
+    ap = _ptrs([planes.alpha[l] for l in res])
     lib().rqo_encode(L, B, H, d, g, cap, int(layout["rotate"]), bits,
                      np.ascontiguousarray(planes.ref), x, t0, n,
-                     C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p), C.cast(ap, C.c_void_p))
+                     C.cast(cp, C.c_void_p), C.cast(mp, C.c_void_p), C.cast(ap, C.c_void_p),
+                     alpha_mode(layout))
 
 
 # ---------------------------------------------------------------------------
@@ -310,15 +351,14 @@ def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) ->
 
 def reconstruct(layout: dict, planes: Planes, loop: int, t0: int, n: int) -> np.ndarray:
     """x_hat of loop `loop` for tokens [t0, t0+n): float64 [B, H, n, d].
-    BF16 reference: loop < L-1.  Quantized anchor: any loop; loop L-1 is the
-    dequantized anchor."""
-    L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
+    BF16 reference: a residual loop.  Quantized anchors: any loop; an anchor
+    loop gives the dequantized anchor."""
+    B, H, d = layout["batch"], layout["heads"], layout["d"]
     out = np.zeros((B, H, n, d), dtype=np.float64)
+    an = anchor_loop(layout, loop)
     if anchored(layout):
-        G = group_len(layout)
-        an = (loop // G) * G + G - 1         # the loop's anchor
         anchor = loop == an
-        li = an - 1 if anchor else loop      # stand-in residual planes (unread for the anchor)
+        li = group_order(layout, an)[0] if anchor else loop     # stand-in, unread for the anchor
         lib().rqo_reconstruct_anchored(B, H, d, layout["g"], ref_group(layout),
                                        int(layout["ref_bits"]), layout["cap"],
                                        int(layout["rotate"]), int(layout["bits"][li]),
@@ -327,6 +367,7 @@ def reconstruct(layout: dict, planes: Planes, loop: int, t0: int, n: int) -> np.
                                        planes.alpha[li].ctypes.data, -1 if anchor else loop,
                                        t0, n, out)
         return out
+    assert loop != an, "the BF16 reference is not reconstructed"
     lib().rqo_reconstruct(B, H, d, layout["g"], layout["cap"], int(layout["rotate"]),
                           int(layout["bits"][loop]), planes.ref, planes.codes[loop],
                           planes.meta[loop], planes.alpha[loop], t0, n, out)
@@ -348,17 +389,18 @@ def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: i
     """Attention output (float64 [d]) of loop `loop`'s query for (b, h) over
     the n_ctx cached tokens and then the tail rows (bf16 bits [T, d] of this
     (loop, b, h)), if given."""
-    L, B, H, d = layout["n_loops"], layout["batch"], layout["heads"], layout["d"]
-    # One anchor group at a time: the C side sees the group's loops as a
-    # schedule of G loops whose last is the reference.
-    G = group_len(layout) if anchored(layout) else L
-    g0 = (loop // G) * G
-    an = g0 + G - 1
-    # The reference loop attends over the reference alone; its residual plane
-    # arguments are ignored by the C side, so the group's first planes stand in.
-    li = g0 if loop == an else loop
+    B, H, d = layout["batch"], layout["heads"], layout["d"]
+    an = anchor_loop(layout, loop)
+    is_ref = loop == an
+    # The C side sees a schedule of G loops whose last is the reference: the
+    # row's loop is either that reference or a residual (view index 0, with
+    # its own planes); every view loop carries this loop's query.
+    G = len(group_order(layout, an))
+    li = group_order(layout, an)[0] if is_ref else loop
+    c_loop = G - 1 if is_ref else 0
     bits = int(layout["bits"][li])
-    q_grp = np.ascontiguousarray(np.asarray(q_bits, dtype=np.uint16)[g0:g0 + G])
+    q = np.asarray(q_bits, dtype=np.uint16)
+    q_view = np.ascontiguousarray(np.repeat(q[loop][None], G, axis=0))
     out = np.zeros(d, dtype=np.float64)
     ptr = lambda a: None if a is None else np.ascontiguousarray(a).ctypes.data
     keep = []
@@ -383,7 +425,7 @@ def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: i
                             ptr(kref), ptr(kp.codes[li]), ptr(kp.meta[li]), ptr(kp.alpha[li]),
                             ptr(vref), ptr(vp.codes[li]), ptr(vp.meta[li]), ptr(vp.alpha[li]),
                             ga, abits, *[ptr(x) for x in anc], tk, tv, n_tail,
-                            q_grp, loop - g0, b, h, n_ctx, float(scale), out)
+                            q_view, c_loop, b, h, n_ctx, float(scale), out)
     return out
 
 

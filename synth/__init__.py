@@ -44,6 +44,8 @@ class Workload:
     ref_bits: int = 0               # 0: BF16 reference; 2/4: quantized anchor
     ref_group: int = 0              # the anchor's group size (0: g)
     group_loops: int = 0            # loops per anchor group (0: one group)
+    ref_first: int = 0              # 1: first loop of each group is the reference
+    alpha_mode: int = 0             # 0 least squares, 1 alpha = 1, 2 norm ratio
     extra: dict = field(default_factory=dict)
 
 

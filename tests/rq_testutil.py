@@ -21,21 +21,24 @@ def tol_rel_row(got: np.ndarray, want: np.ndarray) -> np.ndarray:
 def oracle_layout(w: synth.Workload, batch: int, cap: int) -> dict:
     return dict(n_loops=w.n_loops, batch=batch, heads=w.heads, d=w.d, g=w.g, cap=cap,
                 rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits, ref_group=w.ref_group,
-                group_loops=w.group_loops)
+                group_loops=w.group_loops, ref_first=w.ref_first, alpha_mode=w.alpha_mode)
 
 
 def gpu_layout(w: synth.Workload, batch: int, cap: int):
     import decode_attention_rq_amd as rq
     return rq.Layout(n_loops=w.n_loops, batch=batch, n_heads=w.heads, head_dim=w.d, group=w.g,
                      capacity=cap, rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits,
-                     ref_group=w.ref_group, group_loops=w.group_loops)
+                     ref_group=w.ref_group, group_loops=w.group_loops, ref_first=w.ref_first,
+                     alpha_mode=w.alpha_mode)
 
 
 def encoder_input(w: synth.Workload, loops: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
-    """rq_encode's input: the residual loops, plus the anchor's own input
-    last when the reference is a quantized anchor."""
+    """rq_encode's input in loop order: with a BF16 reference the other loops;
+    with quantized anchors every loop, the drawn reference being the first
+    loop (First-loop policy) or the last."""
     if w.ref_bits:
-        return torch.cat([loops, ref.unsqueeze(0)])
+        parts = [ref.unsqueeze(0), loops] if w.ref_first else [loops, ref.unsqueeze(0)]
+        return torch.cat(parts)
     return loops
 
 
@@ -87,9 +90,9 @@ class Case:
                 return t[tuple(idx)].unsqueeze(ax + 1)
         lay = oracle_layout(w, B, n)
         kp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None,
-                           w.group_loops)
+                           w.group_loops, w.ref_first)
         vp = oracle.Planes(w.n_loops, B, H, w.d, w.g, n, w.bits, w.ref_bits, w.ref_group or None,
-                           w.group_loops)
+                           w.group_loops, w.ref_first)
         if bh_list is None:
             kr, vr, kl, vl, q = (self.data["k_ref"], self.data["v_ref"], self.data["k_loops"],
                                  self.data["v_loops"], self.data["q"])

@@ -292,3 +292,27 @@ def test_anchor_groups_check_every_anchor(rq):
     assert _decode(rq, lay, k=k, v=v, mask=0b0001) == INVALID     # loop 0 needs its group's anchor
     assert _decode(rq, lay, k=k, v=v, mask=0b1100, ws_bytes=1) == WORKSPACE   # group 1 does not
     assert _encode(rq, lay, k=k, v=v) == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha_mode=3), UNSUPPORTED), (dict(alpha_mode=-1), UNSUPPORTED), (dict(ref_first=2), INVALID),
+])
+def test_policy_validation(rq, kw, code):
+    lay = _layout(rq, **kw)
+    assert _encode(rq, lay) == code
+    assert _decode(rq, lay) == code
+
+
+def test_first_loop_policy_planes(rq):
+    """With the first loop as reference, loop 0 has no residual planes and the
+    last loop does."""
+    lay = _layout(rq, ref_first=1, bits=[0, 2, 2, 2])
+    k, v = _cache(rq), _cache(rq)
+    k.codes[0] = k.meta[0] = k.alpha[0] = 0
+    v.codes[0] = v.meta[0] = v.alpha[0] = 0
+    k.codes[3], k.meta[3], k.alpha[3] = FAKE + 0x3000, FAKE + 0x300000, FAKE + 0x30000000
+    v.codes[3], v.meta[3], v.alpha[3] = FAKE + 0x3000, FAKE + 0x300000, FAKE + 0x30000000
+    assert _decode(rq, lay, k=k, v=v, ws_bytes=1) == WORKSPACE
+    k.alpha[3] = 0
+    assert _decode(rq, lay, k=k, v=v) == INVALID
+    assert _decode(rq, lay, k=k, v=v, mask=0b0111, ws_bytes=1) == WORKSPACE

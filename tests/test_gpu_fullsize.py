@@ -103,10 +103,11 @@ def test_encode_empty_range_touches_nothing():
     import decode_attention_rq_amd as rq
     w = synth.WORKLOADS["tiny"]
     case = Case(w, 16, cap=32)
-    before = [plane_bits(t).copy() for t in case.k.codes + case.k.meta + case.k.alpha]
+    planes = [t for t in case.k.codes + case.k.meta + case.k.alpha if t is not None]
+    before = [plane_bits(t).copy() for t in planes]
     # n = 0 at the end of the cache: valid, enqueues nothing (any aligned
     # pointer stands in for the empty inputs)
     rq.rq_encode(case.lay, case.k, case.v, case.k.ref, case.v.ref, 32, 0)
     torch.cuda.synchronize()
-    after = [plane_bits(t) for t in case.k.codes + case.k.meta + case.k.alpha]
+    after = [plane_bits(t) for t in planes]
     assert all(np.array_equal(a, b) for a, b in zip(before, after))

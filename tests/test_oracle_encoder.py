@@ -223,3 +223,81 @@ def test_groups_are_contiguous_dims(oracle):
     scales = meta[0::2]
     assert scales[1] == 0 and all(scales[k] != 0 for k in (0, 2, 3))
     assert meta[3] == np.float16(_f32(x)[32]).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# scaling-coefficient variants (Table 9 columns "Residual", "Norm-ratio",
+# "LS scaling"; Fig. 3 right: alpha = 1 without LS)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_alpha_modes_closed_forms(oracle, seed):
+    rng = np.random.default_rng(300 + seed)
+    d = 128
+    y = _bf16(rng.standard_normal(d) * np.exp(0.5 * rng.standard_normal(d)))
+    x = _bf16(_f32(y) * rng.uniform(0.5, 1.2) + 0.3 * rng.standard_normal(d))
+    yf = _f32(y)
+    xd, yd = _f32(x).astype(np.float64), yf.astype(np.float64)
+    # no scaling: exactly one
+    assert oracle.alpha_mode_f32(x, yf, 1) == 1.0
+    # norm ratio: ||x|| / ||y|| to FP32 rounding of the sums
+    nr = oracle.alpha_mode_f32(x, yf, 2)
+    assert abs(nr - np.linalg.norm(xd) / np.linalg.norm(yd)) <= 1e-6 * nr
+    # least squares is the default mode and minimises the residual energy
+    ls = oracle.alpha_mode_f32(x, yf, 0)
+    assert ls == oracle.alpha_f32(x, y)
+    e = lambda a: float(((xd - a * yd) ** 2).sum())
+    assert e(ls) <= e(nr) and e(ls) <= e(1.0)
+
+
+def test_norm_ratio_ignores_sign_least_squares_does_not(oracle):
+    """x = -2 y: least squares finds -2 exactly, the norm ratio +2."""
+    rng = np.random.default_rng(9)
+    y = _bf16(rng.standard_normal(64))
+    x = _bf16(-2.0 * _f32(y))
+    yf = _f32(y)
+    assert oracle.alpha_mode_f32(x, yf, 0) == -2.0
+    assert oracle.alpha_mode_f32(x, yf, 2) == 2.0
+    # and a zero reference gives 0 for both
+    z = np.zeros(64, dtype=np.float32)
+    assert oracle.alpha_mode_f32(x, z, 0) == 0.0 and oracle.alpha_mode_f32(x, z, 2) == 0.0
+
+
+@pytest.mark.parametrize("anchored", [False, True])
+def test_first_loop_policy_is_a_relabelling(oracle, anchored):
+    """Table 1 / Table 9: the First-loop policy references loop 1 instead of the
+    last.  Encoding loops [r, a, b, c] with the first as reference gives, loop
+    for loop, the planes of encoding [a, b, c, r] with the last as reference."""
+    import synth
+    rng = np.random.default_rng(5)
+    L, B, H, d, g, n = 4, 1, 2, 64, 16, 10
+    ref = _bf16(rng.standard_normal((B, H, n, d)))
+    loops = _bf16(0.9 * _f32(ref)[None] + 0.1 * rng.standard_normal((L - 1, B, H, n, d)))
+    extra = dict(ref_bits=4, ref_group=32) if anchored else {}
+    base = dict(n_loops=L, batch=B, heads=H, d=d, g=g, cap=n, rotate=1, **extra)
+    first = dict(base, bits=[0, 2, 4, 2], ref_first=1)
+    last = dict(base, bits=[2, 4, 2, 0])
+    pf = oracle.Planes(L, B, H, d, g, n, first["bits"], extra.get("ref_bits", 0), extra.get("ref_group"),
+                       ref_first=1)
+    pl = oracle.Planes(L, B, H, d, g, n, last["bits"], extra.get("ref_bits", 0), extra.get("ref_group"))
+    if anchored:
+        oracle.encode(first, pf, np.concatenate([ref[None], loops]), 0, n)
+        oracle.encode(last, pl, np.concatenate([loops, ref[None]]), 0, n)
+    else:
+        pf.ref[:], pl.ref[:] = ref, ref
+        oracle.encode(first, pf, loops, 0, n)
+        oracle.encode(last, pl, loops, 0, n)
+    perm = [3, 0, 1, 2]             # loop of `first` -> loop of `last`
+    for lf, ll in enumerate(perm):
+        for name in ("codes", "meta", "alpha"):
+            a, b = getattr(pf, name)[lf], getattr(pl, name)[ll]
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert np.array_equal(a, b), (lf, name)
+    q = _bf16(rng.standard_normal((L, B, H, d)))
+    qp = q[[1, 2, 3, 0]]           # the same queries in `last`'s loop order
+    for lf, ll in enumerate(perm):
+        if anchored or lf != 0:
+            assert np.array_equal(oracle.reconstruct(first, pf, lf, 0, n), oracle.reconstruct(last, pl, ll, 0, n))
+        assert np.array_equal(oracle.decode_row(first, pf, pf, q, lf, 0, 1, n, 0.2),
+                              oracle.decode_row(last, pl, pl, qp, ll, 0, 1, n, 0.2))
