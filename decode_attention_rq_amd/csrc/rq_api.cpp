@@ -175,7 +175,7 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
 
   const int G = group_len(L);
   const int64_t bh = (int64_t)L->batch * L->n_heads;
-  const int vpw = 64 / (L->head_dim / 8);
+  const int vpw = 64 / (L->head_dim / rq::kEncodeElemsPerLane);   // vectors per encode wave
   const int chunks = (n + vpw - 1) / vpw;
   if (bh * chunks * 2 > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
   const rq_cache *sides[2] = {k, v};

@@ -32,12 +32,36 @@ __device__ __forceinline__ uint32_t f32_to_f16_sat(float x) {
 // lane exchange
 // ---------------------------------------------------------------------------
 
-// Value of `x` in lane (lane ^ mask).  Masks < 32 stay inside 32-lane halves
-// and use ds_swizzle (bitmask mode, no LDS allocation); 32 uses ds_bpermute.
+// DPP lane moves inside a 16-lane row (VALU only, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
+
+constexpr int kDppQuadReverse = 0x1B;    // quad_perm [3,2,1,0]
+
+// Value of `x` in lane (lane ^ mask).  Masks 1 and 2 are one DPP quad
+// permutation; 4 is the half-row mirror (i -> 7-i) after a quad reversal
+// (4a+b -> 4a+3-b), 8 the row mirror (i -> 15-i) after the half-row mirror:
+// VALU moves, no LDS traffic.  16 uses ds_swizzle (bitmask mode, no LDS
+// allocation) and 32 ds_bpermute.
 template <int MASK>
 __device__ __forceinline__ float xor_lane(float x) {
   static_assert(MASK > 0 && MASK < 64 && (MASK & (MASK - 1)) == 0, "power-of-two lane mask");
-  if constexpr (MASK < 32) {
+  if constexpr (MASK == 1) {
+    return dpp<kDppQuadXor1>(x);
+  } else if constexpr (MASK == 2) {
+    return dpp<kDppQuadXor2>(x);
+  } else if constexpr (MASK == 4) {
+    return dpp<kDppHalfMirror>(dpp<kDppQuadReverse>(x));
+  } else if constexpr (MASK == 8) {
+    return dpp<kDppRowMirror>(dpp<kDppHalfMirror>(x));
+  } else if constexpr (MASK < 32) {
     // offset[15] = 0: and_mask = 0x1f, or_mask = 0, xor_mask = MASK
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
                                                                   0x1f | (MASK << 10)));
@@ -87,17 +111,6 @@ __device__ __forceinline__ float group_min(float x) {
   return x;
 }
 
-// DPP lane moves inside a 16-lane row (VALU only, no LDS traffic).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
-}
-constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
-constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
-
 // Sum over aligned groups of N in {8, 16, 32} lanes, every lane receiving
 // the total.  After the quad sums, a mirror pairs each lane with one in the
 // other half of its 8 (then 16) lanes.
@@ -114,13 +127,15 @@ __device__ __forceinline__ float group_sum_dpp(float x) {
 
 // One cross-lane butterfly stage of the Walsh-Hadamard transform: element i
 // of this lane pairs with element i of lane (lane ^ MASK).  The lane with the
-// MASK bit clear holds the lower index a and keeps a + b; its partner keeps
-// a - b.  Same two IEEE operations, same operand order, as the sequential
-// definition.
+// MASK bit clear holds the lower index a and keeps a + b; its partner, holding
+// b, keeps a - b.  Both are the partner's value plus this lane's value, the
+// upper lane's sign flipped: b + a = a + b (IEEE addition is commutative) and
+// a + (-b) = a - b, so the results are those of the sequential definition.
 template <int MASK>
 __device__ __forceinline__ float wht_stage(float own, int lane) {
-  float other = xor_lane<MASK>(own);
-  return (lane & MASK) ? (other - own) : (own + other);
+  const float other = xor_lane<MASK>(own);
+  const uint32_t flip = (lane & MASK) ? 0x80000000u : 0u;
+  return other + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, own) ^ flip);
 }
 
 // In-register Walsh-Hadamard transform (unnormalized) of a D-vector spread

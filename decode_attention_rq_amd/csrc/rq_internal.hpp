@@ -10,6 +10,9 @@
 namespace rq {
 
 // Kernel argument blocks.  Plane pointers are per residual loop.
+// Encoder lane mapping: consecutive dims of one vector per lane.
+constexpr int kEncodeElemsPerLane = 32;
+
 // One encode launch covers one anchor group: residual loops 0..n_res-1 of the
 // launch and, with a quantized anchor, the anchor at index n_res.
 struct EncodeSide {
