@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=256, help="(batch, head) pairs the oracle decodes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-baseline", action="store_true")
+    p.add_argument("--graphs", action="store_true",
+                   help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
     p.add_argument("--mode", default="decode", choices=["decode", "copy"],
                    help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling")
     a = p.parse_args()
@@ -199,6 +201,35 @@ def timed(fn, steps, warmup):
         fn(i)
     e1.record()
     torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def timed_graph(fn, steps, warmup):
+    """Mean ms per step of fn, captured once into a HIP graph (torch's
+    CUDAGraph on the current stream) and replayed `steps` times after
+    `warmup` replays; HIP events bracket the replays."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(0)
+    for i in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
     return e0.elapsed_time(e1) / steps
 
 
@@ -624,7 +655,7 @@ def grid_bench(args, w, budget=250e9):
                 for kv_, vv_, tv_ in views:
                     for l in range(L):
                         rq.rq_decode_attn_tail(lay_b, kv_, vv_, tv_, q, 1 << l, n, scale, out, ws, splits)
-            ms = timed(step, steps, 2)
+            ms = (timed_graph if args.graphs else timed)(step, steps, 2)
             rq_rows.append({"batch": B, "ms_per_step": round(ms, 3), "tokens_per_s": round(B / (ms / 1e3), 1)})
         del layers, tails, views
         torch.cuda.empty_cache()
@@ -649,7 +680,7 @@ def grid_bench(args, w, budget=250e9):
                     for ks, vs in views:
                         for l in range(L):
                             rq.rq_bf16_decode_attn(blay, ks, vs, q, 1 << l, nb, scale, out, ws, splits)
-                ms = timed(bstep, steps, 2)
+                ms = (timed_graph if args.graphs else timed)(bstep, steps, 2)
                 bf_rows.append({"batch": B, "ms_per_step": round(ms, 3), "tokens_per_s": round(B / (ms / 1e3), 1)})
             del bl, views
             torch.cuda.empty_cache()
@@ -673,7 +704,8 @@ def grid_bench(args, w, budget=250e9):
             "data": "synthetic",
             "config": {"workload": f"{w.name}: {NL} layers x ({H} heads, head_dim {d}, {L} loops, INT{w.ref_bits} "
                                    f"anchor g={w.ref_group}, residual bits {w.bits} g={w.g}, {T} BF16 tail tokens), "
-                                   f"contexts {w.extra['contexts']}"},
+                                   f"contexts {w.extra['contexts']}",
+                       "timing": "HIP graph replay" if args.graphs else "eager launches"},
             "grid": rows}
 
 

@@ -11,7 +11,7 @@ namespace rq {
 // kTailBatch tokens (loads issued together, reductions interleaved) with its
 // own online softmax; the waves' states meet in LDS.  Wave 0 then merges the
 // splits' records with the tail state by log-sum-exp and finishes the row.
-constexpr int kTailBatch = 8;
+constexpr int kTailBatch = 16;
 constexpr int kMergeWaves = 4;
 
 template <int D>
@@ -21,6 +21,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
   const int bh = blockIdx.x, s = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const bool residual = s < n_res;
+
+  // split records of this (slot, batch*head): their maximum first, so the
+  // record loads overlap the tail walk
+  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
+  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
+  float M = -FLT_MAX;
+  if (wave == 0)
+    for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
 
   float mt = -FLT_MAX, lt = 0.0f, ot[E];
 #pragma unroll
@@ -93,11 +101,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
     }
   }
 
-  // split records of this (slot, batch*head)
-  const size_t stride = (size_t)kMaxSlots * a.bh * REC;
-  const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
-  float M = -FLT_MAX;
-  for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
   M = group_max<64>(M);
   const float Mall = fmaxf(M, mt);
 
