@@ -426,6 +426,69 @@ void rqo_encode_anchored(int L, int B, int H, int d, int g, int ga, int abits,
             }
 }
 
+/* Chained references (RQ page Table 9 "Previous-loop" / "Next-loop"; Fig. 3
+ * left): each loop's reference is its neighbour towards the group's root
+ * loop, as decode will rebuild it.  After a loop is encoded against y, the
+ * next loop's reference is that loop's FP32 reconstruction
+ *   y <- fmaf(a, y, r_hat),  r_hat = c*H(fmaf(code, s, z)) (or unrotated)
+ * (the reading: closed loop, one rounding per FMA, the butterflies of the
+ * rotation in their usual order).  ord lists the group's residual loops from
+ * the root outwards; xin holds the loops of the group in loop order. */
+void rqo_reconstruct32_vector(const uint8_t *packed, const uint16_t *meta, uint16_t alpha,
+                              float *y, int d, int g, int bits, int rotate)
+{
+    uint8_t codes[RQO_MAX_D];
+    float u[RQO_MAX_D];
+    rqo_unpack(packed, d, bits, codes);
+    for (int i = 0; i < d; ++i) {
+        int k = i / g;
+        u[i] = fmaf((float)codes[i], rqo_f16_to_f32(meta[2 * k]), rqo_f16_to_f32(meta[2 * k + 1]));
+    }
+    if (rotate)
+        rqo_fwht_f32(u, d);
+    float a = rqo_f16_to_f32(alpha);
+    for (int i = 0; i < d; ++i)
+        y[i] = fmaf(a, y[i], u[i]);
+}
+
+/* Encode tokens [t0, t0+n) of one group with chained references.
+ *   L: loops in the group; root: the reference loop (index within the group);
+ *   ord[0..L-2]: residual loops from the root outwards; abits: 0 = the root is
+ *   the BF16 ref plane (ref), else a quantized anchor whose input is xin[root];
+ *   xin: bf16 [L][B][H][n][d] when anchored, else [L][B][H][n][d] with the
+ *   root's entry unused (the caller passes the group's loops in loop order,
+ *   the root's slot may hold anything). */
+void rqo_encode_chain(int L, int B, int H, int d, int g, int ga, int abits, int cap,
+                      int rotate, int alpha_mode, const int *bits, int root, const int *ord,
+                      const uint16_t *ref, const uint16_t *xin, int t0, int n,
+                      uint8_t **codes, uint16_t **meta, uint16_t **alpha)
+{
+    int G = d / g, Ga = d / ga;
+    float y[RQO_MAX_D];
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = 0; t < n; ++t) {
+                size_t bh = (size_t)b * H + h;
+                size_t slot = bh * cap + (size_t)(t0 + t);
+                if (abits) {
+                    const uint16_t *yi = xin + ((((size_t)root * B + b) * H + h) * n + t) * d;
+                    rqo_anchor_vector(yi, d, ga, abits, rotate, codes[root] + slot * (d * abits / 8),
+                                      meta[root] + slot * 2 * Ga, y);
+                } else {
+                    for (int i = 0; i < d; ++i)
+                        y[i] = rqo_bf16_to_f32(ref[slot * d + i]);
+                }
+                for (int k = 0; k < L - 1; ++k) {
+                    int l = ord[k], nb = d * bits[l] / 8;
+                    const uint16_t *x = xin + ((((size_t)l * B + b) * H + h) * n + t) * d;
+                    uint8_t *pc = codes[l] + slot * nb;
+                    uint16_t *pm = meta[l] + slot * 2 * G;
+                    rqo_encode_vector_ym(x, y, d, g, bits[l], rotate, alpha_mode, pc, pm, alpha[l] + slot);
+                    rqo_reconstruct32_vector(pc, pm, alpha[l][slot], y, d, g, bits[l], rotate);
+                }
+            }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Reconstruction and attention (FP64)                                       */
 /* ------------------------------------------------------------------------ */
@@ -523,6 +586,59 @@ void rqo_reconstruct_anchored(int B, int H, int d, int g, int ga, int abits, int
                     rqo_reconstruct_vector_y(codes + slot * nb, meta + slot * 2 * G, alpha[slot],
                                              y, d, g, bits, rotate, o);
             }
+}
+
+/* Chain reconstruction in FP64 of one vector of loop ord[upto] (0-based
+ * position along the chain from the root): y = root; y = a*y + r_hat for
+ * ord[0..upto].  rootv: the root's FP64 vector. */
+void rqo_reconstruct_chain_vector(const uint8_t **pc, const uint16_t **pm, const uint16_t **pa,
+                                  const int *bits, const int *ord, int upto, const double *rootv,
+                                  int d, int g, int rotate, double *out)
+{
+    double u[RQO_MAX_D];
+    memcpy(out, rootv, sizeof(double) * (size_t)d);
+    for (int k = 0; k <= upto; ++k) {
+        int l = ord[k];
+        rqo_dequant_f64(pc[l], pm[l], d, g, bits[l], rotate, u);
+        double a = rqo_f16_to_f32(*pa[l]);
+        for (int i = 0; i < d; ++i)
+            out[i] = a * out[i] + u[i];
+    }
+}
+
+/* FP64 rows of one (batch*head) bh, tokens [t0, t0+n), of the loop at chain
+ * position `upto` (-1: the root itself) of a group with chained references:
+ * the root is the BF16 plane `ref` (abits == 0) or the anchor planes ac/am;
+ * codes/meta/alpha are indexed by the loop's index within the group.
+ * out: float64 [n][d]. */
+void rqo_chain_rows(int d, int g, int ga, int abits, int cap, int rotate, const int *bits,
+                    const int *ord, int upto, const uint16_t *ref, const uint8_t *ac,
+                    const uint16_t *am, const uint8_t **codes, const uint16_t **meta,
+                    const uint16_t **alpha, int bh, int t0, int n, double *out)
+{
+    int G = d / g, Ga = abits ? d / ga : 0;
+    double rootv[RQO_MAX_D];
+    const uint8_t *pc[RQO_MAX_D];
+    const uint16_t *pm[RQO_MAX_D], *pa[RQO_MAX_D];
+    for (int t = 0; t < n; ++t) {
+        size_t slot = (size_t)bh * cap + (size_t)(t0 + t);
+        if (abits)
+            rqo_dequant_f64(ac + slot * (d * abits / 8), am + slot * 2 * Ga, d, ga, abits, rotate, rootv);
+        else
+            for (int i = 0; i < d; ++i)
+                rootv[i] = rqo_bf16_to_f32(ref[slot * d + i]);
+        for (int k = 0; k <= upto; ++k) {
+            int l = ord[k];
+            pc[l] = codes[l] + slot * (d * bits[l] / 8);
+            pm[l] = meta[l] + slot * 2 * G;
+            pa[l] = alpha[l] + slot;
+        }
+        if (upto < 0)
+            memcpy(out + (size_t)t * d, rootv, sizeof(double) * (size_t)d);
+        else
+            rqo_reconstruct_chain_vector(pc, pm, pa, bits, ord, upto, rootv, d, g, rotate,
+                                         out + (size_t)t * d);
+    }
 }
 
 /* Softmax attention of one query over n keys/values, in FP64:

@@ -97,6 +97,14 @@ def lib():
         L.rqo_reconstruct_anchored.argtypes = ([C.c_int] * 9 + [_u8p, _u16p, C.c_void_p, C.c_void_p,
                                                                 C.c_void_p, C.c_int, C.c_int,
                                                                 C.c_int, _f64p])
+        L.rqo_encode_chain.restype = None
+        L.rqo_encode_chain.argtypes = ([C.c_int] * 10 + [_i32p, C.c_int, _i32p, C.c_void_p, _u16p,
+                                                         C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                                         C.c_void_p])
+        L.rqo_chain_rows.restype = None
+        L.rqo_chain_rows.argtypes = ([C.c_int] * 6 + [_i32p, _i32p, C.c_int, C.c_void_p, C.c_void_p,
+                                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                      C.c_int, C.c_int, C.c_int, _f64p])
         L.rqo_decode_row_ex.restype = None
         L.rqo_decode_row_ex.argtypes = ([C.c_int] * 8
                                         + [C.c_void_p] * 8
@@ -267,6 +275,51 @@ def anchor_loop(layout: dict, l: int) -> int:
     return g0 if ref_first(layout) else g0 + G - 1
 
 
+def ref_chain(layout: dict) -> bool:
+    """Chained references (Table 9 "Previous-loop" / "Next-loop"): each loop's
+    reference is its neighbour towards the group's root loop."""
+    return bool(layout.get("ref_chain", 0))
+
+
+def chain_order(layout: dict, l: int):
+    """(g0, root, order) of loop l's group: the group's first loop, its root
+    (reference) loop, and its residual loops from the root outwards."""
+    G = group_len(layout) if anchored(layout) else layout["n_loops"]
+    g0 = (l // G) * G
+    root = anchor_loop(layout, g0)
+    if ref_first(layout):
+        order = list(range(g0 + 1, g0 + G))
+    else:
+        order = list(range(g0 + G - 2, g0 - 1, -1))
+    return g0, root, order
+
+
+def _pp(arrs):
+    """Array of pointers; None entries become NULL."""
+    return (C.c_void_p * max(1, len(arrs)))(*[0 if a is None else a.ctypes.data for a in arrs])
+
+
+def _chain_rows(layout: dict, planes: "Planes", loop: int, bh: int, t0: int, n: int) -> np.ndarray:
+    g0, root, order = chain_order(layout, loop)
+    G = len(order) + 1
+    d = layout["d"]
+    bits = np.ascontiguousarray([layout["bits"][g0 + i] if g0 + i != root else 0 for i in range(G)],
+                                dtype=np.int32)
+    ordi = np.ascontiguousarray([l - g0 for l in order], dtype=np.int32)
+    upto = -1 if loop == root else order.index(loop)
+    out = np.zeros((n, d), dtype=np.float64)
+    ab = int(layout.get("ref_bits", 0))
+    grp = lambda lst: [lst[g0 + i] for i in range(G)]
+    lib().rqo_chain_rows(d, layout["g"], ref_group(layout), ab, layout["cap"], int(layout["rotate"]),
+                         bits, ordi, upto,
+                         None if ab else planes.ref.ctypes.data,
+                         planes.codes[root].ctypes.data if ab else None,
+                         planes.meta[root].ctypes.data if ab else None,
+                         C.cast(_pp(grp(planes.codes)), C.c_void_p), C.cast(_pp(grp(planes.meta)), C.c_void_p),
+                         C.cast(_pp(grp(planes.alpha)), C.c_void_p), bh, t0, n, out)
+    return out
+
+
 def group_order(layout: dict, l: int):
     """The loops of loop l's group as the C side takes them: the group's
     residual loops in loop order, then its reference."""
@@ -319,6 +372,30 @@ def encode(layout: dict, planes: Planes, x_bits: np.ndarray, t0: int, n: int) ->
     L, B, H = layout["n_loops"], layout["batch"], layout["heads"]
     d, g, cap = layout["d"], layout["g"], layout["cap"]
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if ref_chain(layout):
+        G = group_len(layout) if anchored(layout) else L
+        if anchored(layout):
+            assert x.shape == (L, B, H, n, d)
+        else:
+            assert x.shape == (L - 1, B, H, n, d)
+            root = anchor_loop(layout, 0)
+            full = np.zeros((L, B, H, n, d), dtype=np.uint16)
+            full[[l for l in range(L) if l != root]] = x
+            x = full
+        for g0 in range(0, L, G):
+            _, root, order = chain_order(layout, g0)
+            bits = np.ascontiguousarray([layout["bits"][g0 + i] if g0 + i != root else 0 for i in range(G)],
+                                        dtype=np.int32)
+            ordi = np.ascontiguousarray([l - g0 for l in order], dtype=np.int32)
+            grp = lambda lst: [lst[g0 + i] for i in range(G)]
+            lib().rqo_encode_chain(G, B, H, d, g, ref_group(layout), int(layout.get("ref_bits", 0)), cap,
+                                   int(layout["rotate"]), alpha_mode(layout), bits, root - g0, ordi,
+                                   None if anchored(layout) else planes.ref.ctypes.data,
+                                   np.ascontiguousarray(x[g0:g0 + G]), t0, n,
+                                   C.cast(_pp(grp(planes.codes)), C.c_void_p),
+                                   C.cast(_pp(grp(planes.meta)), C.c_void_p),
+                                   C.cast(_pp(grp(planes.alpha)), C.c_void_p))
+        return
     if anchored(layout):
         assert x.shape == (L, B, H, n, d)
         G = group_len(layout)
@@ -356,6 +433,12 @@ def reconstruct(layout: dict, planes: Planes, loop: int, t0: int, n: int) -> np.
     B, H, d = layout["batch"], layout["heads"], layout["d"]
     out = np.zeros((B, H, n, d), dtype=np.float64)
     an = anchor_loop(layout, loop)
+    if ref_chain(layout):
+        assert anchored(layout) or loop != an, "the BF16 reference is not reconstructed"
+        for b in range(B):
+            for h in range(H):
+                out[b, h] = _chain_rows(layout, planes, loop, b * H + h, t0, n)
+        return out
     if anchored(layout):
         anchor = loop == an
         li = group_order(layout, an)[0] if anchor else loop     # stand-in, unread for the anchor
@@ -390,6 +473,14 @@ def decode_row(layout: dict, kp: Planes, vp: Planes, q_bits: np.ndarray, loop: i
     the n_ctx cached tokens and then the tail rows (bf16 bits [T, d] of this
     (loop, b, h)), if given."""
     B, H, d = layout["batch"], layout["heads"], layout["d"]
+    if ref_chain(layout):
+        k = _chain_rows(layout, kp, loop, b * H + h, 0, n_ctx)
+        v = _chain_rows(layout, vp, loop, b * H + h, 0, n_ctx)
+        if tail_k is not None:
+            k = np.concatenate([k, bf16_bits_to_f32(np.asarray(tail_k).ravel()).reshape(-1, d).astype(np.float64)])
+            v = np.concatenate([v, bf16_bits_to_f32(np.asarray(tail_v).ravel()).reshape(-1, d).astype(np.float64)])
+        qv = bf16_bits_to_f32(np.asarray(q_bits, dtype=np.uint16)[loop, b, h]).astype(np.float64)
+        return attention(qv, k, v, scale)
     an = anchor_loop(layout, loop)
     is_ref = loop == an
     # The C side sees a schedule of G loops whose last is the reference: the

@@ -262,3 +262,92 @@ def test_anchor_groups_are_independent_schedules(oracle):
             want = oracle.decode_row(sub, part, part, q[g0:g0 + G], l, 0, 1, n, 0.3, tk[g0 + l, 0, 1],
                                      tv[g0 + l, 0, 1])
             assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# chained references (Table 9 "Previous-loop" / "Next-loop")
+# --------------------------------------------------------------------------
+
+def _chain_layout(L, ref_first, anchored, n, d=64, g=16):
+    lay = dict(n_loops=L, batch=1, heads=2, d=d, g=g, cap=n, rotate=1, bits=[2] * L, ref_chain=1,
+               ref_first=ref_first)
+    if anchored:
+        lay.update(ref_bits=4, ref_group=32)
+    return lay
+
+
+@pytest.mark.parametrize("ref_first", [0, 1])
+def test_chain_references_the_neighbour(oracle, ref_first):
+    """Loops that halve along the chain: with the neighbour as reference every
+    stored alpha is 0.5 (the Last-loop policy would store 0.5, 0.25, 0.125)."""
+    rng = np.random.default_rng(17)
+    L, n, d = 4, 6, 64
+    lay = _chain_layout(L, ref_first, False, n, d=d)
+    root = 0 if ref_first else L - 1
+    y = _bf16(rng.standard_normal((1, 2, n, d)))
+    yf = _f32(y)
+    loops = {}
+    for k, l in enumerate(oracle.chain_order(lay, 0)[2]):
+        loops[l] = _bf16(yf * 0.5 ** (k + 1))            # exact in BF16
+    x = np.stack([loops[l] for l in range(L) if l != root])
+    p = oracle.Planes(L, 1, 2, d, 16, n, lay["bits"], ref_first=ref_first)
+    p.ref[:] = y
+    oracle.encode(lay, p, x, 0, n)
+    for l in range(L):
+        if l != root:
+            assert np.all(p.alpha[l] == 0x3800), l          # FP16 0.5
+            # and the chain rebuilds each loop exactly (zero residuals)
+            assert np.array_equal(oracle.reconstruct(lay, p, l, 0, n), _f32(loops[l]).astype(np.float64))
+
+
+@pytest.mark.parametrize("anchored", [False, True])
+@pytest.mark.parametrize("ref_first", [0, 1])
+def test_chain_error_does_not_accumulate(oracle, anchored, ref_first):
+    """Closed loop along the chain: each loop is rebuilt to within its own
+    grid error, however far from the root (an open chain would add up the
+    errors of every loop in between)."""
+    w = synth.Workload("c", n_loops=4, batch=1, heads=2, d=64, g=16, n_ctx=30, bits=[2, 2, 2],
+                       c=[0.8, 0.85, 0.9], sigma=[0.15, 0.12, 0.1], rotate=1, seed=23)
+    data = synth.draw_layer(w)
+    lay = _chain_layout(4, ref_first, anchored, 30)
+    root = 0 if ref_first else 3
+    loops = [bf16_bits(data["k_loops"][i]) for i in range(3)]
+    refb = bf16_bits(data["k_ref"])
+    seq = [refb] + loops if ref_first else loops + [refb]      # loop order
+    p = oracle.Planes(4, 1, 2, 64, 16, 30, lay["bits"], 4 if anchored else 0, 32 if anchored else None,
+                      ref_first=ref_first)
+    if anchored:
+        oracle.encode(lay, p, np.stack(seq), 0, 30)
+    else:
+        p.ref[:] = refb
+        oracle.encode(lay, p, np.stack([seq[l] for l in range(4) if l != root]), 0, 30)
+    for l in range(4):
+        if l == root:
+            continue
+        xh = oracle.reconstruct(lay, p, l, 0, 30)
+        x = _f32(seq[l]).astype(np.float64)
+        s = oracle.f16_bits_to_f32(p.meta[l][..., 0].ravel()).reshape(p.meta[l].shape[:-1]).astype(np.float64)
+        grid = np.sqrt((16 * (s / 2) ** 2).sum(-1))
+        err = np.linalg.norm(x - xh, axis=-1)
+        assert np.all(err <= grid * (1 + 1e-3) + 1e-5 * np.linalg.norm(x, axis=-1)), l
+        # decode over the chain's reconstruction is plain attention over it
+        q = _bf16(np.random.default_rng(l).standard_normal((4, 1, 2, 64)))
+        got = oracle.decode_row(lay, p, p, q, l, 0, 1, 30, 0.3)
+        want = _sdpa(_f32(q[l, 0, 1]).astype(np.float64), xh[0, 1], xh[0, 1], 0.3)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_chain_of_one_residual_is_the_plain_policy(oracle):
+    """With a single residual loop its neighbour is the root: the chain policy
+    gives the Last-loop bytes."""
+    rng = np.random.default_rng(3)
+    y = _bf16(rng.standard_normal((1, 2, 9, 64)))
+    x = _bf16(0.9 * _f32(y) + 0.1 * rng.standard_normal((1, 1, 2, 9, 64)))
+    base = dict(n_loops=2, batch=1, heads=2, d=64, g=16, cap=9, rotate=1, bits=[2])
+    pa = oracle.Planes(2, 1, 2, 64, 16, 9, [2])
+    pb = oracle.Planes(2, 1, 2, 64, 16, 9, [2])
+    pa.ref[:], pb.ref[:] = y, y
+    oracle.encode(base, pa, x, 0, 9)
+    oracle.encode(dict(base, ref_chain=1), pb, x, 0, 9)
+    assert np.array_equal(pa.codes[0], pb.codes[0]) and np.array_equal(pa.meta[0], pb.meta[0])
+    assert np.array_equal(pa.alpha[0], pb.alpha[0])
