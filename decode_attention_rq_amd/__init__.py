@@ -29,7 +29,7 @@ class rq_layout(C.Structure):
                 ("head_dim", C.c_int32), ("group", C.c_int32), ("capacity", C.c_int32),
                 ("rotate", C.c_int32), ("bits", C.c_int32 * RQ_MAX_LOOPS),
                 ("ref_bits", C.c_int32), ("ref_group", C.c_int32), ("group_loops", C.c_int32),
-                ("ref_first", C.c_int32), ("alpha_mode", C.c_int32)]
+                ("ref_first", C.c_int32), ("alpha_mode", C.c_int32), ("ref_chain", C.c_int32)]
 
 
 class rq_cache(C.Structure):
@@ -103,6 +103,7 @@ class Layout:
     group_loops: int = 0     # loops per anchor group (0: all loops, one group)
     ref_first: int = 0       # 1: each group's first loop is its reference
     alpha_mode: int = 0      # 0 least squares, 1 alpha = 1, 2 norm ratio
+    ref_chain: int = 0       # 1: each loop refers to its neighbour towards the reference
 
     @property
     def anchor_group(self) -> int:
@@ -123,6 +124,7 @@ class Layout:
         s.group_loops = int(self.group_loops)
         s.ref_first = int(self.ref_first)
         s.alpha_mode = int(self.alpha_mode)
+        s.ref_chain = int(self.ref_chain)
         return s
 
 

@@ -33,6 +33,10 @@ rq_status check_layout(const rq_layout *L) {
   if (G < 2 || G > L->n_loops || L->n_loops % G != 0) return RQ_ERR_UNSUPPORTED;
   if (L->ref_first != 0 && L->ref_first != 1) return RQ_ERR_INVALID_ARG;
   if (L->alpha_mode < 0 || L->alpha_mode > 2) return RQ_ERR_UNSUPPORTED;
+  if (L->ref_chain != 0 && L->ref_chain != 1) return RQ_ERR_INVALID_ARG;
+  // a chain pass reads every link between the root and the loop: at most
+  // kMaxRes residual loops per group; anchors of 4 bits or BF16 roots
+  if (L->ref_chain && (G - 1 > rq::kMaxRes || L->ref_bits == 2)) return RQ_ERR_UNSUPPORTED;
   const int aof = L->ref_first ? 0 : G - 1;         // the anchor's place in its group
   for (int l = 0; l < L->n_loops; ++l)
     if (l % G != aof && L->bits[l] != 2 && L->bits[l] != 4) return RQ_ERR_UNSUPPORTED;
@@ -57,6 +61,18 @@ int anchor_of(const rq_layout *L, int l) {
   return (l / G) * G + (L->ref_first ? 0 : G - 1);
 }
 bool is_anchor(const rq_layout *L, int l) { return anchor_of(L, l) == l; }
+
+// The residual loops of loop g0's group from the root outwards (the chain
+// order; also the encode order).  Returns their number.
+int chain_order(const rq_layout *L, int g0, int *ord) {
+  const int G = group_len(L);
+  int n = 0;
+  if (L->ref_first)
+    for (int l = g0 + 1; l < g0 + G; ++l) ord[n++] = l;
+  else
+    for (int l = g0 + G - 2; l >= g0; --l) ord[n++] = l;
+  return n;
+}
 
 // The reference planes of the group whose anchor is loop a: the BF16 ref
 // plane, or the anchor's codes and meta.
@@ -187,8 +203,12 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
     const int an = anchor_of(L, g0);
     int res[RQ_MAX_LOOPS], nres = 0;                 // this group's residual loops
-    for (int l = g0; l < g0 + G; ++l)
-      if (l != an) res[nres++] = l;
+    if (L->ref_chain) {
+      nres = chain_order(L, g0, res);                // root outwards: each refers to the previous
+    } else {
+      for (int l = g0; l < g0 + G; ++l)
+        if (l != an) res[nres++] = l;
+    }
     // input index of loop l
     auto in_index = [&](int l) { return L->ref_bits ? l : (l < an ? l : l - 1); };
     rq::EncodeArgs a;
@@ -213,6 +233,7 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
     a.abits = L->ref_bits;
     a.agroup = anchor_group(L);
     a.alpha_mode = L->alpha_mode;
+    a.chain = L->ref_chain;
     a.n_res = G - 1;
     a.bh = (int32_t)bh;
     a.cap = L->capacity;
@@ -275,6 +296,12 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
       if (!ref_planes_ok(L, k, an) || !ref_planes_ok(L, v, an)) return RQ_ERR_INVALID_ARG;
       if (!is_anchor(L, l) && (!residual_planes_ok(k, l) || !residual_planes_ok(v, l)))
         return RQ_ERR_INVALID_ARG;
+      if (L->ref_chain && !is_anchor(L, l)) {        // every link between the root and l
+        int ord[RQ_MAX_LOOPS];
+        const int nc = chain_order(L, (l / group_len(L)) * group_len(L), ord);
+        for (int c = 0; c < nc && ord[c] != l; ++c)
+          if (!residual_planes_ok(k, ord[c]) || !residual_planes_ok(v, ord[c])) return RQ_ERR_INVALID_ARG;
+      }
     }
     if (n_tail > 0 && (!aligned16(tail->k[l]) || !aligned16(tail->v[l]))) return RQ_ERR_INVALID_ARG;
   }
@@ -311,6 +338,7 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.n_tail = n_tail;
   a.tcap = tail ? tail->capacity : 0;
   a.records = (S > 1 || n_tail > 0) ? 1 : 0;
+  a.out_mask = loop_mask;
   a.group = L->group;
   a.rotate = L->rotate;
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
@@ -322,8 +350,19 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
     const int ref_loop = anchor_of(L, g0);    // this group's reference / anchor
     int res[RQ_MAX_LOOPS], nres = 0;
-    for (int l = g0; l < g0 + G; ++l)
-      if (l != ref_loop && ((loop_mask >> l) & 1u)) res[nres++] = l;
+    if (L->ref_chain) {
+      // one pass over the chain from the farthest loop asked for to the root,
+      // slots farthest first (each slot's reference is the next slot)
+      int ord[RQ_MAX_LOOPS];
+      const int nc = chain_order(L, g0, ord);
+      int far = -1;
+      for (int c = 0; c < nc; ++c)
+        if ((loop_mask >> ord[c]) & 1u) far = c;
+      for (int c = far; c >= 0; --c) res[nres++] = ord[c];
+    } else {
+      for (int l = g0; l < g0 + G; ++l)
+        if (l != ref_loop && ((loop_mask >> l) & 1u)) res[nres++] = l;
+    }
     bool want_ref = (loop_mask >> ref_loop) & 1u;
     if (nres == 0 && !want_ref) continue;
     if (L->ref_bits) {
@@ -362,7 +401,7 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
       }
       hipError_t e;
       if (n_ctx > 0)
-        e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, stream);
+        e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, L->ref_chain != 0, stream);
       else   // the tail alone: the merge kernel attends over it, no split records
         e = rq::launch_merge(a, L->head_dim, cnt, cnt + (want_ref ? 1 : 0), stream);
       if (e != hipSuccess) return RQ_ERR_DEVICE;
@@ -420,6 +459,7 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
   rq::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
   a.records = S > 1 ? 1 : 0;
+  a.out_mask = 0xffffffffu;
   a.agroup = 32;
   a.ws = static_cast<float *>(workspace);
   a.out = out;
@@ -439,7 +479,8 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
     a.kref = static_cast<const uint16_t *>(k_loops[l]);
     a.vref = static_cast<const uint16_t *>(v_loops[l]);
     a.qloop[0] = l;
-    if (rq::launch_decode(a, L->head_dim, 0, true, 0, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    if (rq::launch_decode(a, L->head_dim, 0, true, 0, false, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
       return RQ_ERR_DEVICE;
   }
   return RQ_OK;
@@ -471,6 +512,18 @@ rq_status rq_reconstruct(const rq_layout *L, const rq_cache *c, int32_t loop, in
     a.meta = static_cast<const uint32_t *>(c->meta[loop]);
     a.alpha = static_cast<const uint16_t *>(c->alpha[loop]);
     a.bits = L->bits[loop];
+    if (L->ref_chain) {                             // the links between the root and loop
+      int ord[RQ_MAX_LOOPS];
+      const int nc = chain_order(L, (loop / group_len(L)) * group_len(L), ord);
+      for (int q = 0; q < nc && ord[q] != loop; ++q) {
+        if (!residual_planes_ok(c, ord[q])) return RQ_ERR_INVALID_ARG;
+        a.pcodes[a.npre] = static_cast<const uint8_t *>(c->codes[ord[q]]);
+        a.pmeta[a.npre] = static_cast<const uint32_t *>(c->meta[ord[q]]);
+        a.palpha[a.npre] = static_cast<const uint16_t *>(c->alpha[ord[q]]);
+        a.pbits[a.npre] = L->bits[ord[q]];
+        ++a.npre;
+      }
+    }
   }
   a.out = out;
   a.bh = L->batch * L->n_heads;

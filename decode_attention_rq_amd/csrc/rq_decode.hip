@@ -21,6 +21,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
   const int bh = blockIdx.x, s = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const bool residual = s < n_res;
+  if (!((a.out_mask >> a.qloop[s]) & 1u)) return;   // a chain link computed, not asked for
 
   // split records of this (slot, batch*head): their maximum first, so the
   // record loads overlap the tail walk
@@ -141,7 +142,7 @@ template <int D>
 static int blocks_per_cu_d() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0>, 64 * kWaves, 0) != hipSuccess)
+          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0, false>, 64 * kWaves, 0) != hipSuccess)
     return -1;
   return n;
 }
@@ -155,14 +156,26 @@ int decode_blocks_per_cu(int head_dim) {
   }
 }
 
-template hipError_t launch_decode_aq<0>(const DecodeArgs &, int, int, bool, hipStream_t);
+template hipError_t launch_decode_aq<0, false>(const DecodeArgs &, int, int, bool, hipStream_t);
+// instantiated in rq_decode_anchor{2,4}.hip and rq_decode_chain{0,4}.hip
+extern template hipError_t launch_decode_aq<2, false>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<4, false>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<0, true>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<4, true>(const DecodeArgs &, int, int, bool, hipStream_t);
 
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
-                         hipStream_t st) {
+                         bool chain, hipStream_t st) {
+  if (chain) {
+    switch (anchor_bits) {
+      case 0: return launch_decode_aq<0, true>(a, head_dim, n_res, ref, st);
+      case 4: return launch_decode_aq<4, true>(a, head_dim, n_res, ref, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (anchor_bits) {
-    case 0: return launch_decode_aq<0>(a, head_dim, n_res, ref, st);
-    case 2: return launch_decode_aq<2>(a, head_dim, n_res, ref, st);
-    case 4: return launch_decode_aq<4>(a, head_dim, n_res, ref, st);
+    case 0: return launch_decode_aq<0, false>(a, head_dim, n_res, ref, st);
+    case 2: return launch_decode_aq<2, false>(a, head_dim, n_res, ref, st);
+    case 4: return launch_decode_aq<4, false>(a, head_dim, n_res, ref, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -101,6 +101,7 @@ __device__ __forceinline__ void finish_row(const DecodeArgs &a, int bh, int s, b
                                            float L, float (&o)[D / 64], float (&w)[D / 64],
                                            const float (&t)[D / 64]) {
   constexpr int E = D / 64;
+  if (!((a.out_mask >> a.qloop[s]) & 1u)) return;   // a chain link computed, not asked for
   const bool ref_rot = a.ref_rotated != 0;
   if (residual || ref_rot) {
     if (ref_rot) {
@@ -248,7 +249,11 @@ struct Tile : RefTile<TR, AQ> {
 // rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int NR, bool REF, int B4, int TR, int W, int AQ>
+// CHAIN: chained references (each residual loop's reference is the next slot's
+// reconstruction, the last residual slot's is the pass's reference).  Slot i
+// then scores q_i . K_i with K_i = a_i K_{i+1} + r_i unrolled down the chain,
+// and accumulates p_i (prod a) r_m for every m >= i into its residual sum.
+template <int D, int NR, bool REF, int B4, int TR, int W, int AQ, bool CHAIN>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   constexpr int LANES = D / 8;
   constexpr int ROWS = kWave / LANES;
@@ -418,13 +423,25 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           part[s] = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[s], 0.0f));
         }
       }
+      uint32_t hk[NRA][4];
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        if ((B4 >> m) & 1) code_halves<true>(T.kc[u][m], hk[m]);
+        else code_halves<false>(T.kc[u][m], hk[m]);
+      }
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        const float dc = ((B4 >> i) & 1) ? code_dot<true>(T.kc[u][i], qr[i], 0.0f)
-                                         : code_dot<false>(T.kc[u][i], qr[i], 0.0f);
-        const uint32_t mw = T.km[u][i];
-        const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
-        part[i] = __builtin_fmaf(h_lo(T.ka[u][i]), part[i], t);
+        // K_i = a_i K_{i+1} + r_i: from the reference (part) down to loop i
+        float acc = part[i];
+#pragma unroll
+        for (int m = NR - 1; m >= i; --m) {
+          if (!CHAIN && m != i) continue;
+          const float dc = code_dot_h(hk[m], qr[i], 0.0f);
+          const uint32_t mw = T.km[u][m];
+          const float t = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[i], 0.0f));
+          acc = __builtin_fmaf(h_lo(T.ka[u][m]), acc, t);
+        }
+        part[i] = acc;
       }
       const bool valid = FULL || base + u * ROWS + r < t_end;
 #pragma unroll
@@ -482,25 +499,36 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       float pq[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) pq[s] = quad_bcast(p_own, s);
+      uint32_t hvc[NRA][4];
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        if ((B4 >> m) & 1) code_halves<true>(T.vc[u][m], hvc[m]);
+        else code_halves<false>(T.vc[u][m], hvc[m]);
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float pr = pq[s];
         if (s < NR) {
-          const uint32_t mw = T.vm[u][s];
-          const float wr = __builtin_fmaf(h_lo(T.va[u][s]), pr, 0.0f);
-          const float wq = __builtin_fmaf(h_lo(mw), pr, 0.0f);
-          zacc[s] = __builtin_fmaf(h_hi(mw), pr, zacc[s]);
+          // p (s_m code + z_m) for loop s (and, chained, every loop after it,
+          // each weighted by the alphas on the way), then the reference's part
+          float w = pr;
+#pragma unroll
+          for (int m = s; m < NR; ++m) {
+            if (!CHAIN && m != s) continue;
+            const uint32_t mw = T.vm[u][m];
+            zacc[s] = __builtin_fmaf(h_hi(mw), w, zacc[s]);
+            code_axpy_h(hvc[m], __builtin_fmaf(h_lo(mw), w, 0.0f), ores[s]);
+            w = __builtin_fmaf(h_lo(T.va[u][m]), w, 0.0f);
+          }
           if constexpr (AQ == 0) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(wr, y[p], oref[s][p]);
+            for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(w, y[p], oref[s][p]);
           } else {
             // alpha_V p (s_a code + z_a), into the residual accumulator
             const uint32_t am = T.amv[u];
-            zacc[s] = __builtin_fmaf(h_hi(am), wr, zacc[s]);
-            code_axpy_h(hv, __builtin_fmaf(h_lo(am), wr, 0.0f), ores[s]);
+            zacc[s] = __builtin_fmaf(h_hi(am), w, zacc[s]);
+            code_axpy_h(hv, __builtin_fmaf(h_lo(am), w, 0.0f), ores[s]);
           }
-          if ((B4 >> s) & 1) code_axpy<true>(T.vc[u][s], wq, ores[s]);
-          else code_axpy<false>(T.vc[u][s], wq, ores[s]);
         } else if constexpr (AQ == 0) {
 #pragma unroll
           for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pr, y[p], oref[s][p]);
@@ -616,60 +644,61 @@ constexpr int kWaves = 4;
 template <int NS>
 constexpr int tiles_per_iter() { return NS == 1 ? 4 : kTilesPerIter; }
 
-template <int D, int NR, bool REF, int B4, int AQ>
+template <int D, int NR, bool REF, int B4, int AQ, bool CHAIN>
 static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
   constexpr int TR = tiles_per_iter<NR + (REF ? 1 : 0)>();
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ, CHAIN>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
   return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);
 }
 
 // Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
-template <int D, int NR, bool REF, int AQ>
+template <int D, int NR, bool REF, int AQ, bool CHAIN>
 static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
   int b4 = 0;
   for (int i = 0; i < NR; ++i) b4 |= (a.bits[i] == 4) << i;
   switch (b4) {
-    case 0: return launch_kernel<D, NR, REF, 0, AQ>(a, st);
-    case 1: if constexpr (NR >= 1) return launch_kernel<D, NR, REF, 1, AQ>(a, st); break;
-    case 2: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 2, AQ>(a, st); break;
-    case 3: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 3, AQ>(a, st); break;
-    case 4: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 4, AQ>(a, st); break;
-    case 5: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 5, AQ>(a, st); break;
-    case 6: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 6, AQ>(a, st); break;
-    case 7: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 7, AQ>(a, st); break;
+    case 0: return launch_kernel<D, NR, REF, 0, AQ, CHAIN>(a, st);
+    case 1: if constexpr (NR >= 1) return launch_kernel<D, NR, REF, 1, AQ, CHAIN>(a, st); break;
+    case 2: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 2, AQ, CHAIN>(a, st); break;
+    case 3: if constexpr (NR >= 2) return launch_kernel<D, NR, REF, 3, AQ, CHAIN>(a, st); break;
+    case 4: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 4, AQ, CHAIN>(a, st); break;
+    case 5: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 5, AQ, CHAIN>(a, st); break;
+    case 6: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 6, AQ, CHAIN>(a, st); break;
+    case 7: if constexpr (NR >= 3) return launch_kernel<D, NR, REF, 7, AQ, CHAIN>(a, st); break;
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, int AQ>
+template <int D, int AQ, bool CHAIN>
 static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
   if (ref) {
     switch (n_res) {
-      case 0: return launch_bits<D, 0, true, AQ>(a, st);
-      case 1: return launch_bits<D, 1, true, AQ>(a, st);
-      case 2: return launch_bits<D, 2, true, AQ>(a, st);
-      case 3: return launch_bits<D, 3, true, AQ>(a, st);
+      case 0: return launch_bits<D, 0, true, AQ, CHAIN>(a, st);
+      case 1: return launch_bits<D, 1, true, AQ, CHAIN>(a, st);
+      case 2: return launch_bits<D, 2, true, AQ, CHAIN>(a, st);
+      case 3: return launch_bits<D, 3, true, AQ, CHAIN>(a, st);
     }
   } else {
     switch (n_res) {
-      case 1: return launch_bits<D, 1, false, AQ>(a, st);
-      case 2: return launch_bits<D, 2, false, AQ>(a, st);
-      case 3: return launch_bits<D, 3, false, AQ>(a, st);
+      case 1: return launch_bits<D, 1, false, AQ, CHAIN>(a, st);
+      case 2: return launch_bits<D, 2, false, AQ, CHAIN>(a, st);
+      case 3: return launch_bits<D, 3, false, AQ, CHAIN>(a, st);
     }
   }
   return hipErrorInvalidValue;
 }
 
-// One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits).
-template <int AQ>
+// One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits),
+// chained references or not.
+template <int AQ, bool CHAIN>
 hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
   switch (head_dim) {
-    case 64: return launch_decode_d<64, AQ>(a, n_res, ref, st);
-    case 128: return launch_decode_d<128, AQ>(a, n_res, ref, st);
-    case 256: return launch_decode_d<256, AQ>(a, n_res, ref, st);
+    case 64: return launch_decode_d<64, AQ, CHAIN>(a, n_res, ref, st);
+    case 128: return launch_decode_d<128, AQ, CHAIN>(a, n_res, ref, st);
+    case 256: return launch_decode_d<256, AQ, CHAIN>(a, n_res, ref, st);
     default: return hipErrorInvalidValue;
   }
 }

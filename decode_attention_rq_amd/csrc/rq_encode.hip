@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
       for (int p = 0; p < EPL; ++p) y[p] = y[p] * a.rot_c;
     }
   }
-  const float den = dot_sum32<LANES>(y, y);          // exact products for a BF16 y
+  float den = dot_sum32<LANES>(y, y);                // exact products for a BF16 y
 
   for (int l = 0; l < a.n_res; ++l) {
     float x[EPL];
@@ -238,6 +238,23 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
     uint32_t sz[2];
     quantize_store<D>(x, a.bits[l], a.group, q, sz, S.codes[l], S.meta[l], oslot, j, valid);
     if (valid && j == 0) S.alpha[l][oslot] = (uint16_t)a16;
+    if (a.chain && l + 1 < a.n_res) {
+      // chained references: the next loop's reference is this loop's
+      // reconstruction, y <- fma(alpha, y, r_hat), r_hat = c*H(fma(code, s, z))
+#pragma unroll
+      for (int p = 0; p < EPL; ++p) {
+        const uint32_t w = (a.group == 32 || p < 16) ? sz[0] : sz[1];
+        x[p] = __builtin_fmaf(q[p], f16_to_f32(w & 0xffffu), f16_to_f32(w >> 16));
+      }
+      if (a.rotate) {
+        fwht32<LANES>(x, lane);
+#pragma unroll
+        for (int p = 0; p < EPL; ++p) x[p] = x[p] * a.rot_c;
+      }
+#pragma unroll
+      for (int p = 0; p < EPL; ++p) y[p] = __builtin_fmaf(af, y[p], x[p]);
+      den = dot_sum32<LANES>(y, y);
+    }
   }
 }
 

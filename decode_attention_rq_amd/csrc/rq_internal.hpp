@@ -37,6 +37,7 @@ struct EncodeArgs {
   int32_t abits;                     // 0: BF16 reference; 2, 4: quantized anchor
   int32_t agroup;                    // the anchor's group size
   int32_t alpha_mode;                // 0 least squares, 1 alpha = 1, 2 norm ratio
+  int32_t chain;                     // residual i+1's reference is residual i's reconstruction
 };
 
 struct ReconArgs {
@@ -51,6 +52,13 @@ struct ReconArgs {
   float rot_c;
   int32_t chunks;
   int32_t abits, agroup;
+  // chained references: the loops between the root and this one, root side
+  // first, each rebuilt as y = alpha*y + r_hat before this loop's own step
+  int32_t npre;
+  const uint8_t *pcodes[3];
+  const uint32_t *pmeta[3];
+  const uint16_t *palpha[3];
+  int32_t pbits[3];
 };
 
 constexpr int kMaxRes = 3;           // residual loops per decode pass
@@ -73,6 +81,8 @@ struct DecodeArgs {
   const uint16_t *tk[kMaxSlots], *tv[kMaxSlots];   // BF16 tail rows per slot [BH][tcap][D]
   int32_t tcap, n_tail;
   int32_t records;                   // write split records and merge (S > 1 or a tail)
+  uint32_t out_mask;                 // loops whose rows are written (a chain pass also
+                                     // computes the links between them and the root)
   int32_t bh, cap, n_ctx, n_splits, tps;
   int32_t group, rotate;
   float qscale;                      // sm_scale * log2(e)
@@ -85,8 +95,8 @@ hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
 // anchor_bits 0 for a BF16 reference.  Launches the merge kernel too when
 // a.records is set.
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
-                         hipStream_t s);
-template <int AQ>
+                         bool chain, hipStream_t s);
+template <int AQ, bool CHAIN>
 hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
 // The split/tail merge for n_slots loop slots, the first n_res of them residual.
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t s);

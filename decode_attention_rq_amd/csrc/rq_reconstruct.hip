@@ -56,6 +56,13 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const ReconArgs a) {
   } else {
     dequant8<D>(a.acodes, a.ameta, slot, j, a.abits, a.agroup, a.rotate, a.rot_c, lane, y);
   }
+  for (int k = 0; k < a.npre; ++k) {   // chained references: the links from the root
+    float u[8];
+    dequant8<D>(a.pcodes[k], a.pmeta[k], slot, j, a.pbits[k], a.group, a.rotate, a.rot_c, lane, u);
+    const float ak = f16_to_f32(a.palpha[k][slot]);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) y[p] = __builtin_fmaf(ak, y[p], u[p]);
+  }
   if (a.codes == nullptr) {            // the anchor loop itself
     if (valid) {
       float4 *o = reinterpret_cast<float4 *>(a.out + ((size_t)bh * a.n + tl) * D + 8 * j);

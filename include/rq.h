@@ -94,6 +94,14 @@ typedef struct {
     int32_t alpha_mode;          /* residual scaling (Table 9 columns): 0 least
                                     squares <x,y>/<y,y>; 1 none (alpha = 1);
                                     2 norm ratio ||x|| / ||y||                      */
+    int32_t ref_chain;           /* 1: chained references (Table 9 "Next-loop", or
+                                    "Previous-loop" with ref_first): each residual
+                                    loop's reference is its neighbour towards the
+                                    group's reference loop, as reconstructed
+                                    (y <- fma(alpha, y, r_hat) in FP32, r_hat =
+                                    c*H_d fma(code, s, z)); decode rebuilds the
+                                    chain.  Needs <= 3 residual loops per group and
+                                    ref_bits 0 or 4                                 */
 } rq_layout;
 
 /* One side (K or V) of one layer's cache: caller-owned device planes.

@@ -46,6 +46,7 @@ class Workload:
     group_loops: int = 0            # loops per anchor group (0: one group)
     ref_first: int = 0              # 1: first loop of each group is the reference
     alpha_mode: int = 0             # 0 least squares, 1 alpha = 1, 2 norm ratio
+    ref_chain: int = 0              # 1: each loop refers to its neighbour towards the reference
     extra: dict = field(default_factory=dict)
 
 

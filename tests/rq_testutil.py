@@ -21,7 +21,8 @@ def tol_rel_row(got: np.ndarray, want: np.ndarray) -> np.ndarray:
 def oracle_layout(w: synth.Workload, batch: int, cap: int) -> dict:
     return dict(n_loops=w.n_loops, batch=batch, heads=w.heads, d=w.d, g=w.g, cap=cap,
                 rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits, ref_group=w.ref_group,
-                group_loops=w.group_loops, ref_first=w.ref_first, alpha_mode=w.alpha_mode)
+                group_loops=w.group_loops, ref_first=w.ref_first, alpha_mode=w.alpha_mode,
+                ref_chain=w.ref_chain)
 
 
 def gpu_layout(w: synth.Workload, batch: int, cap: int):
@@ -29,7 +30,7 @@ def gpu_layout(w: synth.Workload, batch: int, cap: int):
     return rq.Layout(n_loops=w.n_loops, batch=batch, n_heads=w.heads, head_dim=w.d, group=w.g,
                      capacity=cap, rotate=w.rotate, bits=list(w.bits), ref_bits=w.ref_bits,
                      ref_group=w.ref_group, group_loops=w.group_loops, ref_first=w.ref_first,
-                     alpha_mode=w.alpha_mode)
+                     alpha_mode=w.alpha_mode, ref_chain=w.ref_chain)
 
 
 def encoder_input(w: synth.Workload, loops: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:

@@ -316,3 +316,24 @@ def test_first_loop_policy_planes(rq):
     k.alpha[3] = 0
     assert _decode(rq, lay, k=k, v=v) == INVALID
     assert _decode(rq, lay, k=k, v=v, mask=0b0111, ws_bytes=1) == WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ref_chain=2), INVALID),
+    (dict(ref_chain=1, n_loops=5, bits=[2, 2, 2, 2]), UNSUPPORTED),       # 4 residual loops in a chain
+    (dict(ref_chain=1, ref_bits=2, ref_group=32), UNSUPPORTED),           # INT2 anchors not chained
+])
+def test_chain_validation(rq, kw, code):
+    lay = _layout(rq, **kw)
+    k = _anchor_cache(rq, lay.n_loops) if lay.ref_bits else _cache(rq, lay.n_loops)
+    v = _anchor_cache(rq, lay.n_loops) if lay.ref_bits else _cache(rq, lay.n_loops)
+    assert _encode(rq, lay, k=k, v=v) == code
+    assert _decode(rq, lay, k=k, v=v, mask=1) == code
+
+
+def test_chain_decode_checks_every_link(rq):
+    """Next-loop chain: decoding loop 0 reads loops 1 and 2 too."""
+    lay = _layout(rq, ref_chain=1)
+    k = _cache(rq, bad=("alpha", 1, 0))
+    assert _decode(rq, lay, k=k, mask=0b0001) == INVALID
+    assert _decode(rq, lay, k=k, mask=0b0100, ws_bytes=1) == WORKSPACE   # loop 2 needs only itself

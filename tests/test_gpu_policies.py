@@ -83,3 +83,75 @@ def test_policy_parity(oracle, name):
                 assert tol_rel_row(got[l], want[l]).max() <= 2e-3, (mask, l)
             else:
                 assert np.isnan(got[l]).all()
+
+
+# --------------------------------------------------------------------------
+# chained references (Table 9 "Next-loop", "Previous-loop")
+# --------------------------------------------------------------------------
+
+def _wc(ref_first=0, ref_bits=0, group_loops=0, L=4, seed=81):
+    w = _w(ref_first=ref_first, ref_bits=ref_bits, group_loops=group_loops, L=L, g=16, seed=seed)
+    w.ref_chain = 1
+    return w
+
+
+CHAIN_CASES = {
+    "next-loop-bf16": _wc(),
+    "next-loop-anchor": _wc(ref_bits=4),
+    "previous-loop-anchor": _wc(ref_first=1, ref_bits=4),
+    "previous-loop-bf16": _wc(ref_first=1),
+    "next-loop-groups": _wc(ref_bits=4, group_loops=4, L=8),
+}
+
+
+@pytest.mark.parametrize("name", list(CHAIN_CASES))
+def test_chain_parity(oracle, name):
+    import decode_attention_rq_amd as rq
+    w = CHAIN_CASES[name]
+    n = 301
+    case = Case(w, n, cap=310, t_chunks=[(0, 150), (150, 151)])
+    lay, kp, vp, qb = case.oracle_planes(oracle)
+    for side, planes in (("k", kp), ("v", vp)):
+        gc = getattr(case, side)
+        for l in range(w.n_loops):
+            for nm in ("codes", "meta", "alpha"):
+                want = getattr(planes, nm)[l]
+                if want is not None:
+                    assert np.array_equal(plane_bits(getattr(gc, nm)[l])[:, :, :n], want[:, :, :n]), (side, l, nm)
+    for l in range(w.n_loops):
+        if case.lay.is_anchor(l) and not w.ref_bits:
+            continue
+        out = torch.empty(case.B, w.heads, 40, w.d, dtype=torch.float32, device="cuda")
+        rq.rq_reconstruct(case.lay, case.k, l, 5, 40, out)
+        torch.cuda.synchronize()
+        want = oracle.reconstruct(lay, kp, l, 5, 40)
+        g0, root, order = oracle.chain_order(lay, l)
+        links = [m for m in [root] + order if m != root or w.ref_bits]
+        s = np.max([plane_bits(case.k.meta[m])[:, :, 5:45, :, 0].view(np.float16).astype(np.float64).max(-1)
+                    for m in links], axis=0)
+        err = np.abs(out.cpu().double().numpy() - want).max(-1)
+        assert np.all(err <= 1e-3 * s), l
+    scale = 1.0 / np.sqrt(w.d)
+    tl = synth.draw_tail(w, 4, batch=case.B, n=3, device="cuda")
+    tail = rq.Tail([tl["k"][l].contiguous() for l in range(w.n_loops)],
+                   [tl["v"][l].contiguous() for l in range(w.n_loops)], 3)
+    tkb = np.stack([synth.bf16_bits(tl["k"][l]) for l in range(w.n_loops)])
+    tvb = np.stack([synth.bf16_bits(tl["v"][l]) for l in range(w.n_loops)])
+    masks = [((1 << w.n_loops) - 1, 0, None), ((1 << w.n_loops) - 1, 2, "tail")]
+    masks += [(1 << l, s, None) for l, s in zip(range(w.n_loops), [0, 1, 3, 0, 2, 1, 0, 1])]
+    for mask, splits, tailed in masks:
+        out = torch.full((w.n_loops, case.B, w.heads, w.d), float("nan"), device="cuda")
+        ws = rq.workspace_for(case.lay, n, splits)
+        if tailed:
+            rq.rq_decode_attn_tail(case.lay, case.k, case.v, tail, case.q, mask, n, scale, out, ws, splits)
+            want = oracle.decode(lay, kp, vp, qb, mask, n, scale, tkb, tvb)
+        else:
+            rq.rq_decode_attn(case.lay, case.k, case.v, case.q, mask, n, scale, out, ws, splits)
+            want = oracle.decode(lay, kp, vp, qb, mask, n, scale)
+        torch.cuda.synchronize()
+        got = out.cpu().double().numpy()
+        for l in range(w.n_loops):
+            if (mask >> l) & 1:
+                assert tol_rel_row(got[l], want[l]).max() <= 2e-3, (mask, l)
+            else:
+                assert np.isnan(got[l]).all(), (mask, l)
