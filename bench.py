@@ -498,7 +498,8 @@ def anchor_bench(args, w):
 
     dev, n, T, L = "cuda", w.n_ctx, w.extra["tail"], w.n_loops
     B, H, d = w.batch, w.heads, w.d
-    lay = rq.Layout(L, B, H, d, w.g, n, w.rotate, w.bits, ref_bits=w.ref_bits, ref_group=w.ref_group)
+    lay = rq.Layout(L, B, H, d, w.g, n, w.rotate, w.bits, ref_bits=w.ref_bits, ref_group=w.ref_group,
+                    ref_chain=w.ref_chain)
     scale = 1.0 / np.sqrt(d)
     reps = []
     for r in range(args.replicas):
@@ -538,19 +539,23 @@ def anchor_bench(args, w):
     span_ms = ev[0][0].elapsed_time(ev[-1][L])
     ms = span_ms / steps
     tail_bytes = B * H * T * 2 * d * 2
-    res_call = B * H * n * loop_read_bytes_per_token(w.bits[0], w.g, d, w.ref_bits, w.ref_group) \
-        + tail_bytes + B * H * d * 2 + B * H * d * 4
-    anchor_call = B * H * n * 2 * (d * w.ref_bits // 8 + 4 * (d // w.ref_group)) + tail_bytes \
-        + B * H * d * 2 + B * H * d * 4
-    step_bytes = (L - 1) * res_call + anchor_call
+    anchor_tok = 2 * (d * w.ref_bits // 8 + 4 * (d // w.ref_group))
+    res_tok = 2 * (d * w.bits[0] // 8 + 4 * (d // w.g) + 2)
+    # residual planes one loop's call reads: its own; with chained references
+    # also every link between it and the anchor (loop L-1 - l of them)
+    links = [(L - 1 - l) if w.ref_chain else 1 for l in range(L - 1)] + [0]
+    call_bytes = [B * H * n * (anchor_tok + links[l] * res_tok) + tail_bytes + B * H * d * 6 for l in range(L)]
+    step_bytes = sum(call_bytes)
+    res_call = sum(call_bytes[:L - 1]) / (L - 1)
     res_us = float(call_ms[:, :L - 1].mean()) * 1e3
     roof = {"bound": "hbm", "achieved": round(res_call / (res_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(res_call / (res_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "one residual loop's call: decode_kernel (1 residual loop, INT4 anchor) + merge with "
-                      "the BF16 tail",
+            "kernel": "a residual loop's call (mean over the three): decode_kernel against the INT4 anchor"
+                      + (" along the reference chain" if w.ref_chain else "") + " + merge with the BF16 tail",
             "algorithmic_bytes_per_launch": res_call, "launch_us_mean": round(res_us, 2),
             "anchor_loop_call_us_mean": round(float(call_ms[:, L - 1].mean()) * 1e3, 2)}
-    res = {"metric": "per-loop decode tokens/s, [2,2,2,4] INT4 anchor + INT2 residuals g=16, 8k ctx + 64 BF16 tail",
+    res = {"metric": "per-loop decode tokens/s, [2,2,2,4] INT4 anchor + INT2 residuals g=16, 8k ctx + 64 BF16 tail"
+                     + (", Next-loop chained references" if w.ref_chain else ""),
            "value": round(B / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -735,7 +740,7 @@ def main():
     if args.workload == "peak-batch-8k":
         print(json.dumps(peak_batch_bench(args, w)), flush=True)
         return
-    if args.workload == "anchor-8k-perloop":
+    if args.workload in ("anchor-8k-perloop", "chain-8k-perloop"):
         print(json.dumps(anchor_bench(args, w)), flush=True)
         return
     if args.workload.startswith("grid-"):

@@ -75,6 +75,12 @@ WORKLOADS = {
                                   n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
                                   sigma=[0.15, 0.12, 0.1], rotate=1, seed=5, ref_bits=4,
                                   ref_group=32, extra={"tail": 64}),
+    # The same with chained references (Next-loop policy, Table 9): decoding
+    # loop l rebuilds the chain from the anchor through loops L-2 .. l.
+    "chain-8k-perloop": Workload("chain-8k-perloop", n_loops=4, batch=16, heads=16, d=128, g=16,
+                                 n_ctx=8192, bits=[2, 2, 2], c=[0.8, 0.85, 0.9],
+                                 sigma=[0.15, 0.12, 0.1], rotate=1, seed=8, ref_bits=4,
+                                 ref_group=32, ref_chain=1, extra={"tail": 64}),
     # The pages' throughput grid (Fig. 4: g=32 everywhere; Fig. 6: INT2
     # residuals at g=16): 24 layers, contexts 2k-16k, power-of-two batches up
     # to a 250 GB KV budget, per-loop decode, against BF16 per-loop decode.
