@@ -172,6 +172,170 @@ __device__ __forceinline__ void quantize_store(float (&u)[EPL], int bits, int gr
   else *reinterpret_cast<uint2 *>(meta + oslot * G + 2 * j) = make_uint2(sz[0], sz[1]);
 }
 
+// ---- BF16 reference without chains: the common case, in a leaner kernel ----
+
+// One group's FP16 scale and offset from the lane's N values, and the factor
+// the codes use: 1/s (0 when the stored scale is 0, which makes every code 0).
+template <int N>
+__device__ __forceinline__ void group_params(const float *u, float levels, uint32_t &sz, float &z, float &inv) {
+  float mn = u[0], mx = u[0];
+#pragma unroll
+  for (int p = 1; p < N; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
+  const uint32_t s16 = f32_to_f16_sat((mx - mn) / levels);
+  const uint32_t z16 = f32_to_f16_sat(mn);
+  const float s = f16_to_f32(s16);
+  z = f16_to_f32(z16);
+  inv = s != 0.0f ? 1.0f / s : 0.0f;
+  sz = s16 | (z16 << 16);
+}
+
+// Raw buffer access: a wave-uniform base address and byte count in SGPRs, a
+// 32-bit byte offset per lane.  Accesses at or beyond the byte count are
+// dropped by the hardware (loads return 0).  Word 3 selects the untyped
+// 32-bit data format that plain buffer_load/store_dword* use.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// quantize_store without keeping the codes: each code (a small integer in
+// FP32) is added into a 16-bit field of its packed word, held as an exact
+// FP32 integer (sum of code * 2^(bits * i) < 2^16), so packing costs one FMA
+// per code plus two conversions and a shift-or per 32-bit word.  Same codes,
+// same layout.  cr / mr address the code and meta planes from the wave's
+// first token; tok is the lane's token relative to it.
+template <int D, int BITS>
+__device__ __forceinline__ void quantize_pack(const float (&u)[EPL], int group, __amdgpu_buffer_rsrc_t cr,
+                                              __amdgpu_buffer_rsrc_t mr, uint32_t tok, int j, bool valid) {
+  constexpr float levels = (float)((1 << BITS) - 1);
+  constexpr int PER_HALF = 16 / BITS;                 // codes per 16-bit field
+  constexpr int NH = EPL / PER_HALF;                  // 16-bit fields per lane
+  uint32_t sz[2];
+  float z[2], inv[2];
+  if (group == 32) {
+    group_params<32>(u, levels, sz[0], z[0], inv[0]);
+    sz[1] = sz[0]; z[1] = z[0]; inv[1] = inv[0];
+  } else {
+    group_params<16>(u, levels, sz[0], z[0], inv[0]);
+    group_params<16>(u + 16, levels, sz[1], z[1], inv[1]);
+  }
+  float h[NH];
+#pragma unroll
+  for (int f = 0; f < NH; ++f) h[f] = 0.0f;
+#pragma unroll
+  for (int p = 0; p < EPL; ++p) {
+    const int g = p / 16;
+    const float c = __builtin_amdgcn_fmed3f(__builtin_rintf((u[p] - z[g]) * inv[g]), 0.0f, levels);
+    h[p / PER_HALF] = __builtin_fmaf(c, (float)(1 << (BITS * (p % PER_HALF))), h[p / PER_HALF]);
+  }
+  if (!valid) return;
+  uint32_t w[NH / 2];
+#pragma unroll
+  for (int k = 0; k < NH / 2; ++k) w[k] = (uint32_t)h[2 * k] | ((uint32_t)h[2 * k + 1] << 16);
+  if constexpr (BITS == 2) {
+    const u32x2_t v = {w[0], w[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(v, cr, tok * (D / 4) + 8 * j, 0, 0);
+  } else {
+    const u32x4_t v = {w[0], w[1], w[2], w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, cr, tok * (D / 2) + 16 * j, 0, 0);
+  }
+  const uint32_t G = D / group;
+  if (group == 32) {
+    __builtin_amdgcn_raw_buffer_store_b32(sz[0], mr, 4 * (tok * G + j), 0, 0);
+  } else {
+    const u32x2_t v = {sz[0], sz[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(v, mr, 4 * (tok * G + 2 * j), 0, 0);
+  }
+}
+
+__device__ __forceinline__ void load_raw32(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t (&w)[EPL / 8]) {
+#pragma unroll
+  for (int k = 0; k < EPL / 8; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 16 * k, 0);
+}
+
+__device__ __forceinline__ void unpack_raw32(const u32x4_t (&w)[EPL / 8], float (&f)[EPL]) {
+#pragma unroll
+  for (int k = 0; k < EPL / 8; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[8 * k + 2 * e] = bf16lo(w[k][e]);
+      f[8 * k + 2 * e + 1] = bf16hi(w[k][e]);
+    }
+  }
+}
+
+// The encoder for a BF16 reference and references that are not chained (the
+// arithmetic of encode_kernel on that path, step for step, bit-identical
+// output).  Everything that depends only on the wave (its side, batch*head
+// and token chunk) is wave-uniform, so every plane is a buffer at the wave's
+// first token addressed by 32-bit lane offsets (no 64-bit address registers);
+// the codes are packed as they are made, and the next loop's input is loaded
+// while the current loop is quantized.  140 VGPRs: three waves per SIMD.
+// (Forcing four waves spills y and runs slower.)
+template <int D>
+__global__ __launch_bounds__(256) void encode_plain_kernel(const EncodeArgs a) {
+  constexpr int LANES = D / EPL;
+  constexpr int VPW = kWave / LANES;
+  const int lane = threadIdx.x & 63;
+  const int task = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= 2 * a.tasks_per_side || a.n_res == 0) return;   // whole wave
+  const int side = task >= a.tasks_per_side ? 1 : 0;
+  const int tk = task - side * a.tasks_per_side;
+  const int bh = tk / a.chunks;
+  const int chunk = tk - bh * a.chunks;
+  const int j = lane % LANES;
+  const int t_first = chunk * VPW;                   // the wave's first token in [0, n)
+  const int nw = min(VPW, a.n - t_first);            // the wave's valid tokens
+  const uint32_t tok = (uint32_t)(lane / LANES);     // relative to t_first
+  const bool valid = (int)tok < nw;
+  const uint32_t tokc = valid ? tok : (uint32_t)(nw - 1);   // in-bounds stand-in for loads
+  const EncodeSide &S = a.side[side];
+  const size_t row0 = (size_t)bh * a.cap + (size_t)(a.t0 + t_first);   // output slot of t_first
+  const size_t xrow0 = (size_t)bh * a.n + (size_t)t_first;            // input row of t_first
+  const uint32_t xoff = 2 * (tokc * D + EPL * j);
+  const uint32_t rows = (uint32_t)nw * (2 * D);
+
+  u32x4_t raw[EPL / 8];
+  load_raw32(plane(S.xin[0] + xrow0 * D, rows), xoff, raw);
+  float y[EPL];
+  {
+    u32x4_t yr[EPL / 8];
+    load_raw32(plane(S.ref + row0 * D, rows), xoff, yr);
+    unpack_raw32(yr, y);
+  }
+  const float den = dot_sum32<LANES>(y, y);
+
+  for (int l = 0; l < a.n_res; ++l) {
+    float x[EPL];
+    unpack_raw32(raw, x);
+    if (l + 1 < a.n_res) load_raw32(plane(S.xin[l + 1] + xrow0 * D, rows), xoff, raw);
+    float alpha32;
+    if (a.alpha_mode == 1) {
+      alpha32 = 1.0f;
+    } else if (a.alpha_mode == 2) {
+      const float nx = dot_sum32<LANES>(x, x);
+      alpha32 = den > 0.0f ? __builtin_sqrtf(nx) / __builtin_sqrtf(den) : 0.0f;
+    } else {
+      const float num = dot_sum32<LANES>(x, y);
+      alpha32 = den > 0.0f ? num / den : 0.0f;
+    }
+    const uint32_t a16 = f32_to_f16_sat(alpha32);
+    const float af = f16_to_f32(a16);
+#pragma unroll
+    for (int p = 0; p < EPL; ++p) x[p] = __builtin_fmaf(-af, y[p], x[p]);
+    rotate_canonical<LANES>(x, a.rotate, a.rot_c, lane);
+    const int G = D / a.group;
+    const __amdgpu_buffer_rsrc_t mr = plane(S.meta[l] + row0 * G, (uint32_t)nw * 4 * G);
+    if (a.bits[l] == 2)
+      quantize_pack<D, 2>(x, a.group, plane(S.codes[l] + row0 * (D / 4), (uint32_t)nw * (D / 4)), mr, tok, j, valid);
+    else
+      quantize_pack<D, 4>(x, a.group, plane(S.codes[l] + row0 * (D / 2), (uint32_t)nw * (D / 2)), mr, tok, j, valid);
+    if (valid && j == 0)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, plane(S.alpha[l] + row0, (uint32_t)nw * 2), 2 * tok, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   constexpr int LANES = D / EPL;
@@ -261,10 +425,20 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s) {
   const int tasks = 2 * a.tasks_per_side;
   const dim3 grid((tasks + 3) / 4), block(256);
+  const bool plain = a.abits == 0 && !a.chain;
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL(encode_kernel<256>, grid, block, 0, s, a); break;
+    case 64:
+      if (plain) hipLaunchKernelGGL(encode_plain_kernel<64>, grid, block, 0, s, a);
+      else hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, s, a);
+      break;
+    case 128:
+      if (plain) hipLaunchKernelGGL(encode_plain_kernel<128>, grid, block, 0, s, a);
+      else hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, s, a);
+      break;
+    case 256:
+      if (plain) hipLaunchKernelGGL(encode_plain_kernel<256>, grid, block, 0, s, a);
+      else hipLaunchKernelGGL(encode_kernel<256>, grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
