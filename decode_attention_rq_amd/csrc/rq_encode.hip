@@ -29,18 +29,6 @@ namespace rq {
 // the lane.
 constexpr int EPL = kEncodeElemsPerLane;
 
-__device__ __forceinline__ void load_bf16x32(const uint16_t *p, float (&f)[EPL]) {
-  const uint4 *q = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-  for (int k = 0; k < EPL / 8; ++k) {
-    const uint4 w = q[k];
-    f[8 * k + 0] = bf16lo(w.x); f[8 * k + 1] = bf16hi(w.x);
-    f[8 * k + 2] = bf16lo(w.y); f[8 * k + 3] = bf16hi(w.y);
-    f[8 * k + 4] = bf16lo(w.z); f[8 * k + 5] = bf16hi(w.z);
-    f[8 * k + 6] = bf16lo(w.w); f[8 * k + 7] = bf16hi(w.w);
-  }
-}
-
 // sum_i a[i] * b[i] over the whole vector in the contract order: each block
 // of 8 consecutive products by pairwise halving (distances 4, 2, 1), then the
 // D/8 block sums by pairwise halving from the largest distance.  The lane
@@ -93,27 +81,29 @@ __device__ __forceinline__ void fwht32(float (&v)[EPL], int lane) {
   }
 }
 
-// Quantize one group of N values of the lane (rotated if the layout rotates,
-// and -0 already canonicalised to +0): min/max, FP16 scale and offset, codes
-// by round-half-even of (u - z) * (1/s) clamped to the grid (all 0 if the
-// stored scale is 0).  q receives the codes as floats.
-template <int N>
-__device__ __forceinline__ void quantize_group(float *u, int bits, uint32_t &s16, uint32_t &z16, float *q) {
-  float mn = u[0], mx = u[0];
+// Raw buffer access: a wave-uniform base address and byte count in SGPRs, a
+// 32-bit byte offset per lane (no 64-bit address registers).  Accesses at or
+// beyond the byte count are dropped by the hardware (loads return 0).  Word 3
+// selects the untyped 32-bit data format of plain buffer_load/store_dword*.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void load_raw32(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t (&w)[EPL / 8]) {
 #pragma unroll
-  for (int p = 1; p < N; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
-  const float levels = (float)((1 << bits) - 1);
-  s16 = f32_to_f16_sat((mx - mn) / levels);
-  z16 = f32_to_f16_sat(mn);
-  const float s = f16_to_f32(s16);
-  const float z = f16_to_f32(z16);
-  if (s != 0.0f) {
-    const float inv = 1.0f / s;
+  for (int k = 0; k < EPL / 8; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 16 * k, 0);
+}
+
+__device__ __forceinline__ void unpack_raw32(const u32x4_t (&w)[EPL / 8], float (&f)[EPL]) {
 #pragma unroll
-    for (int p = 0; p < N; ++p) q[p] = __builtin_amdgcn_fmed3f(__builtin_rintf((u[p] - z) * inv), 0.0f, levels);
-  } else {
+  for (int k = 0; k < EPL / 8; ++k) {
 #pragma unroll
-    for (int p = 0; p < N; ++p) q[p] = 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      f[8 * k + 2 * e] = bf16lo(w[k][e]);
+      f[8 * k + 2 * e + 1] = bf16hi(w[k][e]);
+    }
   }
 }
 
@@ -132,93 +122,51 @@ __device__ __forceinline__ void rotate_canonical(float (&v)[EPL], int rotate, fl
   }
 }
 
-// Quantize the lane's 32 values in groups of `group` (16 or 32), store the
-// packed codes (code p of the lane at bits [bits*p, +bits) of its
-// 32*bits/8-byte slice, LSB first) and the (scale | zero << 16) words of its
-// groups.  q receives the codes.
-template <int D>
-__device__ __forceinline__ void quantize_store(float (&u)[EPL], int bits, int group, float (&q)[EPL],
-                                               uint32_t (&sz)[2], uint8_t *codes, uint32_t *meta,
-                                               size_t oslot, int j, bool valid) {
-  uint32_t s16[2], z16[2];
-  int ng;
-  if (group == 32) {
-    quantize_group<32>(u, bits, s16[0], z16[0], q);
-    ng = 1;
-  } else {
-    quantize_group<16>(u, bits, s16[0], z16[0], q);
-    quantize_group<16>(u + 16, bits, s16[1], z16[1], q + 16);
-    ng = 2;
-  }
-  sz[0] = s16[0] | (z16[0] << 16);
-  sz[1] = ng == 2 ? (s16[1] | (z16[1] << 16)) : sz[0];
-  if (!valid) return;
-  if (bits == 2) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      w0 |= (uint32_t)q[p] << (2 * p);
-      w1 |= (uint32_t)q[16 + p] << (2 * p);
-    }
-    *reinterpret_cast<uint2 *>(codes + oslot * (D / 4) + 8 * j) = make_uint2(w0, w1);
-  } else {
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int p = 0; p < EPL; ++p) w[p / 8] |= (uint32_t)q[p] << (4 * (p % 8));
-    *reinterpret_cast<uint4 *>(codes + oslot * (D / 2) + 16 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  const int G = D / group;
-  if (ng == 1) meta[oslot * G + j] = sz[0];
-  else *reinterpret_cast<uint2 *>(meta + oslot * G + 2 * j) = make_uint2(sz[0], sz[1]);
-}
-
-// ---- BF16 reference without chains: the common case, in a leaner kernel ----
-
-// One group's FP16 scale and offset from the lane's N values, and the factor
-// the codes use: 1/s (0 when the stored scale is 0, which makes every code 0).
+// One group of N values of the lane (rotated if the layout rotates, -0
+// already canonicalised to +0): min/max, then the FP16 scale s = (max-min)/
+// (2^b - 1) and offset z = min as stored, and the factor the codes use, 1/s
+// (0 when the stored scale is 0, which makes every code 0).
 template <int N>
-__device__ __forceinline__ void group_params(const float *u, float levels, uint32_t &sz, float &z, float &inv) {
+__device__ __forceinline__ void group_params(const float *u, float levels, uint32_t &sz, float &s, float &z,
+                                             float &inv) {
   float mn = u[0], mx = u[0];
 #pragma unroll
   for (int p = 1; p < N; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
   const uint32_t s16 = f32_to_f16_sat((mx - mn) / levels);
   const uint32_t z16 = f32_to_f16_sat(mn);
-  const float s = f16_to_f32(s16);
+  s = f16_to_f32(s16);
   z = f16_to_f32(z16);
   inv = s != 0.0f ? 1.0f / s : 0.0f;
   sz = s16 | (z16 << 16);
 }
 
-// Raw buffer access: a wave-uniform base address and byte count in SGPRs, a
-// 32-bit byte offset per lane.  Accesses at or beyond the byte count are
-// dropped by the hardware (loads return 0).  Word 3 selects the untyped
-// 32-bit data format that plain buffer_load/store_dword* use.
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// quantize_store without keeping the codes: each code (a small integer in
-// FP32) is added into a 16-bit field of its packed word, held as an exact
-// FP32 integer (sum of code * 2^(bits * i) < 2^16), so packing costs one FMA
-// per code plus two conversions and a shift-or per 32-bit word.  Same codes,
-// same layout.  cr / mr address the code and meta planes from the wave's
-// first token; tok is the lane's token relative to it.
-template <int D, int BITS>
-__device__ __forceinline__ void quantize_pack(const float (&u)[EPL], int group, __amdgpu_buffer_rsrc_t cr,
+// Quantize the lane's 32 values in groups of `group` (16 or 32): code =
+// round-half-even of (u - z) * (1/s), clamped to [0, 2^b - 1].  Stores the
+// packed codes (code p of the lane at bits [b*p, +b) of its 32*b/8-byte
+// slice, LSB first) and the (scale | zero << 16) words of its groups.  With
+// DEQ, u becomes the dequantized values fma(code, s, z) (for a reference
+// that a later step rebuilds).
+//
+// Codes are not kept: each code (a small integer in FP32) is added into a
+// 16-bit field of its packed word, held as an exact FP32 integer (sum of
+// code * 2^(b*i) < 2^16), so packing costs one FMA per code plus two
+// conversions and a shift-or per 32-bit word.  cr / mr address the code and
+// meta planes from the wave's first token; tok is the lane's token relative
+// to it.
+template <int D, int BITS, bool DEQ>
+__device__ __forceinline__ void quantize_pack(float (&u)[EPL], int group, __amdgpu_buffer_rsrc_t cr,
                                               __amdgpu_buffer_rsrc_t mr, uint32_t tok, int j, bool valid) {
   constexpr float levels = (float)((1 << BITS) - 1);
   constexpr int PER_HALF = 16 / BITS;                 // codes per 16-bit field
   constexpr int NH = EPL / PER_HALF;                  // 16-bit fields per lane
   uint32_t sz[2];
-  float z[2], inv[2];
+  float sc[2], z[2], inv[2];
   if (group == 32) {
-    group_params<32>(u, levels, sz[0], z[0], inv[0]);
-    sz[1] = sz[0]; z[1] = z[0]; inv[1] = inv[0];
+    group_params<32>(u, levels, sz[0], sc[0], z[0], inv[0]);
+    sz[1] = sz[0]; sc[1] = sc[0]; z[1] = z[0]; inv[1] = inv[0];
   } else {
-    group_params<16>(u, levels, sz[0], z[0], inv[0]);
-    group_params<16>(u + 16, levels, sz[1], z[1], inv[1]);
+    group_params<16>(u, levels, sz[0], sc[0], z[0], inv[0]);
+    group_params<16>(u + 16, levels, sz[1], sc[1], z[1], inv[1]);
   }
   float h[NH];
 #pragma unroll
@@ -228,6 +176,7 @@ __device__ __forceinline__ void quantize_pack(const float (&u)[EPL], int group, 
     const int g = p / 16;
     const float c = __builtin_amdgcn_fmed3f(__builtin_rintf((u[p] - z[g]) * inv[g]), 0.0f, levels);
     h[p / PER_HALF] = __builtin_fmaf(c, (float)(1 << (BITS * (p % PER_HALF))), h[p / PER_HALF]);
+    if constexpr (DEQ) u[p] = __builtin_fmaf(c, sc[g], z[g]);
   }
   if (!valid) return;
   uint32_t w[NH / 2];
@@ -249,37 +198,37 @@ __device__ __forceinline__ void quantize_pack(const float (&u)[EPL], int group, 
   }
 }
 
-__device__ __forceinline__ void load_raw32(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t (&w)[EPL / 8]) {
-#pragma unroll
-  for (int k = 0; k < EPL / 8; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 16 * k, 0);
+// quantize_pack for a bit width known at run time, onto the planes of one
+// loop (codes / meta at the wave's first output slot row0, nw valid tokens).
+template <int D, bool DEQ>
+__device__ __forceinline__ void quantize_loop(float (&u)[EPL], int bits, int group, uint8_t *codes, uint32_t *meta,
+                                              size_t row0, int nw, uint32_t tok, int j, bool valid) {
+  const int G = D / group;
+  const __amdgpu_buffer_rsrc_t mr = plane(meta + row0 * G, (uint32_t)nw * 4 * G);
+  if (bits == 2)
+    quantize_pack<D, 2, DEQ>(u, group, plane(codes + row0 * (D / 4), (uint32_t)nw * (D / 4)), mr, tok, j, valid);
+  else
+    quantize_pack<D, 4, DEQ>(u, group, plane(codes + row0 * (D / 2), (uint32_t)nw * (D / 2)), mr, tok, j, valid);
 }
 
-__device__ __forceinline__ void unpack_raw32(const u32x4_t (&w)[EPL / 8], float (&f)[EPL]) {
-#pragma unroll
-  for (int k = 0; k < EPL / 8; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[8 * k + 2 * e] = bf16lo(w[k][e]);
-      f[8 * k + 2 * e + 1] = bf16hi(w[k][e]);
-    }
-  }
-}
-
-// The encoder for a BF16 reference and references that are not chained (the
-// arithmetic of encode_kernel on that path, step for step, bit-identical
-// output).  Everything that depends only on the wave (its side, batch*head
-// and token chunk) is wave-uniform, so every plane is a buffer at the wave's
-// first token addressed by 32-bit lane offsets (no 64-bit address registers);
-// the codes are packed as they are made, and the next loop's input is loaded
-// while the current loop is quantized.  140 VGPRs: three waves per SIMD.
-// (Forcing four waves spills y and runs slower.)
+// One wave encodes VPW tokens of one (side, batch*head): the reference (the
+// BF16 final loop, or a quantized anchor: quantized like a residual without
+// the LS coefficient, then dequantized and rotated back as the residuals'
+// reference), then each residual loop in turn.  With chains each loop's
+// reconstruction becomes the next loop's reference.
+//
+// Everything that depends only on the wave is wave-uniform, so every plane
+// is a buffer at the wave's first token addressed by 32-bit lane offsets;
+// the next loop's input is loaded while the current loop is quantized.
+// About 140 VGPRs: three waves per SIMD (forcing four spills y and runs
+// slower).
 template <int D>
-__global__ __launch_bounds__(256) void encode_plain_kernel(const EncodeArgs a) {
+__global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   constexpr int LANES = D / EPL;
   constexpr int VPW = kWave / LANES;
   const int lane = threadIdx.x & 63;
   const int task = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (task >= 2 * a.tasks_per_side || a.n_res == 0) return;   // whole wave
+  if (task >= 2 * a.tasks_per_side) return;          // whole wave
   const int side = task >= a.tasks_per_side ? 1 : 0;
   const int tk = task - side * a.tasks_per_side;
   const int bh = tk / a.chunks;
@@ -295,83 +244,19 @@ __global__ __launch_bounds__(256) void encode_plain_kernel(const EncodeArgs a) {
   const size_t xrow0 = (size_t)bh * a.n + (size_t)t_first;            // input row of t_first
   const uint32_t xoff = 2 * (tokc * D + EPL * j);
   const uint32_t rows = (uint32_t)nw * (2 * D);
+  auto input = [&](int i) { return plane(S.xin[i] + xrow0 * D, rows); };
 
   u32x4_t raw[EPL / 8];
-  load_raw32(plane(S.xin[0] + xrow0 * D, rows), xoff, raw);
   float y[EPL];
   {
     u32x4_t yr[EPL / 8];
-    load_raw32(plane(S.ref + row0 * D, rows), xoff, yr);
+    load_raw32(a.abits == 0 ? plane(S.ref + row0 * D, rows) : input(a.n_res), xoff, yr);
+    if (a.n_res > 0) load_raw32(input(0), xoff, raw);
     unpack_raw32(yr, y);
   }
-  const float den = dot_sum32<LANES>(y, y);
-
-  for (int l = 0; l < a.n_res; ++l) {
-    float x[EPL];
-    unpack_raw32(raw, x);
-    if (l + 1 < a.n_res) load_raw32(plane(S.xin[l + 1] + xrow0 * D, rows), xoff, raw);
-    float alpha32;
-    if (a.alpha_mode == 1) {
-      alpha32 = 1.0f;
-    } else if (a.alpha_mode == 2) {
-      const float nx = dot_sum32<LANES>(x, x);
-      alpha32 = den > 0.0f ? __builtin_sqrtf(nx) / __builtin_sqrtf(den) : 0.0f;
-    } else {
-      const float num = dot_sum32<LANES>(x, y);
-      alpha32 = den > 0.0f ? num / den : 0.0f;
-    }
-    const uint32_t a16 = f32_to_f16_sat(alpha32);
-    const float af = f16_to_f32(a16);
-#pragma unroll
-    for (int p = 0; p < EPL; ++p) x[p] = __builtin_fmaf(-af, y[p], x[p]);
-    rotate_canonical<LANES>(x, a.rotate, a.rot_c, lane);
-    const int G = D / a.group;
-    const __amdgpu_buffer_rsrc_t mr = plane(S.meta[l] + row0 * G, (uint32_t)nw * 4 * G);
-    if (a.bits[l] == 2)
-      quantize_pack<D, 2>(x, a.group, plane(S.codes[l] + row0 * (D / 4), (uint32_t)nw * (D / 4)), mr, tok, j, valid);
-    else
-      quantize_pack<D, 4>(x, a.group, plane(S.codes[l] + row0 * (D / 2), (uint32_t)nw * (D / 2)), mr, tok, j, valid);
-    if (valid && j == 0)
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, plane(S.alpha[l] + row0, (uint32_t)nw * 2), 2 * tok, 0, 0);
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
-  constexpr int LANES = D / EPL;
-  constexpr int VPW = kWave / LANES;
-  const int lane = threadIdx.x & 63;
-  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= 2 * a.tasks_per_side) return;          // whole wave
-  const int side = task >= a.tasks_per_side ? 1 : 0;
-  const int tk = task - side * a.tasks_per_side;
-  const int bh = tk / a.chunks;
-  const int chunk = tk - bh * a.chunks;
-  const int j = lane % LANES;
-  const int tl = chunk * VPW + lane / LANES;         // token within [0, n)
-  const bool valid = tl < a.n;
-  const int tlc = valid ? tl : a.n - 1;              // in-bounds stand-in for loads
-  const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tlc);
-  const size_t oslot = (size_t)bh * a.cap + (size_t)(a.t0 + tl);
-  const EncodeSide &S = a.side[side];
-  const size_t xrow = ((size_t)bh * a.n + tlc) * D + EPL * j;
-
-  float y[EPL];
-  if (a.abits == 0) {
-    load_bf16x32(S.ref + slot * D + EPL * j, y);
-  } else {
-    // the anchor: its input (index n_res) quantized like a residual (groups
-    // of agroup, no LS coefficient); y becomes its dequantized value
-    load_bf16x32(S.xin[a.n_res] + xrow, y);
+  if (a.abits != 0) {
     rotate_canonical<LANES>(y, a.rotate, a.rot_c, lane);
-    float q[EPL];
-    uint32_t sz[2];
-    quantize_store<D>(y, a.abits, a.agroup, q, sz, S.codes[a.n_res], S.meta[a.n_res], oslot, j, valid);
-#pragma unroll
-    for (int p = 0; p < EPL; ++p) {
-      const uint32_t w = (a.agroup == 32 || p < 16) ? sz[0] : sz[1];
-      y[p] = __builtin_fmaf(q[p], f16_to_f32(w & 0xffffu), f16_to_f32(w >> 16));
-    }
+    quantize_loop<D, true>(y, a.abits, a.agroup, S.codes[a.n_res], S.meta[a.n_res], row0, nw, tok, j, valid);
     if (a.rotate) {
       fwht32<LANES>(y, lane);
 #pragma unroll
@@ -382,7 +267,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 
   for (int l = 0; l < a.n_res; ++l) {
     float x[EPL];
-    load_bf16x32(S.xin[l] + xrow, x);
+    unpack_raw32(raw, x);
+    if (l + 1 < a.n_res) load_raw32(input(l + 1), xoff, raw);
     float alpha32;
     if (a.alpha_mode == 1) {
       alpha32 = 1.0f;
@@ -398,18 +284,15 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 #pragma unroll
     for (int p = 0; p < EPL; ++p) x[p] = __builtin_fmaf(-af, y[p], x[p]);
     rotate_canonical<LANES>(x, a.rotate, a.rot_c, lane);
-    float q[EPL];
-    uint32_t sz[2];
-    quantize_store<D>(x, a.bits[l], a.group, q, sz, S.codes[l], S.meta[l], oslot, j, valid);
-    if (valid && j == 0) S.alpha[l][oslot] = (uint16_t)a16;
-    if (a.chain && l + 1 < a.n_res) {
-      // chained references: the next loop's reference is this loop's
-      // reconstruction, y <- fma(alpha, y, r_hat), r_hat = c*H(fma(code, s, z))
-#pragma unroll
-      for (int p = 0; p < EPL; ++p) {
-        const uint32_t w = (a.group == 32 || p < 16) ? sz[0] : sz[1];
-        x[p] = __builtin_fmaf(q[p], f16_to_f32(w & 0xffffu), f16_to_f32(w >> 16));
-      }
+    const bool link = a.chain && l + 1 < a.n_res;     // the next loop refers to this one
+    if (link)
+      quantize_loop<D, true>(x, a.bits[l], a.group, S.codes[l], S.meta[l], row0, nw, tok, j, valid);
+    else
+      quantize_loop<D, false>(x, a.bits[l], a.group, S.codes[l], S.meta[l], row0, nw, tok, j, valid);
+    if (valid && j == 0)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, plane(S.alpha[l] + row0, (uint32_t)nw * 2), 2 * tok, 0, 0);
+    if (link) {
+      // chained references: y <- fma(alpha, y, r_hat), r_hat = c * H(fma(code, s, z))
       if (a.rotate) {
         fwht32<LANES>(x, lane);
 #pragma unroll
@@ -425,20 +308,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s) {
   const int tasks = 2 * a.tasks_per_side;
   const dim3 grid((tasks + 3) / 4), block(256);
-  const bool plain = a.abits == 0 && !a.chain;
   switch (head_dim) {
-    case 64:
-      if (plain) hipLaunchKernelGGL(encode_plain_kernel<64>, grid, block, 0, s, a);
-      else hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, s, a);
-      break;
-    case 128:
-      if (plain) hipLaunchKernelGGL(encode_plain_kernel<128>, grid, block, 0, s, a);
-      else hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, s, a);
-      break;
-    case 256:
-      if (plain) hipLaunchKernelGGL(encode_plain_kernel<256>, grid, block, 0, s, a);
-      else hipLaunchKernelGGL(encode_kernel<256>, grid, block, 0, s, a);
-      break;
+    case 64: hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(encode_kernel<256>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
