@@ -160,25 +160,33 @@ __device__ __forceinline__ float fma_half(float a, uint32_t w, float c) {
 // subnormal number c * 2^(b-24), exact.  Code p lands in half (p / 4) of word
 // w[p % 4] at mantissa bit position pos(p) = 2 * (p % 4), for INT2 and INT4
 // alike, so one set of 2^(24 - pos) factors serves every loop:
-//   INT2 (16-bit word x, code p at bits 2p): bytes x0 = c0..c3, x1 = c4..c7 are
-//   spread to the two halves, then masked per code.
+//   INT2 (the lane's 16 code bits, code p at bits 2p, in the aligned 32-bit
+//   word x that holds them, selected by sel): its bytes c0..c3 and c4..c7
+//   are spread to the two halves, then masked per code.
 //   INT4 (32-bit word x, code p at bits 4p): the halves already hold c0..c3
 //   and c4..c7; code q of each half is shifted down by 2q bits, then masked.
 template <bool INT4>
-__device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4]) {
+__device__ __forceinline__ void code_halves(uint32_t x, uint32_t (&w)[4], uint32_t sel) {
   if constexpr (INT4) {
     w[0] = x & 0x000F000Fu;
     w[1] = (x >> 2) & 0x003C003Cu;
     w[2] = (x >> 4) & 0x00F000F0u;
     w[3] = (x >> 6) & 0x03C003C0u;
   } else {
-    const uint32_t X = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [x.b0, 0, x.b1, 0]
+    const uint32_t X = __builtin_amdgcn_perm(0u, x, sel);             // [b_lo, 0, b_hi, 0]
     w[0] = X & 0x00030003u;
     w[1] = X & 0x000C000Cu;
     w[2] = X & 0x00300030u;
     w[3] = X & 0x00C000C0u;
   }
 }
+
+// An INT2 lane reads the aligned 32-bit word holding its 2 code bytes (lanes
+// 2i and 2i+1 share one word): the byte-permute selector that spreads the
+// lane's own bytes, [b0, 0, b1, 0] for an even lane and [b2, 0, b3, 0] for an
+// odd one.  A full-word load keeps the value 32 bits wide through the tile
+// registers, so no mask is needed before the permute.
+__device__ __forceinline__ uint32_t int2_sel(int j) { return (j & 1) ? 0x0c030c02u : 0x0c010c00u; }
 
 // Mantissa bit position of code p in its half (so its half reads c * 2^(pos-24)).
 __host__ __device__ constexpr int code_pos(int p) { return 2 * (p & 3); }
@@ -194,13 +202,6 @@ __device__ __forceinline__ float code_dot_h(const uint32_t (&w)[4], const float 
   return acc;
 }
 
-template <bool INT4>
-__device__ __forceinline__ float code_dot(uint32_t x, const float (&coef)[8], float acc) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
-  return code_dot_h(w, coef, acc);
-}
-
 // acc[p] += wgt * half_p  (the accumulator then carries 2^(pos-24)).
 __device__ __forceinline__ void code_axpy_h(const uint32_t (&w)[4], float wgt, float (&acc)[8]) {
 #pragma unroll
@@ -208,13 +209,6 @@ __device__ __forceinline__ void code_axpy_h(const uint32_t (&w)[4], float wgt, f
     acc[q] = fma_half<0>(wgt, w[q], acc[q]);
     acc[q + 4] = fma_half<1>(wgt, w[q], acc[q + 4]);
   }
-}
-
-template <bool INT4>
-__device__ __forceinline__ void code_axpy(uint32_t x, float wgt, float (&acc)[8]) {
-  uint32_t w[4];
-  code_halves<INT4>(x, w);
-  code_axpy_h(w, wgt, acc);
 }
 
 // The low / high FP16 half of a 32-bit word, for use as an fma operand
@@ -265,6 +259,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   static_assert(W >= NS, "one merging wave per loop slot");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane % LANES, r = lane / LANES;
+  const uint32_t sel2 = int2_sel(j);                // INT2 code bytes in the loaded word
   const int split = blockIdx.x, bh = blockIdx.y;
   const int t_begin = split * a.tps;
   const int t_end = min(t_begin + a.tps, a.n_ctx);
@@ -370,8 +365,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           T.ak[u] = ldg<uint32_t>(kac, t * (D / 2) + 4 * j);
           T.av[u] = ldg<uint32_t>(vac, t * (D / 2) + 4 * j);
         } else {
-          T.ak[u] = ldg<uint16_t>(kac, t * (D / 4) + 2 * j);
-          T.av[u] = ldg<uint16_t>(vac, t * (D / 4) + 2 * j);
+          T.ak[u] = ldg<uint32_t>(kac, t * (D / 4) + 4 * (j >> 1));
+          T.av[u] = ldg<uint32_t>(vac, t * (D / 4) + 4 * (j >> 1));
         }
         T.amk[u] = ldg<uint32_t>(kam, ((t << ashift) + ka_) * 4);
         T.amv[u] = ldg<uint32_t>(vam, ((t << ashift) + ka_) * 4);
@@ -382,8 +377,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           T.kc[u][i] = ldg<uint32_t>(kc[i], t * (D / 2) + 4 * j);
           T.vc[u][i] = ldg<uint32_t>(vc[i], t * (D / 2) + 4 * j);
         } else {
-          T.kc[u][i] = ldg<uint16_t>(kc[i], t * (D / 4) + 2 * j);
-          T.vc[u][i] = ldg<uint16_t>(vc[i], t * (D / 4) + 2 * j);
+          T.kc[u][i] = ldg<uint32_t>(kc[i], t * (D / 4) + 4 * (j >> 1));
+          T.vc[u][i] = ldg<uint32_t>(vc[i], t * (D / 4) + 4 * (j >> 1));
         }
         T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
         T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
@@ -415,7 +410,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       } else {
         // anchor dot per slot: s_a (q' . code) + z_a sum(q'), codes as halves
         uint32_t hk[4];
-        code_halves<AINT4>(T.ak[u], hk);
+        code_halves<AINT4>(T.ak[u], hk, sel2);
         const uint32_t mw = T.amk[u];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -426,8 +421,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       uint32_t hk[NRA][4];
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
-        if ((B4 >> m) & 1) code_halves<true>(T.kc[u][m], hk[m]);
-        else code_halves<false>(T.kc[u][m], hk[m]);
+        if ((B4 >> m) & 1) code_halves<true>(T.kc[u][m], hk[m], sel2);
+        else code_halves<false>(T.kc[u][m], hk[m], sel2);
       }
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -451,12 +446,23 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       }
     }
 
-    // online softmax; rescale only when the max grows by more than the slack
+    // online softmax; rescale only when the max grows by more than the slack.
+    // One test over all slots guards the (rarely taken) rescale code, so
+    // every score sum is complete before the branch and each sum's last lane
+    // move fuses into its add.
+    float mts[NS];
+    bool grow = false;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      float mt = sc[0][s];
+      mts[s] = sc[0][s];
 #pragma unroll
-      for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u][s]);
+      for (int u = 1; u < TR; ++u) mts[s] = fmaxf(mts[s], sc[u][s]);
+      grow |= mts[s] > m[s] + kRescaleSlack;
+    }
+    if (grow) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float mt = mts[s];
       if (mt > m[s] + kRescaleSlack) {
         const float f = fexp2(m[s] - mt);
         m[s] = mt;
@@ -473,6 +479,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         }
       }
     }
+    }
 
     // values
 #pragma unroll
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         y[4] = bf16lo(T.yv[u].z); y[5] = bf16hi(T.yv[u].z);
         y[6] = bf16lo(T.yv[u].w); y[7] = bf16hi(T.yv[u].w);
       } else {
-        code_halves<AINT4>(T.av[u], hv);
+        code_halves<AINT4>(T.av[u], hv, sel2);
       }
       // one exponential per lane (slot own), shared across the quad
       float x = sc[u][0] - m[0];
@@ -502,8 +509,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       uint32_t hvc[NRA][4];
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
-        if ((B4 >> m) & 1) code_halves<true>(T.vc[u][m], hvc[m]);
-        else code_halves<false>(T.vc[u][m], hvc[m]);
+        if ((B4 >> m) & 1) code_halves<true>(T.vc[u][m], hvc[m], sel2);
+        else code_halves<false>(T.vc[u][m], hvc[m], sel2);
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {

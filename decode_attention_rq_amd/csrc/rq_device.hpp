@@ -32,11 +32,13 @@ __device__ __forceinline__ uint32_t f32_to_f16_sat(float x) {
 // lane exchange
 // ---------------------------------------------------------------------------
 
-// DPP lane moves inside a 16-lane row (VALU only, no LDS traffic).
+// DPP lane moves inside a 16-lane row (VALU only, no LDS traffic).  Every
+// control used here is a full permutation or broadcast within each row, so
+// no lane reads an invalid source and the destination needs no old value
+// (no zero-initialising move; a move feeding an add fuses into it).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
