@@ -187,13 +187,15 @@ def test_tail_of_zero_tokens_is_plain_decode():
     assert np.array_equal(a, out.cpu().double().numpy())
 
 
-def test_anchor_perloop_full_size(oracle):
-    """The per-loop workload at full size (batch 16, 16 heads, 8192 cached
-    tokens + 64 BF16 tail tokens, INT4 anchor g=32, INT2 residuals g=16), in the
-    launch configuration the benchmark uses, on sampled (batch, head) pairs:
-    bytes of the sampled pairs, then every loop's row, one loop per call."""
+@pytest.mark.parametrize("wname", ["anchor-8k-perloop", "chain-8k-perloop"])
+def test_anchor_perloop_full_size(oracle, wname):
+    """The per-loop workloads at full size (batch 16, 16 heads, 8192 cached
+    tokens + 64 BF16 tail tokens, INT4 anchor g=32, INT2 residuals g=16; Last-
+    loop references, or Next-loop chains), in the launch configuration the
+    benchmark uses, on sampled (batch, head) pairs: bytes of the sampled
+    pairs, then every loop's row, one loop per call."""
     import decode_attention_rq_amd as rq
-    w = synth.WORKLOADS["anchor-8k-perloop"]
+    w = synth.WORKLOADS[wname]
     T = w.extra["tail"]
     n = w.n_ctx
     case = Case(w, n, gen_device="cuda")
