@@ -7,17 +7,22 @@
 namespace rq {
 
 // Kernel M: one workgroup per (batch*head, loop slot).  Its waves share the
-// BF16 tail of the slot's loop (original domain): each wave takes batches of
-// kTailBatch tokens (loads issued together, reductions interleaved) with its
-// own online softmax; the waves' states meet in LDS.  Wave 0 then merges the
-// splits' records with the tail state by log-sum-exp and finishes the row.
-constexpr int kTailBatch = 16;
+// BF16 tail of the slot's loop (original domain) with the decode kernel's
+// lane mapping: D/8 lanes per row, 8 dims per lane, 64/(D/8) rows side by
+// side, kTailRows rows per lane per batch (one 128-bit load per row and
+// lane, row sums by DPP inside the row's lanes, no LDS traffic).  Every lane
+// keeps the online softmax of its row; rows, then waves (through LDS), are
+// merged by log-sum-exp.  Wave 0 then merges the splits' records with the
+// tail state and finishes the row.
+constexpr int kTailRows = 4;
 constexpr int kMergeWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const DecodeArgs a, int n_res) {
   constexpr int E = D / 64;
   constexpr int REC = 2 * D + 2;
+  constexpr int LANES = D / 8;                 // lanes per tail row
+  constexpr int ROWS = kWave / LANES;          // rows side by side in a wave
   const int bh = blockIdx.x, s = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const bool residual = s < n_res;
@@ -35,65 +40,82 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
 #pragma unroll
   for (int e = 0; e < E; ++e) ot[e] = 0.0f;
   if (a.n_tail > 0) {
-    const uint16_t *qrow = a.q + ((size_t)a.qloop[s] * a.bh + bh) * D;
+    const int j = lane % LANES, r = lane / LANES;
     const uint16_t *tk = a.tk[s] + (size_t)bh * a.tcap * D;
     const uint16_t *tv = a.tv[s] + (size_t)bh * a.tcap * D;
-    float qv[E];
+    const uint4 qw = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+    float o8[8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) qv[e] = bf16lo(qrow[lane + 64 * e]);
-    for (int t0 = wave * kTailBatch; t0 < a.n_tail; t0 += nw * kTailBatch) {
-      float kk[kTailBatch][E], vv[kTailBatch][E];
+    for (int p = 0; p < 8; ++p) o8[p] = 0.0f;
+    for (int t0 = wave * ROWS * kTailRows; t0 < a.n_tail; t0 += nw * ROWS * kTailRows) {
+      uint4 kw[kTailRows], vw[kTailRows];
 #pragma unroll
-      for (int i = 0; i < kTailBatch; ++i) {
-        const size_t row = (size_t)min(t0 + i, a.n_tail - 1) * D;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kk[i][e] = bf16lo(tk[row + lane + 64 * e]);
-          vv[i][e] = bf16lo(tv[row + lane + 64 * e]);
-        }
+      for (int i = 0; i < kTailRows; ++i) {
+        const uint32_t t = (uint32_t)min(t0 + i * ROWS + r, a.n_tail - 1);
+        kw[i] = ldg_nt<uint4>(tk, t * (2 * D) + 16 * j);
+        vw[i] = ldg_nt<uint4>(tv, t * (2 * D) + 16 * j);
       }
-      float sc[kTailBatch];
-#pragma unroll
-      for (int i = 0; i < kTailBatch; ++i) {
-        float dp = 0.0f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) dp = __builtin_fmaf(qv[e], kk[i][e], dp);
-        sc[i] = group_sum<64>(dp) * a.qscale;
-      }
+      float sc[kTailRows];
       float mb = -FLT_MAX;
 #pragma unroll
-      for (int i = 0; i < kTailBatch; ++i) {
-        if (t0 + i >= a.n_tail) sc[i] = -INFINITY;
+      for (int i = 0; i < kTailRows; ++i) {
+        float dp = dot2bf0(qw.x, kw[i].x);
+        dp = dot2bf(qw.y, kw[i].y, dp);
+        dp = dot2bf(qw.z, kw[i].z, dp);
+        dp = dot2bf(qw.w, kw[i].w, dp);
+        sc[i] = group_sum_dpp<LANES>(dp) * a.qscale;
+        if (t0 + i * ROWS + r >= a.n_tail) sc[i] = -INFINITY;
         mb = fmaxf(mb, sc[i]);
       }
       if (mb > mt) {
         const float f = fexp2(mt - mb);
         lt *= f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) ot[e] *= f;
+        for (int p = 0; p < 8; ++p) o8[p] *= f;
         mt = mb;
       }
 #pragma unroll
-      for (int i = 0; i < kTailBatch; ++i) {
-        const float p = fexp2(sc[i] - mt);
-        lt += p;
+      for (int i = 0; i < kTailRows; ++i) {
+        const float pw = fexp2(sc[i] - mt);
+        lt += pw;
+        const uint32_t w4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
 #pragma unroll
-        for (int e = 0; e < E; ++e) ot[e] = __builtin_fmaf(p, vv[i][e], ot[e]);
+        for (int c = 0; c < 4; ++c) {
+          o8[2 * c] = __builtin_fmaf(pw, bf16lo(w4[c]), o8[2 * c]);
+          o8[2 * c + 1] = __builtin_fmaf(pw, bf16hi(w4[c]), o8[2 * c + 1]);
+        }
       }
     }
-  }
-  __shared__ float sm[kMergeWaves][2 + D];
-  if (nw > 1) {
-    if (lane == 0) { sm[wave][0] = mt; sm[wave][1] = lt; }
+    // rows of the wave (lane distances LANES, 2 LANES, ...), then waves
+    auto merge_with = [&](float mo, float lo, const float (&oo)[8]) {
+      const float Mx = fmaxf(mt, mo);
+      const float fa = fexp2(mt - Mx), fb = fexp2(mo - Mx);
+      lt = lt * fa + lo * fb;
 #pragma unroll
-    for (int e = 0; e < E; ++e) sm[wave][2 + lane + 64 * e] = ot[e];
+      for (int p = 0; p < 8; ++p) o8[p] = o8[p] * fa + oo[p] * fb;
+      mt = Mx;
+    };
+    auto merge_lanes = [&](auto mask_t) {
+      constexpr int MASK = decltype(mask_t)::value;
+      float oo[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) oo[p] = xor_lane<MASK>(o8[p]);
+      merge_with(xor_lane<MASK>(mt), xor_lane<MASK>(lt), oo);
+    };
+    if constexpr (ROWS >= 2) merge_lanes(std::integral_constant<int, LANES>{});
+    if constexpr (ROWS >= 4) merge_lanes(std::integral_constant<int, LANES * 2>{});
+    if constexpr (ROWS >= 8) merge_lanes(std::integral_constant<int, LANES * 4>{});
+    __shared__ float sm[kMergeWaves][2 + D];
+    if (r == 0) {
+      if (j == 0) { sm[wave][0] = mt; sm[wave][1] = lt; }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) sm[wave][2 + 8 * j + p] = o8[p];
+    }
     __syncthreads();
     if (wave != 0) return;
     mt = sm[0][0];
     for (int w = 1; w < nw; ++w) mt = fmaxf(mt, sm[w][0]);
     lt = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) ot[e] = 0.0f;
     for (int w = 0; w < nw; ++w) {
       const float f = fexp2(sm[w][0] - mt);
       lt = __builtin_fmaf(f, sm[w][1], lt);
