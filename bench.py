@@ -801,7 +801,7 @@ def main():
     achieved = alg_bytes / (launch_ms.mean() / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                "kernel": "decode step: decode_kernel" + (" + decode_merge_kernel" if splits > 1 else ""),
+                "kernel": "decode step: decode_kernel (+ decode_merge_kernel when the step writes split records)",
                 "algorithmic_bytes_per_launch": alg_bytes,
                 "launch_us_mean": round(float(launch_ms.mean()) * 1e3, 2),
                 "launch_us_min": round(float(launch_ms.min()) * 1e3, 2)}

@@ -2,6 +2,7 @@
 // host, fill the kernel argument blocks, enqueue on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -124,31 +125,41 @@ int decode_slots(int head_dim) {
   return n;
 }
 
-// Token splits for a decode step.  Start from about 4096 tokens per split,
-// or more splits when that leaves fewer workgroups than `slots` (compute
-// units times resident decode workgroups per unit); then, up to twice that
-// count, take the split count whose workgroups fill their rounds of `slots`
-// best (fewest splits on ties).  At most 32 splits, and never fewer than 512
-// tokens per split.  Interleaved MI355X timings over batch 4..97 at 8k and
-// 32k context put this rule within about 1% of the best split count, except
-// 2% at batch 97.
+// Token splits for a decode step (in units of 4-wave workgroups; `slots` =
+// compute units times resident decode workgroups per unit).
+//  * Small batch (bh workgroups leave slots idle): enough splits to fill the
+//    slots, but no more than about sqrt(n_ctx / 32): every workgroup runs at
+//    once, and the step is one workgroup's chain of tiles plus a merge that
+//    grows with the split count (8 splits at 2k, 16 from 8k on; never under
+//    256 tokens per split).
+//  * Large batch: a decode step is bound by HBM, and a partial last round of
+//    workgroups still streams at full rate once it holds half the slots.  So
+//    among 1..4 splits take the fewest rounds-equivalent of work, counting a
+//    partial round as at least half a round, with 1% for the merge of more
+//    than one split.
+// Interleaved MI355X timings (batch 1..64, 2k / 8k / 32k, fused and per-loop
+// passes) put this rule within 2% of the best count, 3% at batch 2.
 int auto_splits(const rq_layout *L, int n_ctx, int slots) {
   const int64_t bh = (int64_t)L->batch * L->n_heads;
-  int64_t max_s = n_ctx / 512 > 0 ? n_ctx / 512 : 1;
+  int64_t max_s = n_ctx / 256 > 0 ? n_ctx / 256 : 1;
   if (max_s > 32) max_s = 32;
-  int64_t s0 = (n_ctx + 4095) / 4096;
   const int64_t fill = (slots + bh - 1) / bh;
-  if (fill > s0) s0 = fill;
-  if (s0 > max_s) s0 = max_s;
-  const int64_t s1 = 2 * s0 < max_s ? 2 * s0 : max_s;
-  int64_t best = s0;
-  double best_eff = -1.0;
-  for (int64_t s = s0; s <= s1; ++s) {
-    const int64_t blocks = s * bh;
-    const int64_t rounds = (blocks + slots - 1) / slots;
-    const double eff = (double)blocks / (double)(rounds * slots);
-    if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
+  int64_t best = 1;
+  if (fill > 1) {
+    int64_t lat = (int64_t)std::lround(std::sqrt((double)n_ctx / 32.0));
+    if (lat < 1) lat = 1;
+    if (lat > 16) lat = 16;
+    best = fill < lat ? fill : lat;
+  } else {
+    double best_cost = -1.0;
+    for (int64_t sp = 1; sp <= 4; ++sp) {
+      const int64_t blocks = sp * bh, full = blocks / slots, rem = blocks % slots;
+      const double rounds = (double)full + (rem > 0 ? (double)std::max<int64_t>(rem, slots / 2) / slots : 0.0);
+      const double cost = rounds * (double)((n_ctx + sp - 1) / sp) * (sp > 1 ? 1.01 : 1.0);
+      if (best_cost < 0.0 || cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
+    }
   }
+  if (best > max_s) best = max_s;
   int64_t s = best;
   if (const char *env = std::getenv("RQ_DECODE_SPLITS")) {
     const int v = std::atoi(env);
@@ -339,6 +350,10 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.tcap = tail ? tail->capacity : 0;
   a.records = (S > 1 || n_tail > 0) ? 1 : 0;
   a.out_mask = loop_mask;
+  {
+    const int cus = cu_count();
+    a.wide = (S == 2 && n_tail == 0 && cus > 0 && a.bh <= cus) ? 1 : 0;
+  }
   a.group = L->group;
   a.rotate = L->rotate;
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
