@@ -192,7 +192,10 @@ int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
  *   loop_mask  bit l set = compute loop l; non-zero, no bit >= L
  *   n_ctx      1 <= n_ctx <= capacity
  *   sm_scale   finite softmax scale (1/sqrt(d) for standard attention)
- *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise
+ *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise.
+ *              How splits map onto workgroups is the library's choice (two
+ *              splits of a fused pass may run as one wider workgroup per
+ *              (b, h)); results agree to the tolerance below either way
  *   out        f32 [L][B][H][d]; rows of loops not in the mask are not written
  *   workspace  device scratch of at least rq_decode_workspace_bytes(layout,
  *              n_ctx, n_splits) bytes, 16-byte aligned; no initialisation
@@ -226,7 +229,8 @@ typedef struct {
  *   tail       NULL or a tail; tail->n == 0 makes this call rq_decode_attn
  *   n_ctx      0 <= n_ctx <= capacity, n_ctx + tail->n >= 1 (n_ctx = 0: the
  *              tail alone; no cache plane is read)
- * The tail is meant for tens of tokens: one wave per (row) walks it.
+ * The tail is meant for tens of tokens: the split-merge step attends over it,
+ * four waves per (b, h, loop).
  */
 rq_status rq_decode_attn_tail(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
                               const rq_tail *tail, const void *q, uint32_t loop_mask,
