@@ -39,8 +39,9 @@ def parse():
     p.add_argument("--no-bf16-baseline", action="store_true")
     p.add_argument("--graphs", action="store_true",
                    help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
-    p.add_argument("--mode", default="decode", choices=["decode", "copy"],
-                   help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling")
+    p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep"],
+                   help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling; "
+                        "split-sweep: every token-split count against the automatic one")
     a = p.parse_args()
     a.steps_given = a.steps is not None
     if a.steps is None:
@@ -717,10 +718,78 @@ def grid_bench(args, w, budget=250e9):
             "grid": rows}
 
 
+def split_sweep():
+    """Time every candidate token-split count against rq_decode_splits' choice,
+    interleaved (median of 4 rounds), for a fused call over all four loops (3
+    INT2 g=32 residuals + BF16 reference) and for per-loop calls over the
+    anchored [2,2,2,4] layout (INT4 anchor g=32, INT2 g=16): contexts x
+    batches, 16 heads, head_dim 128.  One JSON line per point on stdout."""
+    import numpy as np
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+    for kind, base, points in (
+            ("fused", synth.WORKLOADS["int2-8k"], [(n, B) for n in (2048, 8192, 32768)
+                                                   for B in (1, 2, 4, 8, 16, 24, 32, 48, 64)]),
+            ("per-loop", synth.WORKLOADS["anchor-8k-perloop"], [(n, B) for n in (2048, 8192)
+                                                                for B in (1, 2, 4, 8, 16, 32, 64, 128)])):
+        for n, B in points:
+            if B * n > 64 * 8192:
+                continue
+            w = synth.Workload("sweep", n_loops=4, batch=B, heads=16, d=128, g=base.g, n_ctx=n, bits=[2, 2, 2],
+                               c=base.c, sigma=base.sigma, rotate=1, seed=3, ref_bits=base.ref_bits,
+                               ref_group=base.ref_group)
+            lay = rq.Layout(4, B, 16, 128, w.g, n, 1, [2, 2, 2], ref_bits=w.ref_bits, ref_group=w.ref_group)
+            d = synth.draw_layer(w, batch=B, n=n, device="cuda")
+            k, v = rq.Cache(lay), rq.Cache(lay)
+            if k.ref is not None:
+                k.ref.copy_(d["k_ref"])
+                v.ref.copy_(d["v_ref"])
+                kin, vin = d["k_loops"], d["v_loops"]
+            else:
+                kin = torch.cat([d["k_loops"], d["k_ref"].unsqueeze(0)]).contiguous()
+                vin = torch.cat([d["v_loops"], d["v_ref"].unsqueeze(0)]).contiguous()
+            rq.rq_encode(lay, k, v, kin, vin, 0, n)
+            q = d["q"].contiguous()
+            del d, kin, vin
+            auto = rq.rq_decode_splits(lay, n)
+            cands = [S for S in (1, 2, 4, 8, 16, 32) if n // S >= 256]
+            wss = {S: rq.workspace_for(lay, n, S) for S in cands}
+            out = torch.empty(4, B, 16, 128, device="cuda")
+            masks = [15] if kind == "fused" else [1, 2, 4, 8]
+            scale = 1.0 / np.sqrt(128)
+
+            def call(S):
+                for m in masks:
+                    rq.rq_decode_attn(lay, k, v, q, m, n, scale, out, wss[S], S)
+            iters = max(3, min(20, int(2e5 // (B * n // 64 + 1000))))
+            res = {S: [] for S in cands}
+            for _ in range(4):
+                for S in cands:
+                    call(S)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(iters):
+                        call(S)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    res[S].append(e0.elapsed_time(e1) / iters * 1e3)
+            med = {S: round(float(np.median(t)), 1) for S, t in res.items()}
+            best = min(med, key=med.get)
+            print(json.dumps({"mode": "split-sweep", "pass": kind, "n_ctx": n, "batch": B, "auto_splits": auto,
+                              "auto_us": med.get(auto), "best_splits": best, "best_us": med[best],
+                              "us_per_step_by_splits": med}), flush=True)
+            del k, v, wss
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.mode == "copy":
         copy_probe()
+        return
+    if args.mode == "split-sweep":
+        split_sweep()
         return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1 (the per-(batch, head) "

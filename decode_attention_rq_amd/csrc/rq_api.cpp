@@ -137,8 +137,9 @@ int decode_slots(int head_dim) {
 //    among 1..4 splits take the fewest rounds-equivalent of work, counting a
 //    partial round as at least half a round, with 1% for the merge of more
 //    than one split.
-// Interleaved MI355X timings (batch 1..64, 2k / 8k / 32k, fused and per-loop
-// passes) put this rule within 2% of the best count, 3% at batch 2.
+// Interleaved MI355X timings (batch 1..128, 2k / 8k / 32k, fused and per-loop
+// passes) put this rule within 2% of the best count at most points, 5% at
+// worst.
 int auto_splits(const rq_layout *L, int n_ctx, int slots) {
   const int64_t bh = (int64_t)L->batch * L->n_heads;
   int64_t max_s = n_ctx / 256 > 0 ? n_ctx / 256 : 1;
