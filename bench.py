@@ -792,7 +792,7 @@ def main():
         split_sweep()
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus must be 1 (the per-(batch, head) "
+        print("bench.py: runs on one GPU; --gpus must be 1 (the per-(batch, head) "
               "work shards across GPUs without exchange, but no multi-GPU path is built)",
               file=sys.stderr)
         sys.exit(2)
