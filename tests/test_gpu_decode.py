@@ -74,13 +74,13 @@ def _check_rows(oracle, case, got, mask, n_ctx, scale=None):
 DECODE_CASES = {
     "tiny-d64-int2-norot": (_w(d=64, bits=(2,), rotate=0, B=1, H=1, seed=0), 128, 128, 0b11, [0, 1, 3]),
     "d128-int2x3": (_w(), 1000, 1024, 0b1111, [0, 1, 2, 7]),
-    "d128-mixed-ragged": (_w(bits=(4, 2, 2)), 517, 600, 0b1111, [0, 3]),
+    "d128-mixed-ragged": (_w(bits=(4, 2, 2)), 517, 600, 0b1111, [0, 2, 3]),
     "d128-residual-only": (_w(), 300, 300, 0b0101, [0, 5]),
     "d128-reference-only": (_w(), 300, 300, 0b1000, [0]),
     "d128-g16-norot": (_w(g=16, rotate=0), 257, 260, 0b1011, [0]),
     "d64-g32": (_w(d=64, bits=(2, 4)), 333, 333, 0b111, [0, 2]),
-    "d256": (_w(d=256, bits=(2, 2), B=1, H=2), 190, 200, 0b111, [0, 4]),
-    "multipass-6-loops": (_w(bits=(2, 4, 2, 2, 4), B=1, H=2), 150, 150, 0b111111, [0, 3]),
+    "d256": (_w(d=256, bits=(2, 2), B=1, H=2), 190, 200, 0b111, [0, 2, 4]),
+    "multipass-6-loops": (_w(bits=(2, 4, 2, 2, 4), B=1, H=2), 150, 150, 0b111111, [0, 2, 3]),
     "multipass-sparse-mask": (_w(bits=(2, 4, 2, 2, 4), B=1, H=2), 150, 150, 0b101110, [0]),
 }
 
@@ -126,8 +126,11 @@ def test_decode_deterministic():
 
 
 def test_decode_split_invariance():
+    """Split counts (2 splits of a fused pass run as one 8-wave workgroup per
+    (batch, head) here) agree to FP32 reordering, also with a ragged context."""
     w = _w()
-    case = Case(w, 640, cap=640)
-    outs = [_decode_gpu(case, 0b1111, 640, s) for s in (1, 2, 5, 16, 40)]
-    for o in outs[1:]:
-        assert tol_rel_row(o, outs[0]).max() <= 1e-5
+    for n in (640, 653):
+        case = Case(w, n, cap=n)
+        outs = [_decode_gpu(case, 0b1111, n, s) for s in (1, 2, 3, 5, 16, 40)]
+        for o in outs[1:]:
+            assert tol_rel_row(o, outs[0]).max() <= 1e-5
