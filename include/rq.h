@@ -29,8 +29,9 @@
  *     the rq_layout / rq_cache structs themselves, which are host memory and
  *     are only read during the call.
  *   - The library allocates nothing and frees nothing; the caller owns every
- *     buffer.  It keeps no state between calls except a per-device cache of
- *     the compute-unit count, and is safe to call from several host threads.
+ *     buffer.  It keeps no state between calls except per-device caches of
+ *     the compute-unit count and the decode kernel's occupancy, and is safe to
+ *     call from several host threads.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting for it.
  *   - Arguments are validated on the host before anything is enqueued; on any
