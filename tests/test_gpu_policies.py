@@ -16,13 +16,13 @@ from rq_testutil import Case, plane_bits, tol_rel_row
 pytestmark = pytest.mark.gpu
 
 
-def _w(alpha_mode=0, ref_first=0, ref_bits=0, group_loops=0, L=4, g=32, seed=71):
+def _w(alpha_mode=0, ref_first=0, ref_bits=0, group_loops=0, L=4, g=32, seed=71, d=128):
     bits = [2, 4, 2, 2, 2, 4, 2][:L - 1]
     if ref_first:
         bits = [0] + bits                          # loop 0 is the reference
     if group_loops:
         bits = [0 if (l % group_loops == (0 if ref_first else group_loops - 1)) else 2 for l in range(L)]
-    return synth.Workload("p", n_loops=L, batch=2, heads=2, d=128, g=g, n_ctx=0, bits=bits,
+    return synth.Workload("p", n_loops=L, batch=2, heads=2, d=d, g=g, n_ctx=0, bits=bits,
                           c=[0.85] * (L - 1), sigma=[0.12] * (L - 1), rotate=1, seed=seed,
                           ref_bits=ref_bits, ref_group=32 if ref_bits else 0, group_loops=group_loops,
                           ref_first=ref_first, alpha_mode=alpha_mode)
@@ -89,8 +89,8 @@ def test_policy_parity(oracle, name):
 # chained references (Table 9 "Next-loop", "Previous-loop")
 # --------------------------------------------------------------------------
 
-def _wc(ref_first=0, ref_bits=0, group_loops=0, L=4, seed=81):
-    w = _w(ref_first=ref_first, ref_bits=ref_bits, group_loops=group_loops, L=L, g=16, seed=seed)
+def _wc(ref_first=0, ref_bits=0, group_loops=0, L=4, seed=81, d=128, g=16):
+    w = _w(ref_first=ref_first, ref_bits=ref_bits, group_loops=group_loops, L=L, g=g, seed=seed, d=d)
     w.ref_chain = 1
     return w
 
@@ -101,6 +101,9 @@ CHAIN_CASES = {
     "previous-loop-anchor": _wc(ref_first=1, ref_bits=4),
     "previous-loop-bf16": _wc(ref_first=1),
     "next-loop-groups": _wc(ref_bits=4, group_loops=4, L=8),
+    "next-loop-anchor-d64": _wc(ref_bits=4, d=64),
+    "previous-loop-bf16-d256-g32": _wc(ref_first=1, d=256, g=32),
+    "next-loop-two-links": _wc(ref_bits=4, L=3),
 }
 
 
