@@ -89,8 +89,9 @@ def test_policy_parity(oracle, name):
 # chained references (Table 9 "Next-loop", "Previous-loop")
 # --------------------------------------------------------------------------
 
-def _wc(ref_first=0, ref_bits=0, group_loops=0, L=4, seed=81, d=128, g=16):
-    w = _w(ref_first=ref_first, ref_bits=ref_bits, group_loops=group_loops, L=L, g=g, seed=seed, d=d)
+def _wc(ref_first=0, ref_bits=0, group_loops=0, L=4, seed=81, d=128, g=16, alpha_mode=0):
+    w = _w(ref_first=ref_first, ref_bits=ref_bits, group_loops=group_loops, L=L, g=g, seed=seed, d=d,
+           alpha_mode=alpha_mode)
     w.ref_chain = 1
     return w
 
@@ -104,6 +105,8 @@ CHAIN_CASES = {
     "next-loop-anchor-d64": _wc(ref_bits=4, d=64),
     "previous-loop-bf16-d256-g32": _wc(ref_first=1, d=256, g=32),
     "next-loop-two-links": _wc(ref_bits=4, L=3),
+    "next-loop-norm-ratio": _wc(ref_bits=4, alpha_mode=2),
+    "previous-loop-alpha-one": _wc(ref_first=1, alpha_mode=1),
 }
 
 
