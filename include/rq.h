@@ -174,7 +174,9 @@ size_t rq_decode_workspace_bytes(const rq_layout *layout, int32_t n_ctx, int32_t
 
 /* rq_decode_splits -- the token-split count rq_decode_attn uses when asked
  * for 0 splits (a function of the layout, n_ctx and the device); < 0 on an
- * invalid layout or device error. */
+ * invalid layout or device error.  For tuning, a positive integer in the
+ * environment variable RQ_DECODE_SPLITS replaces the choice (capped at
+ * n_ctx); it is read on every call. */
 int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
 
 /*
