@@ -96,6 +96,15 @@ rq_status check_cache(const rq_layout *L, const rq_cache *c) {
 
 float rot_const(int d) { return (float)(1.0 / std::sqrt((double)d)); }
 
+// Test hook: with RQ_FAULT_INJECT=launch in the environment, every entry point
+// that enqueues work returns RQ_ERR_DEVICE after validating its arguments and
+// before any HIP call, so callers' device-error paths can be exercised
+// without a GPU.  Read on every call.
+bool launch_fault_injected() {
+  const char *v = std::getenv("RQ_FAULT_INJECT");
+  return v != nullptr && std::strcmp(v, "launch") == 0;
+}
+
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
@@ -211,6 +220,7 @@ rq_status rq_encode(const rq_layout *L, const rq_cache *k, const rq_cache *v, co
   // Inputs: with a BF16 reference the non-reference loops in loop order; with
   // quantized anchors every loop in loop order.
   const size_t loop_elems = (size_t)bh * n * L->head_dim;
+  if (launch_fault_injected()) return RQ_ERR_DEVICE;
   (void)hipGetLastError();
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
     const int an = anchor_of(L, g0);
@@ -362,6 +372,7 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
 
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int G = group_len(L);
+  if (launch_fault_injected()) return RQ_ERR_DEVICE;
   (void)hipGetLastError();
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
     const int ref_loop = anchor_of(L, g0);    // this group's reference / anchor
@@ -488,6 +499,7 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
   a.group = 32;
   a.qscale = sm_scale * 1.4426950408889634f;
   a.rot_c = 1.0f;
+  if (launch_fault_injected()) return RQ_ERR_DEVICE;
   (void)hipGetLastError();
   // every loop attends over its own BF16 cache: the reference-only kernel
   for (int l = 0; l < L->n_loops; ++l) {
@@ -552,6 +564,7 @@ rq_status rq_reconstruct(const rq_layout *L, const rq_cache *c, int32_t loop, in
   const int vpw = 64 / (L->head_dim / 8);
   a.chunks = (n + vpw - 1) / vpw;
   if ((int64_t)a.bh * a.chunks > INT32_MAX - 4) return RQ_ERR_UNSUPPORTED;
+  if (launch_fault_injected()) return RQ_ERR_DEVICE;
   (void)hipGetLastError();
   return rq::launch_reconstruct(a, L->head_dim, static_cast<hipStream_t>(hip_stream)) == hipSuccess
              ? RQ_OK : RQ_ERR_DEVICE;

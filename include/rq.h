@@ -46,6 +46,10 @@
  *     A quantized anchor uses codes[L-1] and meta[L-1] (its own bits and group)
  *     and has no alpha plane and no ref plane.
  *   - Non-finite inputs are not supported (results unspecified, no fault).
+ *   - Test hook: with RQ_FAULT_INJECT=launch in the environment, every entry
+ *     point that enqueues work returns RQ_ERR_DEVICE after validating its
+ *     arguments and before any HIP call (read on every call), so callers'
+ *     device-error paths can be exercised without a GPU.
  */
 #ifndef RQ_H_
 #define RQ_H_
