@@ -190,7 +190,11 @@ size_t workspace_for(const rq_layout *L, int n_splits) {
 
 extern "C" {
 
-const char *rq_status_string(rq_status s) {
+const char *rq_status_string(rq_status status) {
+  // A C caller may pass any int: read the bytes as one, since loading an
+  // out-of-range value through the enum type is undefined in C++.
+  int s;
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case RQ_OK: return "RQ_OK";
     case RQ_ERR_INVALID_ARG: return "RQ_ERR_INVALID_ARG: null or misaligned pointer, or an argument out of range";
