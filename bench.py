@@ -184,6 +184,14 @@ def copy_probe():
     print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}))
 
 
+def system_info():
+    """Device and software versions the numbers were taken with."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def layout_of(w, batch, cap):
     import decode_attention_rq_amd as rq
     return rq.Layout(w.n_loops, batch, w.heads, w.d, w.g, cap, w.rotate, w.bits)
@@ -889,6 +897,7 @@ def main():
         "hbm_gbs": round(achieved, 1),
         "roofline": roofline,
         "wall_s": round(wall, 3),
+        "system": system_info(),
     }
     if not args.no_bf16_baseline:
         del reps
