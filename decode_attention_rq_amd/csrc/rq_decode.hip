@@ -16,6 +16,10 @@ namespace rq {
 // tail state and finishes the row.
 constexpr int kTailRows = 4;
 constexpr int kMergeWaves = 4;
+// Split records read per batch of loads: the merge issues the loads of this
+// many records before it uses any of them, so a merge over S records waits
+// for ceil(S / kRecBatch) memory round trips, not S.
+constexpr int kRecBatch = 8;
 
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const DecodeArgs a, int n_res) {
@@ -28,13 +32,32 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
   const bool residual = s < n_res;
   if (!((a.out_mask >> a.qloop[s]) & 1u)) return;   // a chain link computed, not asked for
 
-  // split records of this (slot, batch*head): their maximum first, so the
-  // record loads overlap the tail walk
+  // split records of this (slot, batch*head): their maximum, and the first
+  // batch of records, are loaded before the tail walk so that those loads
+  // overlap it
   const size_t stride = (size_t)kMaxSlots * a.bh * REC;
   const float *rec0 = a.ws + ((size_t)s * a.bh + bh) * REC;
   float M = -FLT_MAX;
-  if (wave == 0)
+  float rm[kRecBatch], rl[kRecBatch], ro[kRecBatch][E], rr[kRecBatch][E];
+  // records [sp0, sp0 + kRecBatch) into rm/rl/ro/rr; indices past the last
+  // record re-read the last one (and are not used)
+  auto load_recs = [&](int sp0) {
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) {
+      const float *rec = rec0 + (size_t)min(sp0 + i, a.n_splits - 1) * stride;
+      rm[i] = rec[0];
+      rl[i] = rec[1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ro[i][e] = rec[2 + lane + 64 * e];
+        rr[i][e] = residual ? rec[2 + D + lane + 64 * e] : 0.0f;
+      }
+    }
+  };
+  if (wave == 0) {
     for (int sp = lane; sp < a.n_splits; sp += 64) M = fmaxf(M, rec0[sp * stride]);
+    if (a.n_splits > 0) load_recs(0);    // none when only the tail is attended
+  }
 
   float mt = -FLT_MAX, lt = 0.0f, ot[E];
 #pragma unroll
@@ -130,16 +153,22 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const De
   float L = 0.0f, o[E], q[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) { o[e] = 0.0f; q[e] = 0.0f; }
-  for (int sp = 0; sp < a.n_splits; ++sp) {
-    const float *rec = rec0 + sp * stride;
-    const float f = fexp2(rec[0] - Mall);
-    L = __builtin_fmaf(f, rec[1], L);
+  for (int sp0 = 0;;) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(f, rec[2 + lane + 64 * e], o[e]);
-    if (residual) {
+    for (int i = 0; i < kRecBatch; ++i) {
+      if (sp0 + i < a.n_splits) {
+        const float f = fexp2(rm[i] - Mall);
+        L = __builtin_fmaf(f, rl[i], L);
 #pragma unroll
-      for (int e = 0; e < E; ++e) q[e] = __builtin_fmaf(f, rec[2 + D + lane + 64 * e], q[e]);
+        for (int e = 0; e < E; ++e) {
+          o[e] = __builtin_fmaf(f, ro[i][e], o[e]);
+          q[e] = __builtin_fmaf(f, rr[i][e], q[e]);
+        }
+      }
     }
+    sp0 += kRecBatch;
+    if (sp0 >= a.n_splits) break;
+    load_recs(sp0);
   }
   const float ft = fexp2(mt - Mall);
   L = __builtin_fmaf(ft, lt, L);
