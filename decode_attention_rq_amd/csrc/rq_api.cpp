@@ -140,7 +140,9 @@ int decode_slots(int head_dim) {
 //    slots, but no more than about sqrt(n_ctx / 32): every workgroup runs at
 //    once, and the step is one workgroup's chain of tiles plus a merge that
 //    grows with the split count (8 splits at 2k, 16 from 8k on; never under
-//    256 tokens per split).
+//    256 tokens per split).  If those workgroups would not fit one per
+//    compute unit but 8 or more splits would, the most that fit are taken
+//    (they then run 8 waves each).
 //  * Large batch: a decode step is bound by HBM, and a partial last round of
 //    workgroups still streams at full rate once it holds half the slots.  So
 //    among 1..4 splits take the fewest rounds-equivalent of work, counting a
@@ -149,7 +151,7 @@ int decode_slots(int head_dim) {
 // Interleaved MI355X timings (batch 1..128, 2k / 8k / 32k, fused and per-loop
 // passes) put this rule within 2% of the best count at most points, 5% at
 // worst.
-int auto_splits(const rq_layout *L, int n_ctx, int slots) {
+int auto_splits(const rq_layout *L, int n_ctx, int slots, int cus) {
   const int64_t bh = (int64_t)L->batch * L->n_heads;
   int64_t max_s = n_ctx / 256 > 0 ? n_ctx / 256 : 1;
   if (max_s > 32) max_s = 32;
@@ -160,6 +162,10 @@ int auto_splits(const rq_layout *L, int n_ctx, int slots) {
     if (lat < 1) lat = 1;
     if (lat > 16) lat = 16;
     best = fill < lat ? fill : lat;
+    // Workgroups that fit one per compute unit run with 8 waves (see
+    // decode_waves); when `best` does not fit but 8 or more splits would,
+    // take the most that fit: as many waves per unit, half the records.
+    if (cus > 0 && best * bh > cus && cus / bh >= 8) best = cus / bh;
   } else {
     double best_cost = -1.0;
     for (int64_t sp = 1; sp <= 4; ++sp) {
@@ -176,6 +182,37 @@ int auto_splits(const rq_layout *L, int n_ctx, int slots) {
     if (v >= 1) s = v < n_ctx ? v : n_ctx;
   }
   return (int)s;
+}
+
+// Workgroup shape of a decode call with S token splits over bh batch*heads
+// (a kernel with ~250 VGPRs runs at most 8 waves per compute unit):
+//  * wide: two splits, no tail, and bh in (CUs/2, CUs]: the two 4-wave
+//    workgroups of each (b, h) run as one 8-wave workgroup over all tokens,
+//    with no split records and no merge launch (2-10% faster at batch 16
+//    for fused, per-loop, anchored and chained passes; with bh <= CUs/2 it
+//    would leave compute units idle);
+//  * waves8: otherwise, when S*bh <= CUs (one workgroup per unit), each
+//    split runs 8 waves instead of 4 (2-6% faster at batch 1-2);
+//  * else 4-wave workgroups, two per unit.
+// For tuning and tests, RQ_DECODE_WAVES=4 forces 4-wave workgroups, and
+// RQ_DECODE_WAVES=8 forces 8 (two splits and no tail then always run wide).
+// Read on every call.
+void decode_waves(int S, int n_tail, int bh, int32_t *wide, int32_t *waves8) {
+  int force = 0;
+  if (const char *env = std::getenv("RQ_DECODE_WAVES")) {
+    const int v = std::atoi(env);
+    if (v == 4 || v == 8) force = v;
+  }
+  const int cus = cu_count();
+  if (force == 4) {
+    *wide = *waves8 = 0;
+  } else if (force == 8) {
+    *wide = (S == 2 && n_tail == 0) ? 1 : 0;
+    *waves8 = 1;
+  } else {
+    *wide = (S == 2 && n_tail == 0 && cus > 0 && 2 * bh > cus && bh <= cus) ? 1 : 0;
+    *waves8 = (cus > 0 && (int64_t)S * bh <= cus) ? 1 : 0;
+  }
 }
 
 // Workspace: the split records f32 [S][kMaxSlots][BH][2D+2], at least one
@@ -281,7 +318,7 @@ int32_t rq_decode_splits(const rq_layout *L, int32_t n_ctx) {
   if (n_ctx == 0) return 1;
   const int slots = decode_slots(L->head_dim);
   if (slots <= 0) return RQ_ERR_DEVICE;
-  return auto_splits(L, n_ctx, slots);
+  return auto_splits(L, n_ctx, slots, cu_count());
 }
 
 size_t rq_decode_workspace_bytes(const rq_layout *L, int32_t n_ctx, int32_t n_splits) {
@@ -365,10 +402,7 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.tcap = tail ? tail->capacity : 0;
   a.records = (S > 1 || n_tail > 0) ? 1 : 0;
   a.out_mask = loop_mask;
-  {
-    const int cus = cu_count();
-    a.wide = (S == 2 && n_tail == 0 && cus > 0 && a.bh <= cus) ? 1 : 0;
-  }
+  decode_waves(S, n_tail, a.bh, &a.wide, &a.waves8);
   a.group = L->group;
   a.rotate = L->rotate;
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))

@@ -671,29 +671,29 @@ constexpr int kWaves = 4;
 template <int NS>
 constexpr int tiles_per_iter() { return NS == 1 ? 4 : kTilesPerIter; }
 
-// A fused pass (two or more loop slots, BF16 reference) split in two with no
-// tail, whose batch*heads fit one workgroup per compute unit (a.wide), runs
-// as one 8-wave workgroup per batch*head instead: the same waves over the same
-// tokens, two per SIMD as before, with no split records and no merge launch
-// (1.5-5% faster at batch 16, 2k-32k; for single-slot passes, or when the
-// 8-wave workgroups would not all be resident at once, it was slower).
+// Workgroup shape (decided on the host): a call of two splits with no tail
+// whose batch*heads fill the compute units once (a.wide) runs as one 8-wave
+// workgroup per batch*head instead: the same waves over the same tokens, two
+// per SIMD as before, with no split records and no merge launch.  Splits
+// that fit one workgroup per compute unit (a.waves8) run 8 waves each.
 template <int D, int NR, bool REF, int B4, int AQ, bool CHAIN>
 static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   constexpr int NS = NR + (REF ? 1 : 0);
   constexpr int TR = tiles_per_iter<NS>();
-  if constexpr (AQ == 0 && !CHAIN && NS >= 2) {
-    if (a.wide) {
-      DecodeArgs b = a;
-      b.n_splits = 1;
-      b.tps = a.n_ctx;
-      b.records = 0;
-      hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, 2 * kWaves, AQ, CHAIN>), dim3(1, a.bh),
-                         dim3(64 * 2 * kWaves), 0, st, b);
-      return hipGetLastError();
-    }
+  if (a.wide) {
+    DecodeArgs b = a;
+    b.n_splits = 1;
+    b.tps = a.n_ctx;
+    b.records = 0;
+    hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, 2 * kWaves, AQ, CHAIN>), dim3(1, a.bh),
+                       dim3(64 * 2 * kWaves), 0, st, b);
+    return hipGetLastError();
   }
-  const dim3 grid(a.n_splits, a.bh), block(64 * kWaves);
-  hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ, CHAIN>), grid, block, 0, st, a);
+  const dim3 grid(a.n_splits, a.bh);
+  if (a.waves8)
+    hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, 2 * kWaves, AQ, CHAIN>), grid, dim3(64 * 2 * kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ, CHAIN>), grid, dim3(64 * kWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
   return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);

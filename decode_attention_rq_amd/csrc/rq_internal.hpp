@@ -81,8 +81,9 @@ struct DecodeArgs {
   const uint16_t *tk[kMaxSlots], *tv[kMaxSlots];   // BF16 tail rows per slot [BH][tcap][D]
   int32_t tcap, n_tail;
   int32_t records;                   // write split records and merge (S > 1 or a tail)
-  int32_t wide;                      // two splits, no tail, batch*heads <= compute units: a fused
-                                     // BF16-reference pass runs as one 8-wave workgroup per batch*head
+  int32_t wide;                      // run the two splits as one 8-wave workgroup per batch*head,
+                                     // no records (two splits, no tail)
+  int32_t waves8;                    // 8-wave workgroups per split (else 4)
   uint32_t out_mask;                 // loops whose rows are written (a chain pass also
                                      // computes the links between them and the root)
   int32_t bh, cap, n_ctx, n_splits, tps;

@@ -200,9 +200,12 @@ int32_t rq_decode_splits(const rq_layout *layout, int32_t n_ctx);
  *   n_ctx      1 <= n_ctx <= capacity
  *   sm_scale   finite softmax scale (1/sqrt(d) for standard attention)
  *   n_splits   token splits (0 = automatic); 1 <= n_splits <= n_ctx otherwise.
- *              How splits map onto workgroups is the library's choice (two
- *              splits of a fused pass may run as one wider workgroup per
- *              (b, h)); results agree to the tolerance below either way
+ *              How splits map onto workgroups is the library's choice (a
+ *              split runs 4 or 8 waves; two splits without a tail may run as
+ *              one 8-wave workgroup per (b, h)); results agree to the
+ *              tolerance below either way.  For tuning and tests, the
+ *              environment variable RQ_DECODE_WAVES=4 or 8 fixes the waves
+ *              per split (read on every call)
  *   out        f32 [L][B][H][d]; rows of loops not in the mask are not written
  *   workspace  device scratch of at least rq_decode_workspace_bytes(layout,
  *              n_ctx, n_splits) bytes, 16-byte aligned; no initialisation

@@ -19,3 +19,14 @@ def oracle():
     build.build()
     rq_oracle._lib = None
     return rq_oracle
+
+
+@pytest.fixture(params=["auto", "4", "8"])
+def waves(request, monkeypatch):
+    """Decode workgroup shape: the library's choice, or 4 / 8 waves per split
+    forced through RQ_DECODE_WAVES (which the library reads on every call)."""
+    if request.param == "auto":
+        monkeypatch.delenv("RQ_DECODE_WAVES", raising=False)
+    else:
+        monkeypatch.setenv("RQ_DECODE_WAVES", request.param)
+    return request.param

@@ -138,7 +138,7 @@ DECODE_CASES = {
 
 
 @pytest.mark.parametrize("name", list(DECODE_CASES))
-def test_anchored_decode(oracle, name):
+def test_anchored_decode(oracle, name, waves):
     w, n, mask, T, splits = DECODE_CASES[name]
     case = Case(w, n, cap=n + 8)
     tk, tv = _tail(w, case.B, T)

@@ -86,7 +86,7 @@ DECODE_CASES = {
 
 
 @pytest.mark.parametrize("name", list(DECODE_CASES))
-def test_decode(oracle, name):
+def test_decode(oracle, name, waves):
     w, n, cap, mask, splits_list = DECODE_CASES[name]
     case = Case(w, n, cap=cap)
     for splits in splits_list:
@@ -125,12 +125,16 @@ def test_decode_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_decode_split_invariance():
-    """Split counts (2 splits of a fused pass run as one 8-wave workgroup per
-    (batch, head) here) agree to FP32 reordering, also with a ragged context."""
+def test_decode_split_invariance(monkeypatch):
+    """Split counts and workgroup shapes (4 or 8 waves per split; two splits
+    without a tail as one 8-wave workgroup per (batch, head)) agree to FP32
+    reordering, also with a ragged context."""
     w = _w()
     for n in (640, 653):
         case = Case(w, n, cap=n)
-        outs = [_decode_gpu(case, 0b1111, n, s) for s in (1, 2, 3, 5, 16, 40)]
+        outs = []
+        for wv in ("4", "8", ""):
+            monkeypatch.setenv("RQ_DECODE_WAVES", wv)
+            outs += [_decode_gpu(case, 0b1111, n, s) for s in (1, 2, 3, 5, 16, 40)]
         for o in outs[1:]:
             assert tol_rel_row(o, outs[0]).max() <= 1e-5

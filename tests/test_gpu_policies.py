@@ -111,7 +111,7 @@ CHAIN_CASES = {
 
 
 @pytest.mark.parametrize("name", list(CHAIN_CASES))
-def test_chain_parity(oracle, name):
+def test_chain_parity(oracle, name, waves):
     import decode_attention_rq_amd as rq
     w = CHAIN_CASES[name]
     n = 301
