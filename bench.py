@@ -563,7 +563,9 @@ def anchor_bench(args, w):
     roof = {"bound": "hbm", "achieved": round(res_call / (res_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(res_call / (res_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
             "kernel": "a residual loop's call (mean over the three): decode_kernel against the INT4 anchor"
-                      + (" along the reference chain" if w.ref_chain else "") + " + merge with the BF16 tail",
+                      + (" along the reference chain" if w.ref_chain else "")
+                      + " and the BF16 tail (one 8-wave workgroup per (b,h) attends both when the call has two"
+                        " splits; otherwise decode_merge_kernel merges the split records with the tail)",
             "algorithmic_bytes_per_launch": res_call, "launch_us_mean": round(res_us, 2),
             "anchor_loop_call_us_mean": round(float(call_ms[:, L - 1].mean()) * 1e3, 2)}
     res = {"metric": "per-loop decode tokens/s, [2,2,2,4] INT4 anchor + INT2 residuals g=16, 8k ctx + 64 BF16 tail"
@@ -878,7 +880,8 @@ def main():
     achieved = alg_bytes / (launch_ms.mean() / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                "kernel": "decode step: decode_kernel (+ decode_merge_kernel when the step writes split records)",
+                "kernel": "decode step: decode_kernel (+ decode_merge_kernel when the step has more than one "
+                          "workgroup per (b,h))",
                 "algorithmic_bytes_per_launch": alg_bytes,
                 "launch_us_mean": round(float(launch_ms.mean()) * 1e3, 2),
                 "launch_us_min": round(float(launch_ms.min()) * 1e3, 2)}

@@ -186,18 +186,18 @@ int auto_splits(const rq_layout *L, int n_ctx, int slots, int cus) {
 
 // Workgroup shape of a decode call with S token splits over bh batch*heads
 // (a kernel with ~250 VGPRs runs at most 8 waves per compute unit):
-//  * wide: two splits, no tail, and bh in (CUs/2, CUs]: the two 4-wave
-//    workgroups of each (b, h) run as one 8-wave workgroup over all tokens,
-//    with no split records and no merge launch (2-10% faster at batch 16
-//    for fused, per-loop, anchored and chained passes; with bh <= CUs/2 it
-//    would leave compute units idle);
+//  * wide: two splits and bh in (CUs/2, CUs]: the two 4-wave workgroups of
+//    each (b, h) run as one 8-wave workgroup over all tokens, with no split
+//    records and no merge launch (2-10% faster at batch 16 for fused,
+//    per-loop, anchored and chained passes; with bh <= CUs/2 it would leave
+//    compute units idle);
 //  * waves8: otherwise, when S*bh <= CUs (one workgroup per unit), each
 //    split runs 8 waves instead of 4 (2-6% faster at batch 1-2);
 //  * else 4-wave workgroups, two per unit.
 // For tuning and tests, RQ_DECODE_WAVES=4 forces 4-wave workgroups, and
-// RQ_DECODE_WAVES=8 forces 8 (two splits and no tail then always run wide).
-// Read on every call.
-void decode_waves(int S, int n_tail, int bh, int32_t *wide, int32_t *waves8) {
+// RQ_DECODE_WAVES=8 forces 8 (two splits then always run wide).  Read on
+// every call.
+void decode_waves(int S, int bh, int32_t *wide, int32_t *waves8) {
   int force = 0;
   if (const char *env = std::getenv("RQ_DECODE_WAVES")) {
     const int v = std::atoi(env);
@@ -207,10 +207,10 @@ void decode_waves(int S, int n_tail, int bh, int32_t *wide, int32_t *waves8) {
   if (force == 4) {
     *wide = *waves8 = 0;
   } else if (force == 8) {
-    *wide = (S == 2 && n_tail == 0) ? 1 : 0;
+    *wide = S == 2 ? 1 : 0;
     *waves8 = 1;
   } else {
-    *wide = (S == 2 && n_tail == 0 && cus > 0 && 2 * bh > cus && bh <= cus) ? 1 : 0;
+    *wide = (S == 2 && cus > 0 && 2 * bh > cus && bh <= cus) ? 1 : 0;
     *waves8 = (cus > 0 && (int64_t)S * bh <= cus) ? 1 : 0;
   }
 }
@@ -400,9 +400,13 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.tps = tps;
   a.n_tail = n_tail;
   a.tcap = tail ? tail->capacity : 0;
-  a.records = (S > 1 || n_tail > 0) ? 1 : 0;
   a.out_mask = loop_mask;
-  decode_waves(S, n_tail, a.bh, &a.wide, &a.waves8);
+  decode_waves(S, a.bh, &a.wide, &a.waves8);
+  // One split (or the wide form of two): the decode kernel attends the tail
+  // itself and finishes the rows.  Otherwise it writes split records, and
+  // the merge kernel merges them with the tail.
+  a.tail_in = (n_tail > 0 && (S == 1 || a.wide)) ? 1 : 0;
+  a.records = (S > 1 && !a.wide) ? 1 : 0;
   a.group = L->group;
   a.rotate = L->rotate;
   a.qscale = sm_scale * 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
@@ -523,13 +527,14 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
   S = (n_ctx + tps - 1) / tps;
   rq::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
-  a.records = S > 1 ? 1 : 0;
+  a.bh = L->batch * L->n_heads;
+  decode_waves(S, a.bh, &a.wide, &a.waves8);   // the same workgroup shapes as rq_decode_attn
+  a.records = (S > 1 && !a.wide) ? 1 : 0;
   a.out_mask = 0xffffffffu;
   a.agroup = 32;
   a.ws = static_cast<float *>(workspace);
   a.out = out;
   a.q = static_cast<const uint16_t *>(q);
-  a.bh = L->batch * L->n_heads;
   a.cap = L->capacity;
   a.n_ctx = n_ctx;
   a.n_splits = S;

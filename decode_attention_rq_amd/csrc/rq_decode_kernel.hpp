@@ -373,6 +373,80 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
   }
 
+  // ---- BF16 tail rows (a single-split launch attends them here; otherwise
+  // the merge kernel does).  They are the loop's own K and V in the original
+  // domain; each wave takes every W-th group of ROWS rows.  Scores use the
+  // BF16 query; values go to the accumulator the output is finished from:
+  // the reference sums (original domain) with a BF16 reference, or with a
+  // quantized anchor the code sums, which live in the rotated domain and
+  // carry the 2^(pos-24) code factors, so those rows enter as c H v times
+  // those factors (finish_row un-rotates them back).
+  if (a.tail_in) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;   // a chain link not asked for
+      const uint16_t *tk = a.tk[s] + (size_t)bh * a.tcap * D;
+      const uint16_t *tv = a.tv[s] + (size_t)bh * a.tcap * D;
+      uint32_t qw[4];
+      if constexpr (AQ == 0) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) qw[p] = qb[s][p];
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+        qw[0] = w.x; qw[1] = w.y; qw[2] = w.z; qw[3] = w.w;
+      }
+      for (int t0 = wave * ROWS; t0 < a.n_tail; t0 += W * ROWS) {
+        const uint32_t t = (uint32_t)min(t0 + r, a.n_tail - 1);
+        const uint4 kw = ldg_nt<uint4>(tk, t * (2 * D) + 16 * j);
+        const uint4 vw = ldg_nt<uint4>(tv, t * (2 * D) + 16 * j);
+        float dp = dot2bf0(qw[0], kw.x);
+        dp = dot2bf(qw[1], kw.y, dp);
+        dp = dot2bf(qw[2], kw.z, dp);
+        dp = dot2bf(qw[3], kw.w, dp);
+        const float tot = group_sum_dpp<LANES>(dp) * a.qscale;
+        const float sc = t0 + r < a.n_tail ? tot : -INFINITY;
+        if (sc > m[s]) {
+          const float f = fexp2(m[s] - sc);
+          m[s] = sc;
+          if (own == s) l_own *= f;
+          if (s >= OREF_FROM) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+            if (AQ) zref *= f;
+          }
+          if (s < NR) {
+            zacc[s] *= f;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+          }
+        }
+        const float pw = fexp2(sc - m[s]);
+        if (own == s) l_own += pw;
+        float y[8];
+        y[0] = bf16lo(vw.x); y[1] = bf16hi(vw.x);
+        y[2] = bf16lo(vw.y); y[3] = bf16hi(vw.y);
+        y[4] = bf16lo(vw.z); y[5] = bf16hi(vw.z);
+        y[6] = bf16lo(vw.w); y[7] = bf16hi(vw.w);
+        if constexpr (AQ == 0) {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pw, y[p], oref[s][p]);
+        } else {
+          if (a.rotate) {
+            wht8<D>(y, lane);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) y[p] *= a.rot_c;
+          }
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            const float yp = y[p] * (1.0f / (float)(1 << (24 - code_pos(p))));
+            if (s < NR) ores[s][p] = __builtin_fmaf(pw, yp, ores[s][p]);
+            else oref[s][p] = __builtin_fmaf(pw, yp, oref[s][p]);
+          }
+        }
+      }
+    }
+  }
+
   auto load = [&](Tile<TR, NRA, AQ> &T, int base) {
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
