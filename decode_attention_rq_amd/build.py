@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
 SOURCES = ["rq_api.cpp", "rq_encode.hip", "rq_reconstruct.hip", "rq_decode.hip",
            "rq_decode_anchor4.hip", "rq_decode_anchor2.hip", "rq_decode_chain0.hip",
-           "rq_decode_chain4.hip"]
+           "rq_decode_chain4.hip", "rq_decode_chain0_one.hip", "rq_decode_chain4_one.hip"]
 ARCH = os.environ.get("RQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -434,6 +434,14 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
     }
     bool want_ref = (loop_mask >> ref_loop) & 1u;
     if (nres == 0 && !want_ref) continue;
+    // A chain pass whose only wanted output is its first slot (a call for
+    // one loop) computes that slot alone; the links are read, not attended.
+    int chain_mode = 0;
+    if (L->ref_chain) {
+      chain_mode = want_ref ? 1 : 2;
+      for (int i = 1; i < nres; ++i)
+        if ((loop_mask >> res[i]) & 1u) chain_mode = 1;
+    }
     if (L->ref_bits) {
       a.kac = static_cast<const uint8_t *>(k->codes[ref_loop]);
       a.vac = static_cast<const uint8_t *>(v->codes[ref_loop]);
@@ -470,7 +478,7 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
       }
       hipError_t e;
       if (n_ctx > 0)
-        e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, L->ref_chain != 0, stream);
+        e = rq::launch_decode(a, L->head_dim, cnt, want_ref, L->ref_bits, chain_mode, stream);
       else   // the tail alone: the merge kernel attends over it, no split records
         e = rq::launch_merge(a, L->head_dim, cnt, cnt + (want_ref ? 1 : 0), stream);
       if (e != hipSuccess) return RQ_ERR_DEVICE;

@@ -193,7 +193,7 @@ template <int D>
 static int blocks_per_cu_d() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0, false>, 64 * kWaves, 0) != hipSuccess)
+          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0, 0>, 64 * kWaves, 0) != hipSuccess)
     return -1;
   return n;
 }
@@ -207,26 +207,32 @@ int decode_blocks_per_cu(int head_dim) {
   }
 }
 
-template hipError_t launch_decode_aq<0, false>(const DecodeArgs &, int, int, bool, hipStream_t);
-// instantiated in rq_decode_anchor{2,4}.hip and rq_decode_chain{0,4}.hip
-extern template hipError_t launch_decode_aq<2, false>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<4, false>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<0, true>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<4, true>(const DecodeArgs &, int, int, bool, hipStream_t);
+template hipError_t launch_decode_aq<0, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
+// instantiated in rq_decode_anchor{2,4}.hip, rq_decode_chain{0,4}.hip and
+// rq_decode_chain{0,4}_one.hip
+extern template hipError_t launch_decode_aq<2, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<4, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<0, 1>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<4, 1>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<0, 2>(const DecodeArgs &, int, int, bool, hipStream_t);
+extern template hipError_t launch_decode_aq<4, 2>(const DecodeArgs &, int, int, bool, hipStream_t);
 
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
-                         bool chain, hipStream_t st) {
-  if (chain) {
+                         int chain, hipStream_t st) {
+  if (chain == 1 || chain == 2) {
     switch (anchor_bits) {
-      case 0: return launch_decode_aq<0, true>(a, head_dim, n_res, ref, st);
-      case 4: return launch_decode_aq<4, true>(a, head_dim, n_res, ref, st);
+      case 0: return chain == 1 ? launch_decode_aq<0, 1>(a, head_dim, n_res, ref, st)
+                                : launch_decode_aq<0, 2>(a, head_dim, n_res, ref, st);
+      case 4: return chain == 1 ? launch_decode_aq<4, 1>(a, head_dim, n_res, ref, st)
+                                : launch_decode_aq<4, 2>(a, head_dim, n_res, ref, st);
       default: return hipErrorInvalidValue;
     }
   }
+  if (chain != 0) return hipErrorInvalidValue;
   switch (anchor_bits) {
-    case 0: return launch_decode_aq<0, false>(a, head_dim, n_res, ref, st);
-    case 2: return launch_decode_aq<2, false>(a, head_dim, n_res, ref, st);
-    case 4: return launch_decode_aq<4, false>(a, head_dim, n_res, ref, st);
+    case 0: return launch_decode_aq<0, 0>(a, head_dim, n_res, ref, st);
+    case 2: return launch_decode_aq<2, 0>(a, head_dim, n_res, ref, st);
+    case 4: return launch_decode_aq<4, 0>(a, head_dim, n_res, ref, st);
     default: return hipErrorInvalidValue;
   }
 }

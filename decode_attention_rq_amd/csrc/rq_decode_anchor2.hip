@@ -5,6 +5,6 @@
 
 namespace rq {
 
-template hipError_t launch_decode_aq<2, false>(const DecodeArgs &, int, int, bool, hipStream_t);
+template hipError_t launch_decode_aq<2, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
 
 }  // namespace rq

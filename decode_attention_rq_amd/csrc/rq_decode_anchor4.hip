@@ -5,6 +5,6 @@
 
 namespace rq {
 
-template hipError_t launch_decode_aq<4, false>(const DecodeArgs &, int, int, bool, hipStream_t);
+template hipError_t launch_decode_aq<4, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
 
 }  // namespace rq

@@ -6,6 +6,6 @@
 
 namespace rq {
 
-template hipError_t launch_decode_aq<4, true>(const DecodeArgs &, int, int, bool, hipStream_t);
+template hipError_t launch_decode_aq<4, 1>(const DecodeArgs &, int, int, bool, hipStream_t);
 
 }  // namespace rq

@@ -263,20 +263,28 @@ struct Tile : RefTile<TR, AQ> {
 // rescale; below it, weights exp2(s - m) stay <= 2^8 and no rescale is done.
 constexpr float kRescaleSlack = 8.0f;
 
-// CHAIN: chained references (each residual loop's reference is the next slot's
-// reconstruction, the last residual slot's is the pass's reference).  Slot i
-// then scores q_i . K_i with K_i = a_i K_{i+1} + r_i unrolled down the chain,
-// and accumulates p_i (prod a) r_m for every m >= i into its residual sum.
-template <int D, int NR, bool REF, int B4, int TR, int W, int AQ, bool CHAIN>
+// CHAIN (1, 2): chained references (each residual loop's reference is the
+// next slot's reconstruction, the last residual slot's is the pass's
+// reference).  Slot i then scores q_i . K_i with K_i = a_i K_{i+1} + r_i
+// unrolled down the chain, and accumulates p_i (prod a) r_m for every m >= i
+// into its residual sum.  CHAIN == 2 computes slot 0 alone (the other slots
+// are links whose outputs are not asked for).
+template <int D, int NR, bool REF, int B4, int TR, int W, int AQ, int CHAIN>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   constexpr int LANES = D / 8;
   constexpr int ROWS = kWave / LANES;
   constexpr int NS = NR + (REF ? 1 : 0);
   constexpr int NRA = NR > 0 ? NR : 1;
+  // Slots computed: every slot of the pass, or with CHAIN == 2 only slot 0
+  // (a call for one loop along a chain reads every link's planes but wants
+  // none of the links' own outputs).
+  constexpr int NSC = CHAIN == 2 ? 1 : NS;
+  constexpr int NRS = CHAIN == 2 ? 1 : NR;     // residual slots computed
+  constexpr int NRSA = NRS > 0 ? NRS : 1;
   constexpr int TILE = ROWS * TR;
   constexpr int STEP = W * TILE;
   constexpr int REC = 2 * D + 2;
-  static_assert(W >= NS, "one merging wave per loop slot");
+  static_assert(W >= NSC, "one merging wave per loop slot");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane % LANES, r = lane / LANES;
   const uint32_t sel2 = int2_sel(j);                // INT2 code bytes in the loaded word
@@ -320,19 +328,19 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // pre-multiplied by 2^(24 - pos) for its code's position in code_halves
   // (qr); sig is the lane's sum of q' for the offsets.  Scores are scaled by
   // sm_scale*log2(e) after the row sum.
-  constexpr int NQB = AQ ? 1 : NS;
-  constexpr int NQR = AQ ? NS : NRA;
+  constexpr int NQB = AQ ? 1 : NSC;
+  constexpr int NQR = AQ ? NSC : NRSA;
   uint32_t qb[NQB][4];
   float qr[NQR][8], sig[NQR];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int s = 0; s < NSC; ++s) {
     const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
     const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
     if constexpr (!AQ) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) qb[s][p] = wq[p];
     }
-    if (AQ || s < NR) {
+    if (AQ || s < NRS) {
       const int i = s < NQR ? s : 0;
       float f[8];
 #pragma unroll
@@ -358,16 +366,16 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // their residual accumulator (both are code sums in the same domain), so
   // only the anchor's own slot keeps a reference accumulator (with offset
   // share zref).
-  constexpr int OREF_FROM = AQ ? NR : 0;
-  float m[NS], l_own = 0.0f, oref[NS][8], ores[NRA][8], zacc[NRA], zref = 0.0f;
+  constexpr int OREF_FROM = AQ ? NRS : 0;
+  float m[NSC], l_own = 0.0f, oref[NSC][8], ores[NRSA][8], zacc[NRSA], zref = 0.0f;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int s = 0; s < NSC; ++s) {
     m[s] = -FLT_MAX;
 #pragma unroll
     for (int p = 0; p < 8; ++p) oref[s][p] = 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < NRA; ++i) {
+  for (int i = 0; i < NRSA; ++i) {
     zacc[i] = 0.0f;
 #pragma unroll
     for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // those factors (finish_row un-rotates them back).
   if (a.tail_in) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSC; ++s) {
       if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;   // a chain link not asked for
       const uint16_t *tk = a.tk[s] + (size_t)bh * a.tcap * D;
       const uint16_t *tv = a.tv[s] + (size_t)bh * a.tcap * D;
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
             for (int p = 0; p < 8; ++p) oref[s][p] *= f;
             if (AQ) zref *= f;
           }
-          if (s < NR) {
+          if (s < NRS) {
             zacc[s] *= f;
 #pragma unroll
             for (int p = 0; p < 8; ++p) ores[s][p] *= f;
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int p = 0; p < 8; ++p) {
             const float yp = y[p] * (1.0f / (float)(1 << (24 - code_pos(p))));
-            if (s < NR) ores[s][p] = __builtin_fmaf(pw, yp, ores[s][p]);
+            if (s < NRS) ores[s][p] = __builtin_fmaf(pw, yp, ores[s][p]);
             else oref[s][p] = __builtin_fmaf(pw, yp, oref[s][p]);
           }
         }
@@ -485,17 +493,17 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   auto process = [&](const Tile<TR, NRA, AQ> &T, int base, auto full_tile) {
     constexpr bool FULL = decltype(full_tile)::value;
     // scores (log2 units)
-    float sc[TR][NS];
+    float sc[TR][NSC];
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
       // Partial scores of this lane's 8 dims, in units of 1/qscale: the
       // reference dots are exact BF16 products; the residual dots and their
       // offset terms carry q' without the softmax scale, and the FP16 scale,
       // zero and LS coefficient enter v_fma_mix_f32 as stored.
-      float part[NS];
+      float part[NSC];
       if constexpr (AQ == 0) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int s = 0; s < NSC; ++s) {
           float dy = dot2bf0(qb[s][0], T.yk[u].x);
           dy = dot2bf(qb[s][1], T.yk[u].y, dy);
           dy = dot2bf(qb[s][2], T.yk[u].z, dy);
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         code_halves<AINT4>(T.ak[u], hk, sel2);
         const uint32_t mw = T.amk[u];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int s = 0; s < NSC; ++s) {
           const float dc = code_dot_h(hk, qr[s], 0.0f);
           part[s] = __builtin_fmaf(h_lo(mw), dc, __builtin_fmaf(h_hi(mw), sig[s], 0.0f));
         }
@@ -519,7 +527,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         else code_halves<false>(T.kc[u][m], hk[m], sel2);
       }
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
+      for (int i = 0; i < NRS; ++i) {
         // K_i = a_i K_{i+1} + r_i: from the reference (part) down to loop i
         float acc = part[i];
 #pragma unroll
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       }
       const bool valid = FULL || base + u * ROWS + r < t_end;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int s = 0; s < NSC; ++s) {
         const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
         sc[u][s] = FULL ? tot : (valid ? tot : -INFINITY);
       }
@@ -544,10 +552,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     // One test over all slots guards the (rarely taken) rescale code, so
     // every score sum is complete before the branch and each sum's last lane
     // move fuses into its add.
-    float mts[NS];
+    float mts[NSC];
     bool grow = false;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSC; ++s) {
       mts[s] = sc[0][s];
 #pragma unroll
       for (int u = 1; u < TR; ++u) mts[s] = fmaxf(mts[s], sc[u][s]);
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     }
     if (grow) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSC; ++s) {
       const float mt = mts[s];
       if (mt > m[s] + kRescaleSlack) {
         const float f = fexp2(m[s] - mt);
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           for (int p = 0; p < 8; ++p) oref[s][p] *= f;
           if (AQ) zref *= f;
         }
-        if (s < NR) {
+        if (s < NRS) {
           zacc[s] *= f;
 #pragma unroll
           for (int p = 0; p < 8; ++p) ores[s][p] *= f;
@@ -591,15 +599,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       // one exponential per lane (slot own), shared across the quad
       float x = sc[u][0] - m[0];
 #pragma unroll
-      for (int s = 1; s < NS; ++s) {
+      for (int s = 1; s < NSC; ++s) {
         const float xs = sc[u][s] - m[s];
         x = own == s ? xs : x;
       }
       const float p_own = fexp2(x);
       l_own += p_own;
-      float pq[NS];
+      float pq[NSC];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) pq[s] = quad_bcast(p_own, s);
+      for (int s = 0; s < NSC; ++s) pq[s] = NSC == 1 ? p_own : quad_bcast(p_own, s);
       uint32_t hvc[NRA][4];
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
@@ -607,9 +615,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         else code_halves<false>(T.vc[u][m], hvc[m], sel2);
       }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int s = 0; s < NSC; ++s) {
         const float pr = pq[s];
-        if (s < NR) {
+        if (s < NRS) {
           // p (s_m code + z_m) for loop s (and, chained, every loop after it,
           // each weighted by the alphas on the way), then the reference's part
           float w = pr;
@@ -666,29 +674,29 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 
   // undo the 2^(pos-24) factors of the value codes, add the offsets' share
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
+  for (int i = 0; i < NRS; ++i) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) ores[i][p] = __builtin_fmaf(ores[i][p], (float)(1 << (24 - code_pos(p))), zacc[i]);
   }
   if constexpr (AQ > 0 && REF) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) oref[NR][p] = __builtin_fmaf(oref[NR][p], (float)(1 << (24 - code_pos(p))), zref);
+    for (int p = 0; p < 8; ++p) oref[NRS][p] = __builtin_fmaf(oref[NRS][p], (float)(1 << (24 - code_pos(p))), zref);
   }
 
   // ---- merge rows, then waves -----------------------------------------------
-  if constexpr (ROWS >= 2) merge_rows<LANES, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
-  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NS, NR, OREF_FROM>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 2) merge_rows<LANES, NSC, NRS, OREF_FROM>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 4) merge_rows<LANES * 2, NSC, NRS, OREF_FROM>(m, l_own, own, oref, ores);
+  if constexpr (ROWS >= 8) merge_rows<LANES * 4, NSC, NRS, OREF_FROM>(m, l_own, own, oref, ores);
 
-  __shared__ float sm[W][NS][REC];
+  __shared__ float sm[W][NSC][REC];
   if (r == 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSC; ++s) {
       if (j == 0) sm[wave][s][0] = m[s];
       if (j == s) sm[wave][s][1] = l_own;
 #pragma unroll
       for (int p = 0; p < 8; ++p) sm[wave][s][2 + 8 * j + p] = s >= OREF_FROM ? oref[s][p] : 0.0f;
-      if (s < NR) {
+      if (s < NRS) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) sm[wave][s][2 + D + 8 * j + p] = ores[s][p];
       }
@@ -696,9 +704,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   }
   __syncthreads();
   // wave s combines loop slot s over the W waves
-  if (wave < NS) {
+  if (wave < NSC) {
     const int s = wave;
-    const bool residual = s < NR;
+    const bool residual = s < NRS;
     float M = sm[0][s][0];
 #pragma unroll
     for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w][s][0]);
@@ -750,7 +758,7 @@ constexpr int tiles_per_iter() { return NS == 1 ? 4 : kTilesPerIter; }
 // workgroup per batch*head instead: the same waves over the same tokens, two
 // per SIMD as before, with no split records and no merge launch.  Splits
 // that fit one workgroup per compute unit (a.waves8) run 8 waves each.
-template <int D, int NR, bool REF, int B4, int AQ, bool CHAIN>
+template <int D, int NR, bool REF, int B4, int AQ, int CHAIN>
 static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   constexpr int NS = NR + (REF ? 1 : 0);
   constexpr int TR = tiles_per_iter<NS>();
@@ -770,11 +778,12 @@ static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ, CHAIN>), grid, dim3(64 * kWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
+  if constexpr (CHAIN == 2) return launch_merge(a, D, 1, 1, st);
   return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);
 }
 
 // Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
-template <int D, int NR, bool REF, int AQ, bool CHAIN>
+template <int D, int NR, bool REF, int AQ, int CHAIN>
 static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
   int b4 = 0;
   for (int i = 0; i < NR; ++i) b4 |= (a.bits[i] == 4) << i;
@@ -791,8 +800,16 @@ static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-template <int D, int AQ, bool CHAIN>
+template <int D, int AQ, int CHAIN>
 static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
+  if constexpr (CHAIN == 2) {       // slot 0 alone: never the reference slot
+    switch (ref ? -1 : n_res) {
+      case 1: return launch_bits<D, 1, false, AQ, CHAIN>(a, st);
+      case 2: return launch_bits<D, 2, false, AQ, CHAIN>(a, st);
+      case 3: return launch_bits<D, 3, false, AQ, CHAIN>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (ref) {
     switch (n_res) {
       case 0: return launch_bits<D, 0, true, AQ, CHAIN>(a, st);
@@ -812,7 +829,7 @@ static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipS
 
 // One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits),
 // chained references or not.
-template <int AQ, bool CHAIN>
+template <int AQ, int CHAIN>
 hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
   switch (head_dim) {
     case 64: return launch_decode_d<64, AQ, CHAIN>(a, n_res, ref, st);

@@ -96,11 +96,12 @@ struct DecodeArgs {
 hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
 // One decode pass of n_res residual loops (+ the reference loop if ref);
-// anchor_bits 0 for a BF16 reference.  Launches the merge kernel too when
-// a.records is set.
+// anchor_bits 0 for a BF16 reference; chain 0 (independent references), 1
+// (chained references, every slot computed) or 2 (chained, slot 0 alone).
+// Launches the merge kernel too when a.records is set.
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
-                         bool chain, hipStream_t s);
-template <int AQ, bool CHAIN>
+                         int chain, hipStream_t s);
+template <int AQ, int CHAIN>
 hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
 // The split/tail merge for n_slots loop slots, the first n_res of them residual.
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t s);
