@@ -321,7 +321,75 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     va[i] = a.va[i] + row0;
   }
 
+  auto load = [&](Tile<TR, NRA, AQ> &T, int base) {
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+      const uint32_t t = (uint32_t)min(base + u * ROWS + r, t_end - 1);
+      if constexpr (AQ == 0) {
+        T.yk[u] = ldg_nt<uint4>(kref, t * (2 * D) + 16 * j);
+        T.yv[u] = ldg_nt<uint4>(vref, t * (2 * D) + 16 * j);
+      } else {
+        if constexpr (AINT4) {
+          T.ak[u] = ldg_nt<uint32_t>(kac, t * (D / 2) + 4 * j);
+          T.av[u] = ldg_nt<uint32_t>(vac, t * (D / 2) + 4 * j);
+        } else {
+          T.ak[u] = ldg_nt<uint32_t>(kac, t * (D / 4) + 4 * (j >> 1));
+          T.av[u] = ldg_nt<uint32_t>(vac, t * (D / 4) + 4 * (j >> 1));
+        }
+        T.amk[u] = ldg<uint32_t>(kam, ((t << ashift) + ka_) * 4);
+        T.amv[u] = ldg<uint32_t>(vam, ((t << ashift) + ka_) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if ((B4 >> i) & 1) {
+          T.kc[u][i] = ldg_nt<uint32_t>(kc[i], t * (D / 2) + 4 * j);
+          T.vc[u][i] = ldg_nt<uint32_t>(vc[i], t * (D / 2) + 4 * j);
+        } else {
+          T.kc[u][i] = ldg_nt<uint32_t>(kc[i], t * (D / 4) + 4 * (j >> 1));
+          T.vc[u][i] = ldg_nt<uint32_t>(vc[i], t * (D / 4) + 4 * (j >> 1));
+        }
+        T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
+        T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
+        T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
+        T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
+      }
+    }
+  };
+
   // ---- prologue: queries of every loop in the pass -------------------------
+  // The query rows, the first token tile and the first tail rows are loaded
+  // before any of them is used, so their memory latencies overlap.  (The
+  // first tile is loaded even by a wave with no tile in the split: its token
+  // indices are clamped into the split.)
+  uint4 qraw[NSC];
+#pragma unroll
+  for (int s = 0; s < NSC; ++s)
+    qraw[s] = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+  int base = t_begin + wave * TILE;
+  Tile<TR, NRA, AQ> ta, tb;
+  load(ta, base);
+
+  // BF16 tail rows (a single-split launch attends them itself; otherwise the
+  // merge kernel does): each wave takes every W-th group of ROWS rows, TG
+  // groups per chunk, every loop slot's rows at once.  Slots whose loop is
+  // not asked for (chain links) have no tail.
+  constexpr int TG = 2;
+  uint4 tkw[TG][NSC], tvw[TG][NSC];
+  auto load_tail = [&](int t0) {
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      const uint32_t t = (uint32_t)min(t0 + g * W * ROWS + r, a.n_tail - 1);
+#pragma unroll
+      for (int s = 0; s < NSC; ++s) {
+        if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;
+        const size_t o = (size_t)bh * a.tcap * D;
+        tkw[g][s] = ldg_nt<uint4>(a.tk[s] + o, t * (2 * D) + 16 * j);
+        tvw[g][s] = ldg_nt<uint4>(a.tv[s] + o, t * (2 * D) + 16 * j);
+      }
+    }
+  };
+  if (a.tail_in) load_tail(wave * ROWS);
+
   // BF16 reference: its dots use the BF16 query pairs as stored (qb).
   // Code dots (residual loops, and with a quantized anchor the anchor too)
   // use q' = H_n q in FP32 (just q without rotation), each element
@@ -334,7 +402,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   float qr[NQR][8], sig[NQR];
 #pragma unroll
   for (int s = 0; s < NSC; ++s) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
+    const uint4 w = qraw[s];
     const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
     if constexpr (!AQ) {
 #pragma unroll
@@ -381,114 +449,70 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
     for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
   }
 
-  // ---- BF16 tail rows (a single-split launch attends them here; otherwise
-  // the merge kernel does).  They are the loop's own K and V in the original
-  // domain; each wave takes every W-th group of ROWS rows.  Scores use the
-  // BF16 query; values go to the accumulator the output is finished from:
-  // the reference sums (original domain) with a BF16 reference, or with a
-  // quantized anchor the code sums, which live in the rotated domain and
-  // carry the 2^(pos-24) code factors, so those rows enter as c H v times
-  // those factors (finish_row un-rotates them back).
+  // ---- the tail rows.  Scores use the BF16 query; values go to the
+  // accumulator the output is finished from: the reference sums (original
+  // domain) with a BF16 reference, or with a quantized anchor the code sums,
+  // which live in the rotated domain and carry the 2^(pos-24) code factors,
+  // so those rows enter as c H v times those factors (finish_row un-rotates
+  // them back).
   if (a.tail_in) {
+    for (int t0 = wave * ROWS; t0 < a.n_tail; t0 += TG * W * ROWS) {
+      if (t0 != wave * ROWS) load_tail(t0);
 #pragma unroll
-    for (int s = 0; s < NSC; ++s) {
-      if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;   // a chain link not asked for
-      const uint16_t *tk = a.tk[s] + (size_t)bh * a.tcap * D;
-      const uint16_t *tv = a.tv[s] + (size_t)bh * a.tcap * D;
-      uint32_t qw[4];
-      if constexpr (AQ == 0) {
+      for (int g = 0; g < TG; ++g) {
+        const bool valid = t0 + g * W * ROWS + r < a.n_tail;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) qw[p] = qb[s][p];
-      } else {
-        const uint4 w = *reinterpret_cast<const uint4 *>(a.q + ((size_t)a.qloop[s] * a.bh + bh) * D + 8 * j);
-        qw[0] = w.x; qw[1] = w.y; qw[2] = w.z; qw[3] = w.w;
-      }
-      for (int t0 = wave * ROWS; t0 < a.n_tail; t0 += W * ROWS) {
-        const uint32_t t = (uint32_t)min(t0 + r, a.n_tail - 1);
-        const uint4 kw = ldg_nt<uint4>(tk, t * (2 * D) + 16 * j);
-        const uint4 vw = ldg_nt<uint4>(tv, t * (2 * D) + 16 * j);
-        float dp = dot2bf0(qw[0], kw.x);
-        dp = dot2bf(qw[1], kw.y, dp);
-        dp = dot2bf(qw[2], kw.z, dp);
-        dp = dot2bf(qw[3], kw.w, dp);
-        const float tot = group_sum_dpp<LANES>(dp) * a.qscale;
-        const float sc = t0 + r < a.n_tail ? tot : -INFINITY;
-        if (sc > m[s]) {
-          const float f = fexp2(m[s] - sc);
-          m[s] = sc;
-          if (own == s) l_own *= f;
-          if (s >= OREF_FROM) {
+        for (int s = 0; s < NSC; ++s) {
+          if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;   // a chain link not asked for
+          const uint4 kw = tkw[g][s], vw = tvw[g][s], qw = qraw[s];
+          float dp = dot2bf0(qw.x, kw.x);
+          dp = dot2bf(qw.y, kw.y, dp);
+          dp = dot2bf(qw.z, kw.z, dp);
+          dp = dot2bf(qw.w, kw.w, dp);
+          const float tot = group_sum_dpp<LANES>(dp) * a.qscale;
+          const float sc = valid ? tot : -INFINITY;
+          if (sc > m[s]) {
+            const float f = fexp2(m[s] - sc);
+            m[s] = sc;
+            if (own == s) l_own *= f;
+            if (s >= OREF_FROM) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) oref[s][p] *= f;
-            if (AQ) zref *= f;
+              for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+              if (AQ) zref *= f;
+            }
+            if (s < NRS) {
+              zacc[s] *= f;
+#pragma unroll
+              for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+            }
           }
-          if (s < NRS) {
-            zacc[s] *= f;
+          const float pw = fexp2(sc - m[s]);
+          if (own == s) l_own += pw;
+          float y[8];
+          y[0] = bf16lo(vw.x); y[1] = bf16hi(vw.x);
+          y[2] = bf16lo(vw.y); y[3] = bf16hi(vw.y);
+          y[4] = bf16lo(vw.z); y[5] = bf16hi(vw.z);
+          y[6] = bf16lo(vw.w); y[7] = bf16hi(vw.w);
+          if constexpr (AQ == 0) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) ores[s][p] *= f;
-          }
-        }
-        const float pw = fexp2(sc - m[s]);
-        if (own == s) l_own += pw;
-        float y[8];
-        y[0] = bf16lo(vw.x); y[1] = bf16hi(vw.x);
-        y[2] = bf16lo(vw.y); y[3] = bf16hi(vw.y);
-        y[4] = bf16lo(vw.z); y[5] = bf16hi(vw.z);
-        y[6] = bf16lo(vw.w); y[7] = bf16hi(vw.w);
-        if constexpr (AQ == 0) {
+            for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pw, y[p], oref[s][p]);
+          } else {
+            if (a.rotate) {
+              wht8<D>(y, lane);
 #pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] = __builtin_fmaf(pw, y[p], oref[s][p]);
-        } else {
-          if (a.rotate) {
-            wht8<D>(y, lane);
+              for (int p = 0; p < 8; ++p) y[p] *= a.rot_c;
+            }
 #pragma unroll
-            for (int p = 0; p < 8; ++p) y[p] *= a.rot_c;
-          }
-#pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            const float yp = y[p] * (1.0f / (float)(1 << (24 - code_pos(p))));
-            if (s < NRS) ores[s][p] = __builtin_fmaf(pw, yp, ores[s][p]);
-            else oref[s][p] = __builtin_fmaf(pw, yp, oref[s][p]);
+            for (int p = 0; p < 8; ++p) {
+              const float yp = y[p] * (1.0f / (float)(1 << (24 - code_pos(p))));
+              if (s < NRS) ores[s][p] = __builtin_fmaf(pw, yp, ores[s][p]);
+              else oref[s][p] = __builtin_fmaf(pw, yp, oref[s][p]);
+            }
           }
         }
       }
     }
   }
-
-  auto load = [&](Tile<TR, NRA, AQ> &T, int base) {
-#pragma unroll
-    for (int u = 0; u < TR; ++u) {
-      const uint32_t t = (uint32_t)min(base + u * ROWS + r, t_end - 1);
-      if constexpr (AQ == 0) {
-        T.yk[u] = ldg_nt<uint4>(kref, t * (2 * D) + 16 * j);
-        T.yv[u] = ldg_nt<uint4>(vref, t * (2 * D) + 16 * j);
-      } else {
-        if constexpr (AINT4) {
-          T.ak[u] = ldg_nt<uint32_t>(kac, t * (D / 2) + 4 * j);
-          T.av[u] = ldg_nt<uint32_t>(vac, t * (D / 2) + 4 * j);
-        } else {
-          T.ak[u] = ldg_nt<uint32_t>(kac, t * (D / 4) + 4 * (j >> 1));
-          T.av[u] = ldg_nt<uint32_t>(vac, t * (D / 4) + 4 * (j >> 1));
-        }
-        T.amk[u] = ldg<uint32_t>(kam, ((t << ashift) + ka_) * 4);
-        T.amv[u] = ldg<uint32_t>(vam, ((t << ashift) + ka_) * 4);
-      }
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if ((B4 >> i) & 1) {
-          T.kc[u][i] = ldg_nt<uint32_t>(kc[i], t * (D / 2) + 4 * j);
-          T.vc[u][i] = ldg_nt<uint32_t>(vc[i], t * (D / 2) + 4 * j);
-        } else {
-          T.kc[u][i] = ldg_nt<uint32_t>(kc[i], t * (D / 4) + 4 * (j >> 1));
-          T.vc[u][i] = ldg_nt<uint32_t>(vc[i], t * (D / 4) + 4 * (j >> 1));
-        }
-        T.km[u][i] = ldg<uint32_t>(km[i], ((t << gshift) + k) * 4);
-        T.vm[u][i] = ldg<uint32_t>(vm[i], ((t << gshift) + k) * 4);
-        T.ka[u][i] = ldg<uint16_t>(ka[i], t * 2);
-        T.va[u][i] = ldg<uint16_t>(va[i], t * 2);
-      }
-    }
-  };
 
   auto process = [&](const Tile<TR, NRA, AQ> &T, int base, auto full_tile) {
     constexpr bool FULL = decltype(full_tile)::value;
@@ -654,10 +678,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // is processed.  The next tile is always loaded (its token indices clamped
   // into the split), so the loads are straight-line code and the wait before
   // processing a tile covers only that tile's loads.
-  int base = t_begin + wave * TILE;
   if (base < t_end) {
-    Tile<TR, NRA, AQ> ta, tb;
-    load(ta, base);
     while (true) {
       load(tb, base + STEP);
       if (base + TILE <= t_end) process(ta, base, std::true_type{});

@@ -145,11 +145,18 @@ def test_chain_parity(oracle, name, waves):
     tvb = np.stack([synth.bf16_bits(tl["v"][l]) for l in range(w.n_loops)])
     masks = [((1 << w.n_loops) - 1, 0, None), ((1 << w.n_loops) - 1, 2, "tail")]
     masks += [(1 << l, s, None) for l, s in zip(range(w.n_loops), [0, 1, 3, 0, 2, 1, 0, 1])]
+    # one loop with a tail whose other loops' planes are absent (NULL): a
+    # call for one loop along the chain must touch only that loop's tail
+    masks += [(1 << l, s, "own-tail") for l, s in zip(range(w.n_loops), [1, 2, 0, 1, 2, 0, 1, 2])]
     for mask, splits, tailed in masks:
         out = torch.full((w.n_loops, case.B, w.heads, w.d), float("nan"), device="cuda")
         ws = rq.workspace_for(case.lay, n, splits)
         if tailed:
-            rq.rq_decode_attn_tail(case.lay, case.k, case.v, tail, case.q, mask, n, scale, out, ws, splits)
+            tl_call = tail
+            if tailed == "own-tail":
+                tl_call = rq.Tail([t if (mask >> l) & 1 else None for l, t in enumerate(tail.k)],
+                                  [t if (mask >> l) & 1 else None for l, t in enumerate(tail.v)], tail.n)
+            rq.rq_decode_attn_tail(case.lay, case.k, case.v, tl_call, case.q, mask, n, scale, out, ws, splits)
             want = oracle.decode(lay, kp, vp, qb, mask, n, scale, tkb, tvb)
         else:
             rq.rq_decode_attn(case.lay, case.k, case.v, case.q, mask, n, scale, out, ws, splits)
