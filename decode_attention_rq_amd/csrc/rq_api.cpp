@@ -402,10 +402,14 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.tcap = tail ? tail->capacity : 0;
   a.out_mask = loop_mask;
   decode_waves(S, a.bh, &a.wide, &a.waves8);
-  // One split (or the wide form of two): the decode kernel attends the tail
-  // itself and finishes the rows.  Otherwise it writes split records, and
-  // the merge kernel merges them with the tail.
-  a.tail_in = (n_tail > 0 && (S == 1 || a.wide)) ? 1 : 0;
+  // The BF16 tail: with one workgroup per (b,h) (one split, or the wide
+  // form of two) the decode kernel attends it and finishes the rows.  With
+  // 8-wave splits (small batch) the first split attends it as more tokens of
+  // its own, and the merge kernel has no tail to walk (batch 1-2: 2-8%
+  // faster per call).  With 4-wave splits the first split's extra rows
+  // lengthened the step (batch 4-8: 1-3% slower), so the merge kernel walks
+  // the tail.  (A call over the tail alone runs the merge kernel only.)
+  a.tail_in = (n_tail > 0 && S > 0 && (S == 1 || a.wide || a.waves8)) ? 1 : 0;
   a.records = (S > 1 && !a.wide) ? 1 : 0;
   a.group = L->group;
   a.rotate = L->rotate;

@@ -369,10 +369,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   Tile<TR, NRA, AQ> ta, tb;
   load(ta, base);
 
-  // BF16 tail rows (a single-split launch attends them itself; otherwise the
-  // merge kernel does): each wave takes every W-th group of ROWS rows, TG
-  // groups per chunk, every loop slot's rows at once.  Slots whose loop is
-  // not asked for (chain links) have no tail.
+  // BF16 tail rows (the first split's workgroup attends them, as more tokens
+  // of its split): each wave takes every W-th group of ROWS rows, TG groups
+  // per chunk, every loop slot's rows at once.  Slots whose loop is not asked
+  // for (chain links) have no tail.
   constexpr int TG = 2;
   uint4 tkw[TG][NSC], tvw[TG][NSC];
   auto load_tail = [&](int t0) {
@@ -388,7 +388,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       }
     }
   };
-  if (a.tail_in) load_tail(wave * ROWS);
+  const bool tail_here = a.tail_in && split == 0;
+  if (tail_here) load_tail(wave * ROWS);
 
   // BF16 reference: its dots use the BF16 query pairs as stored (qb).
   // Code dots (residual loops, and with a quantized anchor the anchor too)
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // which live in the rotated domain and carry the 2^(pos-24) code factors,
   // so those rows enter as c H v times those factors (finish_row un-rotates
   // them back).
-  if (a.tail_in) {
+  if (tail_here) {
     for (int t0 = wave * ROWS; t0 < a.n_tail; t0 += TG * W * ROWS) {
       if (t0 != wave * ROWS) load_tail(t0);
 #pragma unroll
@@ -799,8 +800,10 @@ static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<D, NR, REF, B4, TR, kWaves, AQ, CHAIN>), grid, dim3(64 * kWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
-  if constexpr (CHAIN == 2) return launch_merge(a, D, 1, 1, st);
-  return launch_merge(a, D, NR, NR + (REF ? 1 : 0), st);
+  DecodeArgs m = a;
+  if (a.tail_in) m.n_tail = 0;        // already in the first split's records
+  if constexpr (CHAIN == 2) return launch_merge(m, D, 1, 1, st);
+  return launch_merge(m, D, NR, NR + (REF ? 1 : 0), st);
 }
 
 // Bit widths of the pass's residual loops as a mask (bit i: loop i is INT4).
