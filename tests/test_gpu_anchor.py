@@ -134,6 +134,10 @@ DECODE_CASES = {
     "norot-g32-a4-tail": (_w(g=32, rotate=0), 300, 0b1011, 5, [0, 1]),
     "d64-a2g16-mixed": (_w(d=64, ga=16, abits=2, bits=(4, 2)), 333, 0b111, 3, [0, 2]),
     "d256-a4g16": (_w(d=256, g=32, ga=16, bits=(2,)), 260, 0b11, 2, [0, 1]),
+    # a tail longer than one batch of tail loads of every workgroup shape
+    # (8 waves x 4 rows x 2 groups = 64 rows), ragged, per loop and fused
+    "long-tail-perloop": (_w(), 400, 0b0100, 150, [0, 1, 2, 3]),
+    "long-tail-fused": (_w(), 400, 0b1111, 139, [0, 1, 2]),
 }
 
 
@@ -159,16 +163,18 @@ def test_tail_alone(oracle, anchored):
     _check(oracle, case, got, 0b1111, 0, tk, tv)
 
 
-def test_bf16_reference_with_tail(oracle):
-    """The tail works with the BF16 reference too (one-token tail: the current
-    token of a looped model's earlier loops)."""
+@pytest.mark.parametrize("T,mask", [(1, 0b0111), (97, 0b1111), (97, 0b0010)])
+def test_bf16_reference_with_tail(oracle, waves, T, mask):
+    """The tail works with the BF16 reference too: a one-token tail (the
+    current token of a looped model's earlier loops), and a ragged tail longer
+    than one batch of tail loads, fused and per loop."""
     w = synth.Workload("b", n_loops=4, batch=2, heads=3, d=128, g=32, n_ctx=0, bits=[2, 4, 2],
                        c=[0.8, 0.85, 0.9], sigma=[0.15, 0.12, 0.1], rotate=1, seed=44)
     case = Case(w, 500, cap=512)
-    tk, tv = _tail(w, case.B, 1)
-    for s in (0, 1, 3):
-        got = _run(case, 0b0111, 500, tk, tv, 1, splits=s)
-        _check(oracle, case, got, 0b0111, 500, tk, tv)
+    tk, tv = _tail(w, case.B, T)
+    for s in (0, 1, 2, 3):
+        got = _run(case, mask, 500, tk, tv, T, splits=s)
+        _check(oracle, case, got, mask, 500, tk, tv)
 
 
 def test_tail_of_zero_tokens_is_plain_decode():
