@@ -12,8 +12,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("d,n,cap,mask,splits", [(128, 700, 768, 0b1111, 0), (128, 700, 768, 0b0110, 3),
-                                                  (64, 129, 129, 0b11, 1), (256, 90, 96, 0b101, 2)])
-def test_bf16_baseline(oracle, d, n, cap, mask, splits):
+                                                  (128, 700, 768, 0b1001, 2), (64, 129, 129, 0b11, 1),
+                                                  (256, 90, 96, 0b101, 2)])
+def test_bf16_baseline(oracle, waves, d, n, cap, mask, splits):
     import decode_attention_rq_amd as rq
     L = 4 if d != 64 else 2
     B, H = 2, 3
