@@ -239,8 +239,9 @@ typedef struct {
  *   tail       NULL or a tail; tail->n == 0 makes this call rq_decode_attn
  *   n_ctx      0 <= n_ctx <= capacity, n_ctx + tail->n >= 1 (n_ctx = 0: the
  *              tail alone; no cache plane is read)
- * The tail is meant for tens of tokens: the split-merge step attends over it,
- * four waves per (b, h, loop).
+ * The tail is meant for tens of tokens: it is attended by one workgroup per
+ * (b, h) (the first split's, or the merge step's, four waves per (b, h,
+ * loop)), not spread over the splits.
  */
 rq_status rq_decode_attn_tail(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
                               const rq_tail *tail, const void *q, uint32_t loop_mask,
