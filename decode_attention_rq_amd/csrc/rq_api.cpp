@@ -52,6 +52,11 @@ rq_status check_layout(const rq_layout *L) {
   return RQ_OK;
 }
 
+// The decode kernels address one (batch, head)'s rows of a plane with 32-bit
+// byte offsets; the widest row is a BF16 row of 2*head_dim bytes, so the
+// largest offset read is below capacity * 2 * head_dim.
+bool rows_fit_u32(int64_t capacity, int head_dim) { return capacity * 2 * head_dim <= ((int64_t)1 << 32); }
+
 int anchor_group(const rq_layout *L) { return L->ref_group ? L->ref_group : L->group; }
 
 // Loops per anchor group, the anchor (reference) loop of loop l's group, and
@@ -350,6 +355,8 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   if (tail && (tail->n < 0 || tail->capacity < tail->n)) return RQ_ERR_INVALID_ARG;
   if (n_ctx < 0 || n_ctx > L->capacity || (int64_t)n_ctx + n_tail < 1) return RQ_ERR_INVALID_ARG;
   if (n_tail > 0 && (int64_t)L->batch * L->n_heads * tail->capacity > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (!rows_fit_u32(L->capacity, L->head_dim) || (n_tail > 0 && !rows_fit_u32(tail->capacity, L->head_dim)))
+    return RQ_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
   if (n_splits < 0 || (n_ctx > 0 && n_splits > n_ctx)) return RQ_ERR_INVALID_ARG;
   for (int l = 0; l < L->n_loops; ++l) {
@@ -526,6 +533,7 @@ rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *co
   if (n_ctx < 1 || n_ctx > L->capacity) return RQ_ERR_INVALID_ARG;
   if (!std::isfinite(sm_scale)) return RQ_ERR_INVALID_ARG;
   if (n_splits < 0 || n_splits > n_ctx) return RQ_ERR_INVALID_ARG;
+  if (!rows_fit_u32(L->capacity, L->head_dim)) return RQ_ERR_UNSUPPORTED;
   for (int l = 0; l < L->n_loops; ++l)
     if (((loop_mask >> l) & 1u) && (!aligned16(k_loops[l]) || !aligned16(v_loops[l])))
       return RQ_ERR_INVALID_ARG;

@@ -64,7 +64,9 @@ extern "C" {
 typedef enum {
     RQ_OK = 0,
     RQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad range, empty mask */
-    RQ_ERR_UNSUPPORTED = -2,  /* head_dim, group, bits or loop count outside the supported set */
+    RQ_ERR_UNSUPPORTED = -2,  /* head_dim, group, bits or loop count outside the supported set;
+                                 decode: capacity * 2 * head_dim above 2^32 bytes (per
+                                 (b, h) plane offsets are 32-bit), likewise a tail's capacity */
     RQ_ERR_WORKSPACE = -3,    /* decode workspace smaller than rq_decode_workspace_bytes */
     RQ_ERR_DEVICE = -4        /* a HIP call or kernel launch reported an error */
 } rq_status;

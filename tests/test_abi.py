@@ -162,6 +162,23 @@ def test_decode_only_checks_planes_of_masked_loops(rq):
     assert _decode(rq, lay, mask=0b1101, k=k, ws_bytes=1) == WORKSPACE
 
 
+def test_decode_rows_must_fit_32bit_offsets(rq):
+    """A (batch, head)'s rows of a plane are addressed with 32-bit byte offsets:
+    capacity * 2 * head_dim may reach 2^32 bytes, not more (cache and tail)."""
+    edge = 1 << 23                                   # * 2 * 256 = 2^32
+    # at the limit the checks pass (a too-small workspace is reported next)
+    assert _decode(rq, _layout(rq, head_dim=256, capacity=edge), ws_bytes=1) == WORKSPACE
+    assert _decode(rq, _layout(rq, head_dim=256, capacity=edge + 1)) == UNSUPPORTED
+    assert _decode(rq, _layout(rq, head_dim=128, capacity=2 * edge + 1)) == UNSUPPORTED
+    lay = _layout(rq, head_dim=256)
+    assert _decode_tail(rq, lay, _tail(rq, cap=edge), ws_bytes=1) == WORKSPACE
+    assert _decode_tail(rq, lay, _tail(rq, cap=edge + 1)) == UNSUPPORTED
+    planes = (C.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    big = _layout(rq, head_dim=256, capacity=edge + 1).c()
+    assert rq._lib.rq_bf16_decode_attn(C.byref(big), planes, planes, FAKE, 1, 32, 0.1, 2, FAKE, FAKE,
+                                       1 << 30, None) == UNSUPPORTED
+
+
 def test_workspace_size_formula(rq):
     lay = _layout(rq).c()
     # 2 splits * 4 slots * (2*2) (b,h) * (2*128+2) floats
