@@ -288,19 +288,34 @@ def append_bench(args, w):
     out = torch.empty(w.n_loops, w.batch, w.heads, w.d, device=dev)
     ws = rq.workspace_for(lay, cap, rq.rq_decode_splits(lay, cap), dev)
     scale = 1.0 / np.sqrt(w.d)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for s_ in range(steps):
+    def append_step(s_):
         t = n0 + s_
-        ev[s_][0].record()
         rq.rq_encode(lay, k, v, step_in[s_][0], step_in[s_][1], t, 1)
+        return t
+
+    # The step rate: two events around the steps (an event marker between two
+    # kernels idles the GPU for ~5 us).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for s_ in range(steps):
+        t = append_step(s_)
+        rq.rq_decode_attn(lay, k, v, q, mask, t + 1, scale, out, ws, rq.rq_decode_splits(lay, t + 1))
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    # The same steps again (each append rewrites its slot with the same bytes)
+    # with events between the phases: the append and decode durations.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s_ in range(steps):
+        ev[s_][0].record()
+        t = append_step(s_)
         ev[s_][1].record()
         rq.rq_decode_attn(lay, k, v, q, mask, t + 1, scale, out, ws, rq.rq_decode_splits(lay, t + 1))
         ev[s_][2].record()
     torch.cuda.synchronize()
     enc_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
     per_tok = layout_bytes_per_token(w.n_loops, w.bits, w.g, w.d)
     dec_bytes = w.batch * w.heads * (n0 + steps / 2) * per_tok
     res = {"metric": "decode tokens/s with one-token append per step, mixed INT4/INT2 residual KV, 8k ctx",
@@ -537,22 +552,38 @@ def anchor_bench(args, w):
         for l in range(L):
             rq.rq_decode_attn_tail(lay, k, v, tail, q, 1 << l, n, scale, out, ws, splits)
 
+    def call(i, l):
+        k, v, tail, q = reps[i % len(reps)]
+        rq.rq_decode_attn_tail(lay, k, v, tail, q, 1 << l, n, scale, out, ws, splits)
+
     steps = args.steps
     for i in range(args.warmup):
         step(i)
+    # The step rate: two events around the steps (an event marker between two
+    # kernels idles the GPU for ~5 us, so the calls are not timed one by one
+    # here).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    # per-call events: the residual-loop calls are the dominant kernel
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(steps)]
+    e0.record()
     for i in range(steps):
-        k, v, tail, q = reps[i % len(reps)]
-        ev[i][0].record()
-        for l in range(L):
-            rq.rq_decode_attn_tail(lay, k, v, tail, q, 1 << l, n, scale, out, ws, splits)
-            ev[i][l + 1].record()
+        step(i)
+    e1.record()
     torch.cuda.synchronize()
-    call_ms = np.array([[ev[i][l].elapsed_time(ev[i][l + 1]) for l in range(L)] for i in range(steps)])
-    span_ms = ev[0][0].elapsed_time(ev[-1][L])
+    span_ms = e0.elapsed_time(e1)
     ms = span_ms / steps
+    # The calls of each loop on their own, back to back (same events): the
+    # mean duration of a residual loop's call, the dominant kernel, and of
+    # the anchor loop's call.
+    call_ms = np.zeros((1, L))
+    for l in range(L):
+        for i in range(3):
+            call(i, l)
+        e0.record()
+        for i in range(steps):
+            call(i, l)
+        e1.record()
+        torch.cuda.synchronize()
+        call_ms[0, l] = e0.elapsed_time(e1) / steps
     tail_bytes = B * H * T * 2 * d * 2
     anchor_tok = 2 * (d * w.ref_bits // 8 + 4 * (d // w.ref_group))
     res_tok = 2 * (d * w.bits[0] // 8 + 4 * (d // w.g) + 2)
