@@ -81,6 +81,108 @@ __device__ __forceinline__ void fwht32(float (&v)[EPL], int lane) {
   }
 }
 
+// One cross-lane stage of the sign-folded transform at lane distance M (1 or
+// 2): w = dpp(w) * s + w for every value, one v_fmac_f32 with a DPP source
+// each (s = -1 on the lane whose bit M is set, +1 on its partner; the
+// product is exact, so the sum is rounded once, as an add).  Written as
+// assembly because the compiler does not combine a lane move into an FMA.
+// Each block begins with two wait states (a DPP instruction must not read a
+// register the previous VALU instruction wrote); inside a block every
+// instruction reads only its own value, written before the block.
+template <int M>
+__device__ __forceinline__ void fmac_dpp_stage(float (&v)[EPL], float s) {
+  static_assert(M == 1 || M == 2, "quad_perm lane distances");
+#pragma unroll
+  for (int o = 0; o < EPL; o += 16) {
+    if constexpr (M == 1) {
+      asm volatile(
+        "s_nop 1\n"
+        "v_fmac_f32_dpp %0, %0, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %1, %1, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %2, %2, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %3, %3, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %4, %4, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %5, %5, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %6, %6, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %7, %7, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %8, %8, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %9, %9, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %10, %10, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %11, %11, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %12, %12, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %13, %13, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %14, %14, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %15, %15, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        : "+v"(v[o + 0]), "+v"(v[o + 1]), "+v"(v[o + 2]), "+v"(v[o + 3]), "+v"(v[o + 4]), "+v"(v[o + 5]), "+v"(v[o + 6]), "+v"(v[o + 7]), "+v"(v[o + 8]), "+v"(v[o + 9]), "+v"(v[o + 10]), "+v"(v[o + 11]), "+v"(v[o + 12]), "+v"(v[o + 13]), "+v"(v[o + 14]), "+v"(v[o + 15])
+        : "v"(s));
+    } else {
+      asm volatile(
+        "s_nop 1\n"
+        "v_fmac_f32_dpp %0, %0, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %1, %1, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %2, %2, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %3, %3, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %4, %4, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %5, %5, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %6, %6, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %7, %7, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %8, %8, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %9, %9, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %10, %10, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %11, %11, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %12, %12, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %13, %13, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %14, %14, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %15, %15, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        : "+v"(v[o + 0]), "+v"(v[o + 1]), "+v"(v[o + 2]), "+v"(v[o + 3]), "+v"(v[o + 4]), "+v"(v[o + 5]), "+v"(v[o + 6]), "+v"(v[o + 7]), "+v"(v[o + 8]), "+v"(v[o + 9]), "+v"(v[o + 10]), "+v"(v[o + 11]), "+v"(v[o + 12]), "+v"(v[o + 13]), "+v"(v[o + 14]), "+v"(v[o + 15])
+        : "v"(s));
+    }
+  }
+}
+
+// The same transform with the partner's value entering each cross-lane
+// stage multiplied by s, the lane's own as is (lane distances 1 and 2 as
+// above, 4 through the lane moves of xor_lane).  The lane whose bit of the
+// stage is set then holds its butterfly output negated (partner - own =
+// -(own's output), rounded alike), and later stages keep that sign, since
+// both lanes of a pair carry the same one.  Returns the lane's resulting
+// sign (+-1) for the caller to fold into its scaling.  A zero may come out
+// with the other sign, so only a caller that turns zeros into +0 afterwards
+// may use it.
+template <int LANES>
+__device__ __forceinline__ float fwht32_signed(float (&v)[EPL], int lane) {
+#pragma unroll
+  for (int h = 1; h < EPL; h *= 2) {
+#pragma unroll
+    for (int j = 0; j < EPL; j += 2 * h) {
+#pragma unroll
+      for (int i = j; i < j + h; ++i) {
+        const float x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+  }
+  float sign = 1.0f;
+  if constexpr (LANES >= 2) {
+    const float s = (lane & 1) ? -1.0f : 1.0f;
+    fmac_dpp_stage<1>(v, s);
+    sign *= s;
+  }
+  if constexpr (LANES >= 4) {
+    const float s = (lane & 2) ? -1.0f : 1.0f;
+    fmac_dpp_stage<2>(v, s);
+    sign *= s;
+  }
+  if constexpr (LANES >= 8) {
+    const float s = (lane & 4) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int p = 0; p < EPL; ++p) v[p] = __builtin_fmaf(xor_lane<4>(v[p]), s, v[p]);
+    sign *= s;
+  }
+  return sign;
+}
+
 // Raw buffer access: a wave-uniform base address and byte count in SGPRs, a
 // 32-bit byte offset per lane (no 64-bit address registers).  Accesses at or
 // beyond the byte count are dropped by the hardware (loads return 0).  Word 3
@@ -113,9 +215,9 @@ __device__ __forceinline__ void unpack_raw32(const u32x4_t (&w)[EPL / 8], float 
 template <int LANES>
 __device__ __forceinline__ void rotate_canonical(float (&v)[EPL], int rotate, float rot_c, int lane) {
   if (rotate) {
-    fwht32<LANES>(v, lane);
+    const float c = rot_c * fwht32_signed<LANES>(v, lane);   // exact: the sign is +-1
 #pragma unroll
-    for (int p = 0; p < EPL; ++p) v[p] = __builtin_fmaf(v[p], rot_c, 0.0f);
+    for (int p = 0; p < EPL; ++p) v[p] = __builtin_fmaf(v[p], c, 0.0f);
   } else {
 #pragma unroll
     for (int p = 0; p < EPL; ++p) v[p] = v[p] + 0.0f;
