@@ -56,31 +56,6 @@ __device__ __forceinline__ float dot_sum32(const float (&a)[EPL], const float (&
   return (bs[0] + bs[2]) + (bs[1] + bs[3]);
 }
 
-// Unnormalized Walsh-Hadamard transform of the vector: butterflies
-// h = 1, ..., 16 inside the lane, then h = 32, 64, 128 across lanes at lane
-// distances 1, 2, 4, ascending as in the sequential definition.
-template <int LANES>
-__device__ __forceinline__ void fwht32(float (&v)[EPL], int lane) {
-#pragma unroll
-  for (int h = 1; h < EPL; h *= 2) {
-#pragma unroll
-    for (int j = 0; j < EPL; j += 2 * h) {
-#pragma unroll
-      for (int i = j; i < j + h; ++i) {
-        const float x = v[i], y = v[i + h];
-        v[i] = x + y;
-        v[i + h] = x - y;
-      }
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < EPL; ++p) {
-    if constexpr (LANES >= 2) v[p] = wht_stage<1>(v[p], lane);
-    if constexpr (LANES >= 4) v[p] = wht_stage<2>(v[p], lane);
-    if constexpr (LANES >= 8) v[p] = wht_stage<4>(v[p], lane);
-  }
-}
-
 // One cross-lane stage of the sign-folded transform at lane distance M (1 or
 // 2): w = dpp(w) * s + w for every value, one v_fmac_f32 with a DPP source
 // each (s = -1 on the lane whose bit M is set, +1 on its partner; the
@@ -140,9 +115,13 @@ __device__ __forceinline__ void fmac_dpp_stage(float (&v)[EPL], float s) {
   }
 }
 
-// The same transform with the partner's value entering each cross-lane
-// stage multiplied by s, the lane's own as is (lane distances 1 and 2 as
-// above, 4 through the lane moves of xor_lane).  The lane whose bit of the
+// Unnormalized Walsh-Hadamard transform of the vector: butterflies
+// h = 1, ..., 16 inside the lane, then h = 32, 64, 128 across lanes at lane
+// distances 1, 2, 4, ascending as in the sequential definition.  In each
+// cross-lane stage the partner's value enters multiplied by s, the lane's
+// own as is (lane distances 1 and 2 as above, 4 through the lane moves of
+// xor_lane), instead of flipping the sign of the own value on the lane that
+// subtracts (one instruction per value, not two).  The lane whose bit of the
 // stage is set then holds its butterfly output negated (partner - own =
 // -(own's output), rounded alike), and later stages keep that sign, since
 // both lanes of a pair carry the same one.  Returns the lane's resulting
@@ -207,6 +186,19 @@ __device__ __forceinline__ void unpack_raw32(const u32x4_t (&w)[EPL / 8], float 
       f[8 * k + 2 * e + 1] = bf16hi(w[k][e]);
     }
   }
+}
+
+// c * H v for a reconstruction (the dequantized anchor, a chain link's
+// residual).  Its inputs fma(code, s, z) are never -0 (code, s >= 0 and z is
+// the min of values whose zeros are +0), so every zero of the sequential
+// transform, and of its product with c > 0, is +0; the sign-folded transform
+// followed by fma(v, +-c, +0), which turns any zero into +0, therefore gives
+// the same bits.
+template <int LANES>
+__device__ __forceinline__ void rotate_rebuilt(float (&v)[EPL], float rot_c, int lane) {
+  const float c = rot_c * fwht32_signed<LANES>(v, lane);
+#pragma unroll
+  for (int p = 0; p < EPL; ++p) v[p] = __builtin_fmaf(v[p], c, 0.0f);
 }
 
 // The values a group quantizer sees: c * H u when rotating, u otherwise, with
@@ -359,11 +351,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   if (a.abits != 0) {
     rotate_canonical<LANES>(y, a.rotate, a.rot_c, lane);
     quantize_loop<D, true>(y, a.abits, a.agroup, S.codes[a.n_res], S.meta[a.n_res], row0, nw, tok, j, valid);
-    if (a.rotate) {
-      fwht32<LANES>(y, lane);
-#pragma unroll
-      for (int p = 0; p < EPL; ++p) y[p] = y[p] * a.rot_c;
-    }
+    if (a.rotate) rotate_rebuilt<LANES>(y, a.rot_c, lane);
   }
   float den = dot_sum32<LANES>(y, y);                // exact products for a BF16 y
 
@@ -395,11 +383,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, plane(S.alpha[l] + row0, (uint32_t)nw * 2), 2 * tok, 0, 0);
     if (link) {
       // chained references: y <- fma(alpha, y, r_hat), r_hat = c * H(fma(code, s, z))
-      if (a.rotate) {
-        fwht32<LANES>(x, lane);
-#pragma unroll
-        for (int p = 0; p < EPL; ++p) x[p] = x[p] * a.rot_c;
-      }
+      if (a.rotate) rotate_rebuilt<LANES>(x, a.rot_c, lane);
 #pragma unroll
       for (int p = 0; p < EPL; ++p) y[p] = __builtin_fmaf(af, y[p], x[p]);
       den = dot_sum32<LANES>(y, y);

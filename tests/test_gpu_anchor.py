@@ -77,6 +77,50 @@ def test_anchored_reconstruct(oracle, name):
         assert np.all(err <= REC_TOL * s), (l, float((err / np.maximum(REC_TOL * s, 1e-30)).max()))
 
 
+@pytest.mark.parametrize("chain", [0, 1])
+def test_zero_signs_of_rebuilt_references(oracle, chain):
+    """References rebuilt from codes (the dequantized, rotated INT4 anchor; a
+    chain link) with exact zeros: a one-hot anchor row rotates to a constant
+    group, which dequantizes to its offset, which rebuilds to one non-zero
+    entry and zeros.  Loops of signed zeros against it make every product of
+    alpha's numerator a zero whose sign depends on those zeros, so the stored
+    alpha (FP16 +0 or -0) shows whether the rebuilt reference's zeros match
+    the oracle's, bit for bit."""
+    import decode_attention_rq_amd as rq
+    from rq_testutil import encoder_input
+    w = _w(B=1, H=2, bits=(2, 2, 2))
+    if chain:
+        w = synth.Workload(w.name, n_loops=w.n_loops, batch=1, heads=2, d=w.d, g=w.g, n_ctx=0, bits=w.bits,
+                           c=w.c, sigma=w.sigma, rotate=1, seed=w.seed, ref_bits=4, ref_group=32, ref_chain=1)
+    n = 12
+    case = Case(w, n, cap=n)
+    for side in ("k", "v"):
+        ref, loops = case.data[side + "_ref"], case.data[side + "_loops"]
+        for t, (dim, val, zero) in enumerate([(0, 1.0, -0.0), (5, -1.0, 0.0), (64, 2.0, -0.0), (127, 0.5, 0.0)]):
+            ref[:, :, t] = 0.0                 # one-hot: rebuilds to one non-zero entry and zeros
+            ref[:, :, t, dim] = val
+            loops[:, :, :, t] = zero           # every product of alpha's numerator a signed zero
+        ref[:, :, 4] = 0.0                     # an all-zero anchor row (alpha's denominator 0)
+        loops[:, :, :, 4] = -0.0
+        loops[:, :, 1, 5] = -0.0               # one loop of -0 against a random anchor row
+    kin = encoder_input(w, case.data["k_loops"], case.data["k_ref"]).cuda().contiguous()
+    vin = encoder_input(w, case.data["v_loops"], case.data["v_ref"]).cuda().contiguous()
+    rq.rq_encode(case.lay, case.k, case.v, kin, vin, 0, n)
+    torch.cuda.synchronize()
+    _, kp, vp, _ = case.oracle_planes(oracle)
+    for side, planes in (("k", kp), ("v", vp)):
+        gc = getattr(case, side)
+        for l in range(w.n_loops):
+            names = ("codes", "meta") + (("alpha",) if l < w.n_loops - 1 else ())
+            for nm in names:
+                got = plane_bits(getattr(gc, nm)[l])[:, :, :n]
+                want = getattr(planes, nm)[l][:, :, :n]
+                assert np.array_equal(got, want), (side, l, nm)
+        # the case is not vacuous: some stored alpha is a negative zero
+        if not chain:
+            assert (plane_bits(gc.alpha[0])[:, :, 0] == 0x8000).any()
+
+
 def _tail(w, B, T, seed=3):
     if T == 0:
         return None, None
