@@ -20,10 +20,12 @@
 // lane, ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane
 // reads ROWS consecutive reference rows, and every loop of the pass shares
 // that load.  Online softmax per (row, loop) in the exp2 domain; rows, then
-// waves (through LDS), are merged by log-sum-exp.  With one split the
-// workgroup finishes the output itself (un-rotation of the residual
-// accumulator, normalisation); with several it writes one record per (split,
-// loop, batch*head) to the workspace and kernel M merges the records.
+// waves (through LDS), are merged by log-sum-exp.  The first split may also
+// attend the BF16 tail rows.  With one split the workgroup finishes the
+// output itself (un-rotation of the residual accumulator, normalisation);
+// with several it writes one record per (split, loop, batch*head) to the
+// workspace and kernel M merges the records (and the tail, if the first
+// split did not take it).
 
 #pragma once
 
