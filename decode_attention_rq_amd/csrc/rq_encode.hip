@@ -315,8 +315,10 @@ __device__ __forceinline__ void quantize_loop(float (&u)[EPL], int bits, int gro
 // is a buffer at the wave's first token addressed by 32-bit lane offsets;
 // the next loop's input is loaded while the current loop is quantized.
 // About 140 VGPRs: three waves per SIMD (forcing four spills y and runs
-// slower).
-template <int D>
+// slower).  CHAIN (chained references) is a template parameter: without it
+// y is fixed over the loops, and the loop carries no copies of it around
+// its back edge.
+template <int D, bool CHAIN>
 __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   constexpr int LANES = D / EPL;
   constexpr int VPW = kWave / LANES;
@@ -358,7 +360,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   for (int l = 0; l < a.n_res; ++l) {
     float x[EPL];
     unpack_raw32(raw, x);
-    if (l + 1 < a.n_res) load_raw32(input(l + 1), xoff, raw);
+    // the next loop's rows; after the last loop a zero-length buffer (the
+    // loads return zeros and touch no memory), so that the prefetch buffer is
+    // written on every iteration and needs no register copies across the
+    // loop's back edge
+    load_raw32(plane(S.xin[min(l + 1, a.n_res - 1)] + xrow0 * D, l + 1 < a.n_res ? rows : 0u), xoff, raw);
     float alpha32;
     if (a.alpha_mode == 1) {
       alpha32 = 1.0f;
@@ -374,19 +380,21 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 #pragma unroll
     for (int p = 0; p < EPL; ++p) x[p] = __builtin_fmaf(-af, y[p], x[p]);
     rotate_canonical<LANES>(x, a.rotate, a.rot_c, lane);
-    const bool link = a.chain && l + 1 < a.n_res;     // the next loop refers to this one
+    const bool link = CHAIN && l + 1 < a.n_res;       // the next loop refers to this one
     if (link)
       quantize_loop<D, true>(x, a.bits[l], a.group, S.codes[l], S.meta[l], row0, nw, tok, j, valid);
     else
       quantize_loop<D, false>(x, a.bits[l], a.group, S.codes[l], S.meta[l], row0, nw, tok, j, valid);
     if (valid && j == 0)
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, plane(S.alpha[l] + row0, (uint32_t)nw * 2), 2 * tok, 0, 0);
-    if (link) {
-      // chained references: y <- fma(alpha, y, r_hat), r_hat = c * H(fma(code, s, z))
-      if (a.rotate) rotate_rebuilt<LANES>(x, a.rot_c, lane);
+    if constexpr (CHAIN) {
+      if (link) {
+        // chained references: y <- fma(alpha, y, r_hat), r_hat = c * H(fma(code, s, z))
+        if (a.rotate) rotate_rebuilt<LANES>(x, a.rot_c, lane);
 #pragma unroll
-      for (int p = 0; p < EPL; ++p) y[p] = __builtin_fmaf(af, y[p], x[p]);
-      den = dot_sum32<LANES>(y, y);
+        for (int p = 0; p < EPL; ++p) y[p] = __builtin_fmaf(af, y[p], x[p]);
+        den = dot_sum32<LANES>(y, y);
+      }
     }
   }
 }
@@ -395,9 +403,18 @@ hipError_t launch_encode(const EncodeArgs &a, int head_dim, hipStream_t s) {
   const int tasks = 2 * a.tasks_per_side;
   const dim3 grid((tasks + 3) / 4), block(256);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL(encode_kernel<256>, grid, block, 0, s, a); break;
+    case 64:
+      if (a.chain) hipLaunchKernelGGL((encode_kernel<64, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((encode_kernel<64, false>), grid, block, 0, s, a);
+      break;
+    case 128:
+      if (a.chain) hipLaunchKernelGGL((encode_kernel<128, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((encode_kernel<128, false>), grid, block, 0, s, a);
+      break;
+    case 256:
+      if (a.chain) hipLaunchKernelGGL((encode_kernel<256, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((encode_kernel<256, false>), grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
