@@ -247,7 +247,7 @@ def timed_graph(fn, steps, warmup):
 
 def append_bench(args, w):
     """Mixed-precision 8k workload: rq_encode prefill of 8192 tokens (mean of
-    three timed calls after an untimed one), then `steps` append steps, each
+    three timed calls after three untimed ones), then `steps` append steps, each
     rq_encode of one new token per (batch, head, loop) plus rq_decode_attn
     over the n+1 tokens.  The
     reference slots (the final loop's own KV write) are in place beforehand."""
@@ -269,9 +269,11 @@ def append_bench(args, w):
     step_in = [(kin[:, :, :, t:t + 1].contiguous(), vin[:, :, :, t:t + 1].contiguous()) for t in range(n0, cap)]
     del data, kin, vin
     torch.cuda.empty_cache()
-    # prefill: one untimed encode of all n0 tokens, then the mean of three
+    # prefill: three untimed encodes of all n0 tokens (~12 ms: from idle the
+    # GPU's clocks take ~10 ms of work to settle), then the mean of three
     # timed ones (each writes the same slots with the same values)
-    rq.rq_encode(lay, k, v, pre_k, pre_v, 0, n0)
+    for _ in range(3):
+        rq.rq_encode(lay, k, v, pre_k, pre_v, 0, n0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
