@@ -216,10 +216,13 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def timed_graph(fn, steps, warmup):
+def timed_graph(fn, steps, warmup, settle_ms=20.0):
     """Mean ms per step of fn, captured once into a HIP graph (torch's
     CUDAGraph on the current stream) and replayed `steps` times after
-    `warmup` replays; HIP events bracket the replays."""
+    `warmup` replays, and after as many more as make ~settle_ms of work (the
+    GPU's clocks take ~10 ms of work to settle after the idle of a capture;
+    short steps would otherwise be timed on the ramp); HIP events bracket the
+    replays."""
     import torch
     fn(0)
     torch.cuda.synchronize()
@@ -232,10 +235,16 @@ def timed_graph(fn, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(warmup):
         g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = max(e0.elapsed_time(e1) / max(warmup, 1), 1e-3)
+    for i in range(min(500, int(settle_ms / per))):
+        g.replay()
+    torch.cuda.synchronize()
     e0.record()
     for i in range(steps):
         g.replay()
