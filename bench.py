@@ -8,8 +8,9 @@ synthetic KV already encoded in HBM.  Two cache replicas alternate so that
 consecutive steps cannot be served from the 256 MB Infinity Cache.
 
 Prints one JSON line: decode tokens/s (batch / step time), the roofline of the
-decode kernel (algorithmic bytes / per-launch time from HIP events), and the
-CPU oracle timed on a bounded sample of the same step.
+decode kernel (algorithmic bytes / mean launch time, from two HIP events on
+the launch stream around the timed steps), and the CPU oracle timed on a
+bounded sample of the same step.
 """
 from __future__ import annotations
 
