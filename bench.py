@@ -25,28 +25,42 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+SETTLE_MS = 25.0        # untimed work before every timed measurement (see parse)
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
-    # From idle the GPU's clocks take ~30 back-to-back decode steps (~9 ms) to
-    # settle (kernel traces show the first steps up to 30% slower), so the
-    # default warm-up covers that before the timed steps.
-    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    # From idle the GPU's clocks take ~10 ms of back-to-back work to settle
+    # (kernel traces show the first ~30 int2-8k steps up to 30% slower), so
+    # after the warm-up steps every timed measurement first runs untimed
+    # steps until this much work is done, whatever --warmup says.
+    p.add_argument("--settle-ms", type=float, default=25.0)
+    p.add_argument("--trials", type=int, default=3,
+                   help="trials of --trial-steps steps after the timed steps (the pages' protocol: "
+                        "one warm-up, three trials, averaged)")
+    p.add_argument("--trial-steps", type=int, default=127)
+    p.add_argument("--cpu-threads", type=int, default=0, help="host threads of the oracle fan-out (0 = all)")
     p.add_argument("--workload", default="int2-8k")
     p.add_argument("--splits", type=int, default=0, help="token splits (0 = library's choice)")
     p.add_argument("--replicas", type=int, default=2)
     p.add_argument("--cpu-sample", type=int, default=256, help="(batch, head) pairs the oracle decodes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-baseline", action="store_true")
+    p.add_argument("--sdpa", action="store_true",
+                   help="int2-8k: also time torch's SDPA (flash / memory-efficient backends) on the BF16 "
+                        "baseline's shapes")
     p.add_argument("--graphs", action="store_true",
                    help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
-    p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep"],
+    p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep", "stream"],
                    help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling; "
-                        "split-sweep: every token-split count against the automatic one")
+                        "split-sweep: every token-split count against the automatic one; "
+                        "stream: the attainable HBM read rate (128-bit read-stream kernel)")
     a = p.parse_args()
+    global SETTLE_MS
+    SETTLE_MS = a.settle_ms
     a.steps_given = a.steps is not None
     if a.steps is None:
         a.steps = 127
@@ -95,42 +109,111 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_pairs: int):
-    """The oracle's decode (FP64 reconstruction + FP64 attention), single
-    thread, on n_pairs (batch, head) pairs of the same workload, all loops;
-    scaled to the full step."""
-    import numpy as np
+def host_threads(requested: int = 0) -> int:
+    """Host threads for the oracle fan-out: the request, else the CPUs this
+    process may run on, at most 16 (a one-GPU share of a GPU host)."""
+    if requested > 0:
+        return requested
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_layer(w, n_pairs: int, n_ctx: int, seed: int):
+    """n_pairs (batch, head) pairs of workload w's layout, drawn and encoded
+    by the oracle (one head per pair: layout batch = n_pairs, heads = 1)."""
     import synth
     from oracle import rq_oracle as orc
     from synth import bf16_bits
 
-    g = synth.generator(w.seed + 1000)
+    g = synth.generator(seed)
     kstd, vstd = synth.channel_std(g, 1, w.d), synth.channel_std(g, 1, w.d)
-    kr, kl = synth.draw_kv(g, w.n_loops, n_pairs, 1, w.n_ctx, w.d, w.c, w.sigma, kstd)
-    vr, vl = synth.draw_kv(g, w.n_loops, n_pairs, 1, w.n_ctx, w.d, w.c, w.sigma, vstd)
+    kr, kl = synth.draw_kv(g, w.n_loops, n_pairs, 1, n_ctx, w.d, w.c, w.sigma, kstd)
+    vr, vl = synth.draw_kv(g, w.n_loops, n_pairs, 1, n_ctx, w.d, w.c, w.sigma, vstd)
     q = synth.draw_queries(g, w.n_loops, n_pairs, 1, w.d)
-    lay = dict(n_loops=w.n_loops, batch=n_pairs, heads=1, d=w.d, g=w.g, cap=w.n_ctx,
+    lay = dict(n_loops=w.n_loops, batch=n_pairs, heads=1, d=w.d, g=w.g, cap=n_ctx,
                rotate=w.rotate, bits=w.bits)
-    kp = orc.Planes(w.n_loops, n_pairs, 1, w.d, w.g, w.n_ctx, w.bits)
-    vp = orc.Planes(w.n_loops, n_pairs, 1, w.d, w.g, w.n_ctx, w.bits)
+    kp = orc.Planes(w.n_loops, n_pairs, 1, w.d, w.g, n_ctx, w.bits)
+    vp = orc.Planes(w.n_loops, n_pairs, 1, w.d, w.g, n_ctx, w.bits)
     kp.ref[:] = bf16_bits(kr)
     vp.ref[:] = bf16_bits(vr)
-    orc.encode(lay, kp, bf16_bits(kl), 0, w.n_ctx)
-    orc.encode(lay, vp, bf16_bits(vl), 0, w.n_ctx)
-    qb = bf16_bits(q)
-    mask = (1 << w.n_loops) - 1
+    kin, vin = bf16_bits(kl), bf16_bits(vl)
+    return lay, kp, vp, kin, vin, bf16_bits(q)
+
+
+def oracle_decode_timing(w, lay, kp, vp, qb, n_pairs: int, n_ctx: int, threads: int, single_pairs: int):
+    """Seconds per (batch, head) pair (all loops over n_ctx tokens) of the
+    oracle's decode (FP64 reconstruction + FP64 attention): single-threaded
+    over single_pairs pairs, and fanned out over `threads` host threads, one
+    (loop, batch, head) row per task, over all n_pairs pairs.  The oracle
+    is plain C called through ctypes, which releases the GIL during the
+    call, so the rows run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from oracle import rq_oracle as orc
+
+    scale = 1.0 / np.sqrt(w.d)
+    rows = [(l, b) for b in range(n_pairs) for l in range(w.n_loops)]
+    run = lambda r: orc.decode_row(lay, kp, vp, qb, r[0], r[1], 0, n_ctx, scale)
+    run(rows[0])                                   # loads the library
     t0 = time.perf_counter()
-    orc.decode(lay, kp, vp, qb, mask, w.n_ctx, 1.0 / np.sqrt(w.d))
-    dt = time.perf_counter() - t0
-    step_s = dt * (w.batch * w.heads) / n_pairs
-    return {"value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_pairs} of {w.batch * w.heads} (batch, head) pairs x {w.n_loops} loops x "
-                      f"{w.n_ctx} tokens decoded in {dt:.1f} s on one core, scaled x"
-                      f"{w.batch * w.heads / n_pairs:.2f} to the full step",
-            "ms_per_step": step_s * 1e3}
+    for r in rows[:single_pairs * w.n_loops]:
+        run(r)
+    one = (time.perf_counter() - t0) / single_pairs
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, rows))
+    many = (time.perf_counter() - t0) / n_pairs
+    return one, many
 
 
-def bf16_baseline(w, n, steps, warmup, splits_rq):
+def cpu_baseline(w, n_pairs: int, threads: int = 0, single_pairs: int = 48, n_ctx: int = 0,
+                 batch: int = 0, what: str = ""):
+    """The oracle's decode (FP64 reconstruction + FP64 attention) on n_pairs
+    (batch, head) pairs of workload w at n_ctx tokens, all loops, scaled to
+    a full step of `batch` x heads x layers pairs: on all host threads (the
+    reported value) and on one.  The oracle's encode of the sample (one
+    thread) is timed too."""
+    threads = host_threads(threads)
+    single_pairs = min(single_pairs, n_pairs)
+    n_ctx = n_ctx or w.n_ctx
+    batch = batch or w.batch
+    lay, kp, vp, kin, vin, qb = oracle_layer(w, n_pairs, n_ctx, w.seed + 1000)
+    from oracle import rq_oracle as orc
+    t0 = time.perf_counter()
+    orc.encode(lay, kp, kin, 0, n_ctx)
+    orc.encode(lay, vp, vin, 0, n_ctx)
+    enc = (time.perf_counter() - t0) / n_pairs
+    one, many = oracle_decode_timing(w, lay, kp, vp, qb, n_pairs, n_ctx, threads, single_pairs)
+    pairs = batch * w.heads * w.layers
+    step_many, step_one = many * pairs, one * pairs
+    return {"value": batch / step_many, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_pairs} of {pairs} (batch, head) pairs x {w.n_loops} loops x {n_ctx} tokens "
+                      f"decoded in {many * n_pairs:.1f} s on {threads} host threads (one (loop, batch, head) "
+                      f"row per task), scaled x{pairs / n_pairs:.2f} to the full step{what}",
+            "ms_per_step": step_many * 1e3, "host_cpu": cpu_model(),
+            "single_thread": {"value": batch / step_one, "unit": "tokens/s", "cores": 1,
+                              "ms_per_step": step_one * 1e3,
+                              "sample": f"{single_pairs} pairs x {w.n_loops} loops in {one * single_pairs:.1f} s"},
+            "encode_single_thread": {"s_per_pair": enc, "tokens_per_s": n_ctx / enc,
+                                     "sample": f"{n_pairs} pairs x {n_ctx} tokens, K and V, "
+                                               f"{w.n_loops - 1} residual loops, one thread"}}
+
+
+def bf16_baseline(w, n, steps, warmup, splits_rq, trials_n=0, trial_steps=127):
     """The same decode step on a BF16 KV cache (every loop its own BF16 K, V),
     timed the same way; the comparison the pages normalise against."""
     import numpy as np
@@ -157,7 +240,7 @@ def bf16_baseline(w, n, steps, warmup, splits_rq):
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
+    settled = settle(step, warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -166,10 +249,12 @@ def bf16_baseline(w, n, steps, warmup, splits_rq):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nbytes = w.batch * w.heads * n * 2 * w.n_loops * w.d * 2
+    trials = run_trials(step, trials_n, trial_steps)
     del reps
     torch.cuda.empty_cache()
     return {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
             "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1), "bytes_per_step": nbytes,
+            "settle_steps": settled, "trials": trials_summary(trials, w.batch, nbytes),
             "kernel": "rq_bf16_decode_attn: the same split-K kernel over BF16 K/V, one launch per loop"}
 
 
@@ -188,6 +273,74 @@ def copy_probe():
     print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}))
 
 
+def stream_probe(args):
+    """The attainable HBM read rate: rq_probe_read_stream over a 4 GiB buffer
+    (16x the 256 MB Infinity Cache), default and non-temporal loads, 4 / 8 /
+    16 workgroups of 256 lanes per compute unit.  One JSON line per point,
+    then a summary line."""
+    import torch
+    import decode_attention_rq_amd as rq
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    steps = args.steps if args.steps_given else 20
+    best = {}
+    for nt in (0, 1):
+        for per_cu in (4, 8, 16):
+            sink = torch.empty(cus * per_cu * 256, dtype=torch.int32, device="cuda")
+            ms = timed(lambda i: rq.rq_probe_read_stream(buf, nt, sink), steps, 2)
+            gbs = nbytes / (ms / 1e3) / 1e9
+            row = {"mode": "stream", "nontemporal": nt, "workgroups_per_cu": per_cu, "ms_per_read": round(ms, 4),
+                   "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            print(json.dumps(row), flush=True)
+            key = "nontemporal" if nt else "default"
+            if gbs > best.get(key, {}).get("gbs", 0):
+                best[key] = row
+    print(json.dumps({"mode": "stream", "bytes_per_read": nbytes, "best": best, "system": system_info()}), flush=True)
+
+
+def sdpa_baseline(w, n, steps, warmup, ours):
+    """torch's scaled_dot_product_attention (flash or memory-efficient
+    backend only; the math backend is never allowed) on the BF16 baseline's
+    shapes: one call per loop, q [B, H, 1, d] against that loop's BF16 K, V
+    [B, H, n, d].  A sanity check that the BF16 baseline kernel is not a
+    straw man.  `ours` = the baseline kernel's output on the same inputs
+    (f32 [L, B, H, d]), compared with the SDPA output."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import synth
+
+    d = synth.draw_layer(w, seed=w.seed, device="cuda")
+    ks = [d["k_loops"][l] for l in range(w.n_loops - 1)] + [d["k_ref"]]
+    vs = [d["v_loops"][l] for l in range(w.n_loops - 1)] + [d["v_ref"]]
+    q = d["q"].contiguous()
+    scale = 1.0 / np.sqrt(w.d)
+    res = {"kernel": "torch.nn.functional.scaled_dot_product_attention, one call per loop"}
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                outs = [None] * w.n_loops
+
+                def step(i):
+                    for l in range(w.n_loops):
+                        outs[l] = F.scaled_dot_product_attention(q[l][:, :, None, :], ks[l], vs[l], scale=scale)
+                ms = timed(step, steps, warmup)
+            got = torch.stack([o[:, :, 0, :].float() for o in outs]).cpu().numpy()
+            ref = ours(ks, vs, q)
+            err = float((np.abs(got - ref).max(-1) / np.abs(ref).max(-1)).max())
+            nbytes = w.batch * w.heads * n * 2 * w.n_loops * w.d * 2
+            res[name] = {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+                         "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+                         "max_row_rel_diff_vs_bf16_baseline_kernel": err}
+        except Exception as e:       # backend unavailable on this build
+            res[name] = {"error": f"{type(e).__name__}: {str(e).splitlines()[0][:200]}"}
+    del d, ks, vs, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def system_info():
     """Device and software versions the numbers were taken with."""
     import torch
@@ -201,12 +354,40 @@ def layout_of(w, batch, cap):
     return rq.Layout(w.n_loops, batch, w.heads, w.d, w.g, cap, w.rotate, w.bits)
 
 
+def settle(fn, start=0, settle_ms=None):
+    """Run fn(start), fn(start+1), ... untimed until about settle_ms of GPU
+    work is done (the clocks ramp up over the first ~10 ms of back-to-back
+    work after an idle period).  The first three calls, bracketed by HIP
+    events, give the per-call time that sizes the rest.  Returns the number
+    of calls made."""
+    import torch
+    settle_ms = SETTLE_MS if settle_ms is None else settle_ms
+    if settle_ms <= 0:
+        return 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(3):
+        fn(start + i)
+    e1.record()
+    torch.cuda.synchronize()
+    done = e0.elapsed_time(e1)
+    per = max(done / 3, 1e-3)
+    more = min(5000, max(0, int((settle_ms - done) / per) + 1))
+    for i in range(more):
+        fn(start + 3 + i)
+    torch.cuda.synchronize()
+    return 3 + more
+
+
 def timed(fn, steps, warmup):
-    """Mean ms per call of fn(i) over `steps` calls after `warmup`, bracketed by
-    device synchronisation (HIP events on the current stream)."""
+    """Mean ms per call of fn(i) over `steps` calls after `warmup` calls and
+    the settling work, bracketed by device synchronisation (HIP events on the
+    current stream)."""
     import torch
     for i in range(warmup):
         fn(i)
+    settle(fn, warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -215,6 +396,36 @@ def timed(fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def run_trials(fn, trials, steps):
+    """The pages' protocol (a warm-up, then three trials of 127 decode steps,
+    averaged): `trials` back-to-back trials of `steps` calls of fn, each
+    bracketed by two HIP events.  Returns ms per call of each trial."""
+    import torch
+    out = []
+    for t in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def trials_summary(ms, batch, nbytes):
+    """Mean and spread of the trials' step times, as tokens/s and GB/s."""
+    import numpy as np
+    if not ms:
+        return None
+    a = np.array(ms)
+    return {"n": len(ms), "ms_per_step": [round(float(x), 4) for x in ms],
+            "ms_mean": round(float(a.mean()), 4), "ms_spread": round(float(a.max() - a.min()), 4),
+            "tokens_per_s_mean": round(float(np.mean(batch / (a / 1e3))), 1),
+            "hbm_gbs_mean": round(float(np.mean(nbytes / (a / 1e3) / 1e9)), 1),
+            "frac_of_peak_mean": round(float(np.mean(nbytes / (a / 1e3) / 1e9)) / HBM_PEAK_GBS, 4)}
 
 
 def timed_graph(fn, steps, warmup, settle_ms=20.0):
@@ -355,6 +566,18 @@ def append_bench(args, w):
                                                     rq.rq_decode_splits(lay_b, n0 + i + 1)), steps, 3)
         res["bf16_baseline"] = {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4)}
         res["speedup_vs_bf16"] = round(res["value"] / res["bf16_baseline"]["value"], 3)
+    if not args.no_cpu_baseline:
+        # the oracle on 8 (batch, head) pairs: its decode at 8k (threads) plus
+        # its encode of one token per pair (one append step), scaled to B x H
+        cb = cpu_baseline(w, 8, args.cpu_threads, 4,
+                          what="; an append step adds the oracle's one-token encode of every pair, one thread")
+        pairs = w.batch * w.heads
+        enc_step_s = pairs * cb["encode_single_thread"]["s_per_pair"] / w.n_ctx
+        step_s = cb["ms_per_step"] / 1e3 + enc_step_s
+        cb["value"] = w.batch / step_s
+        cb["ms_per_step"] = step_s * 1e3
+        cb["prefill_encode_s"] = pairs * cb["encode_single_thread"]["s_per_pair"]
+        res["cpu_baseline"] = cb
     return res
 
 
@@ -424,6 +647,10 @@ def layers_bench(args, w):
         res["speedup_vs_bf16"] = round(res["value"] / res["bf16_baseline"]["value"], 3)
         del bl
         torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, w.heads, args.cpu_threads, 4, n_ctx=n,
+                                           what=" (one layer x one batch element sampled, extrapolated "
+                                                "linearly over layers and batch)")
     return res
 
 
@@ -522,6 +749,10 @@ def peak_batch_bench(args, w, budget=250e9):
         peak_bf = max(r["tokens_per_s"] for r in bf_rows)
         res["sweep_bf16"] = bf_rows
         res["peak_gain_vs_bf16"] = round(peak_rq / peak_bf, 3)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, w.heads, args.cpu_threads, 4, batch=bmax_rq,
+                                           what=f" at batch {bmax_rq} (one layer x one batch element "
+                                                f"sampled, extrapolated linearly over layers and batch)")
     return res
 
 
@@ -844,6 +1075,9 @@ def main():
     if args.mode == "copy":
         copy_probe()
         return
+    if args.mode == "stream":
+        stream_probe(args)
+        return
     if args.mode == "split-sweep":
         split_sweep()
         return
@@ -902,6 +1136,7 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    settled = settle(step, args.warmup)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` decode steps -----------------------
@@ -923,6 +1158,7 @@ def main():
     launch_ms = np.array([span_ms / args.steps])
     ms_per_step = span_ms / args.steps
     tokens_per_s = w.batch / (ms_per_step / 1e3)
+    trials = run_trials(step, args.trials, args.trial_steps)
 
     per_tok = algorithmic_bytes_per_token(w)
     rows = w.n_loops * w.batch * w.heads
@@ -949,19 +1185,33 @@ def main():
         "hbm_gbs": round(achieved, 1),
         "roofline": roofline,
         "wall_s": round(wall, 3),
+        "settle": {"steps": settled, "target_ms": SETTLE_MS},
+        "trials": trials_summary(trials, w.batch, alg_bytes),
         "system": system_info(),
     }
     if not args.no_bf16_baseline:
         del reps
         torch.cuda.empty_cache()
-        bf = bf16_baseline(w, n, args.steps, args.warmup, splits)
+        bf = bf16_baseline(w, n, args.steps, args.warmup, splits, args.trials, args.trial_steps)
         res["bf16_baseline"] = bf
         res["speedup_vs_bf16"] = round(tokens_per_s / bf["value"], 3)
         # KV bytes per (batch, head, token): BF16 for every loop vs this layout;
         # at equal KV memory the feasible batch grows by their ratio
         res["batch_gain_at_equal_kv_memory"] = round(2 * w.n_loops * w.d * 2 / per_tok, 3)
+        if bf.get("trials") and trials:
+            res["speedup_vs_bf16_trials_mean"] = round(bf["trials"]["ms_mean"] / float(np.mean(trials)), 3)
+    if args.sdpa:
+        lay_b = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, n, w.rotate, w.bits)
+        ws_b = rq.workspace_for(lay_b, n, splits, dev)
+
+        def ours(ks, vs, q):
+            o = torch.empty(w.n_loops, w.batch, w.heads, w.d, device=dev)
+            rq.rq_bf16_decode_attn(lay_b, ks, vs, q, mask, n, scale, o, ws_b, splits)
+            torch.cuda.synchronize()
+            return o.cpu().numpy()
+        res["sdpa_baseline"] = sdpa_baseline(w, n, args.steps, args.warmup, ours)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample, w.batch * w.heads))
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample, w.batch * w.heads), args.cpu_threads)
     print(json.dumps(res), flush=True)
 
 

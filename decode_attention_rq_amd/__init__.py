@@ -4,6 +4,11 @@ Argument marshalling only: every step of encode, reconstruction and decode
 runs in the library's HIP kernels (see include/rq.h).  torch supplies device
 memory and the stream.  Importing this module fails if librq.so has not been
 built (python decode_attention_rq_amd/build.py, or __graft_entry__.build()).
+
+Before each call the binding checks every tensor against the layout it is
+passed with: dtype, exact shape, contiguity, and (when a GPU is present)
+that it lives on the GPU; a mismatch raises ValueError and nothing is
+called.  The library itself checks pointers, alignment and ranges.
 """
 from __future__ import annotations
 
@@ -64,6 +69,8 @@ _lib.rq_bf16_decode_attn.restype = C.c_int
 _lib.rq_bf16_decode_attn.argtypes = [_P(rq_layout), _P(C.c_void_p), _P(C.c_void_p), C.c_void_p,
                                      C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.rq_probe_read_stream.restype = C.c_int
+_lib.rq_probe_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
 _lib.rq_reconstruct.restype = C.c_int
 _lib.rq_reconstruct.argtypes = [_P(rq_layout), _P(rq_cache), C.c_int32, C.c_int32, C.c_int32,
                                 C.c_void_p, C.c_void_p]
@@ -85,6 +92,56 @@ def rq_status_string(status: int) -> str:
 def _check(status: int) -> None:
     if status != 0:
         raise RQError(status)
+
+
+def _tensor(t, name: str, dtype, shape=None, allow_none: bool = False) -> None:
+    """ValueError unless t is a contiguous tensor of `dtype` and exactly
+    `shape` (None: any shape), on the GPU when one is present."""
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name}: a tensor is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not t.is_cuda and torch.cuda.is_available():
+        raise ValueError(f"{name}: must be a GPU tensor (device {t.device})")
+
+
+def _check_cache(layout: "Layout", c: "Cache", name: str) -> None:
+    """Every plane of c present has the dtype and shape `layout` gives it."""
+    B, H, d, cap = layout.batch, layout.n_heads, layout.head_dim, layout.capacity
+    if len(c.codes) != layout.n_loops or len(c.meta) != layout.n_loops or len(c.alpha) != layout.n_loops:
+        raise ValueError(f"{name}: planes for {len(c.codes)} loops, layout has {layout.n_loops}")
+    if not layout.ref_bits:
+        _tensor(c.ref, f"{name}.ref", torch.bfloat16, (B, H, cap, d), allow_none=True)
+    for l in range(layout.n_loops):
+        if layout.is_anchor(l):
+            if layout.ref_bits:
+                ga = layout.anchor_group
+                _tensor(c.codes[l], f"{name}.codes[{l}]", torch.uint8, (B, H, cap, d * layout.ref_bits // 8), True)
+                _tensor(c.meta[l], f"{name}.meta[{l}]", torch.float16, (B, H, cap, d // ga, 2), True)
+            continue
+        bits = int(layout.bits[l]) if l < len(layout.bits) else 0
+        if bits not in (2, 4):
+            continue            # the library reports the unsupported width
+        _tensor(c.codes[l], f"{name}.codes[{l}]", torch.uint8, (B, H, cap, d * bits // 8), True)
+        _tensor(c.meta[l], f"{name}.meta[{l}]", torch.float16, (B, H, cap, d // layout.group, 2), True)
+        _tensor(c.alpha[l], f"{name}.alpha[{l}]", torch.float16, (B, H, cap), True)
+
+
+def _check_rows(layout: "Layout", t, name: str, dtype) -> None:
+    """One row per (loop, batch, head): [L, B, H, d]."""
+    _tensor(t, name, dtype, (layout.n_loops, layout.batch, layout.n_heads, layout.head_dim))
+
+
+def _check_workspace(ws) -> None:
+    _tensor(ws, "workspace", ws.dtype if isinstance(ws, torch.Tensor) else torch.uint8)
 
 
 @dataclass
@@ -213,6 +270,12 @@ def rq_encode(layout: Layout, k: Cache, v: Cache, k_in: torch.Tensor, v_in: torc
     """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous, the loops other than
     the BF16 reference in loop order; with quantized anchors [L, B, H, n, d]
     (every loop, anchors included, in loop order)."""
+    _check_cache(layout, k, "k")
+    _check_cache(layout, v, "v")
+    loops = layout.n_loops if layout.ref_bits else layout.n_loops - 1
+    shape = (loops, layout.batch, layout.n_heads, int(n), layout.head_dim) if n > 0 else None
+    _tensor(k_in, "k_in", torch.bfloat16, shape)
+    _tensor(v_in, "v_in", torch.bfloat16, shape)
     lay, kc, vc = layout.c(), k.c(), v.c()
     _check(_lib.rq_encode(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(k_in), _ptr(v_in),
                           int(t0), int(n), _stream(stream)))
@@ -235,6 +298,11 @@ def rq_decode_attn(layout: Layout, k: Cache, v: Cache, q: torch.Tensor, loop_mas
                    sm_scale: float, out: torch.Tensor, workspace: torch.Tensor, n_splits: int = 0,
                    stream=None) -> None:
     """q: bf16 [L, B, H, d]; out: f32 [L, B, H, d]; workspace: device bytes."""
+    _check_cache(layout, k, "k")
+    _check_cache(layout, v, "v")
+    _check_rows(layout, q, "q", torch.bfloat16)
+    _check_rows(layout, out, "out", torch.float32)
+    _check_workspace(workspace)
     lay, kc, vc = layout.c(), k.c(), v.c()
     _check(_lib.rq_decode_attn(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(q), int(loop_mask),
                                int(n_ctx), float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
@@ -246,9 +314,21 @@ class Tail:
     (None for loops never attended); n tokens [0, n) are attended."""
 
     def __init__(self, k: Sequence[Optional[torch.Tensor]], v: Sequence[Optional[torch.Tensor]], n: int):
+        """Every plane present must have the same capacity (the library reads
+        all of them with one row stride)."""
         self.k, self.v, self.n = list(k), list(v), int(n)
-        caps = [t.shape[2] for t in self.k + self.v if t is not None]
-        self.capacity = min(caps) if caps else 0
+        caps = {int(t.shape[2]) for t in self.k + self.v if t is not None and t.dim() == 4}
+        if len(caps) > 1:
+            raise ValueError(f"tail planes of different capacities {sorted(caps)}")
+        self.capacity = caps.pop() if caps else 0
+        if self.n < 0 or self.n > self.capacity:
+            raise ValueError(f"tail: n = {self.n} outside [0, capacity {self.capacity}]")
+
+    def check(self, layout: "Layout") -> None:
+        for side, planes in (("k", self.k), ("v", self.v)):
+            for l, t in enumerate(planes):
+                _tensor(t, f"tail.{side}[{l}]", torch.bfloat16,
+                        (layout.batch, layout.n_heads, self.capacity, layout.head_dim), allow_none=True)
 
     def c(self) -> rq_tail:
         s = rq_tail()
@@ -265,6 +345,13 @@ def rq_decode_attn_tail(layout: Layout, k: Cache, v: Cache, tail: Optional[Tail]
                         loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
                         workspace: torch.Tensor, n_splits: int = 0, stream=None) -> None:
     """rq_decode_attn over n_ctx cached tokens followed by tail.n BF16 tokens."""
+    _check_cache(layout, k, "k")
+    _check_cache(layout, v, "v")
+    _check_rows(layout, q, "q", torch.bfloat16)
+    _check_rows(layout, out, "out", torch.float32)
+    _check_workspace(workspace)
+    if tail is not None:
+        tail.check(layout)
     lay, kc, vc = layout.c(), k.c(), v.c()
     tc = tail.c() if tail is not None else None
     _check(_lib.rq_decode_attn_tail(C.byref(lay), C.byref(kc), C.byref(vc),
@@ -278,6 +365,15 @@ def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops
                         q: torch.Tensor, loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
                         workspace: torch.Tensor, n_splits: int = 0, stream=None) -> None:
     """BF16-KV baseline: k_loops / v_loops are n_loops bf16 [B, H, cap, d] tensors."""
+    shape = (layout.batch, layout.n_heads, layout.capacity, layout.head_dim)
+    if len(k_loops) != layout.n_loops or len(v_loops) != layout.n_loops:
+        raise ValueError(f"k_loops / v_loops: {layout.n_loops} entries expected")
+    for l in range(layout.n_loops):
+        _tensor(k_loops[l], f"k_loops[{l}]", torch.bfloat16, shape, allow_none=True)
+        _tensor(v_loops[l], f"v_loops[{l}]", torch.bfloat16, shape, allow_none=True)
+    _check_rows(layout, q, "q", torch.bfloat16)
+    _check_rows(layout, out, "out", torch.float32)
+    _check_workspace(workspace)
     lay = layout.c()
     kp = (C.c_void_p * layout.n_loops)(*[_ptr(t) for t in k_loops])
     vp = (C.c_void_p * layout.n_loops)(*[_ptr(t) for t in v_loops])
@@ -289,6 +385,8 @@ def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops
 def rq_reconstruct(layout: Layout, c: Cache, loop: int, t0: int, n: int, out: torch.Tensor,
                    stream=None) -> None:
     """out: f32 [B, H, n, d]."""
+    _check_cache(layout, c, "c")
+    _tensor(out, "out", torch.float32, (layout.batch, layout.n_heads, int(n), layout.head_dim))
     lay, cc = layout.c(), c.c()
     _check(_lib.rq_reconstruct(C.byref(lay), C.byref(cc), int(loop), int(t0), int(n), _ptr(out),
                                _stream(stream)))
@@ -300,3 +398,15 @@ def workspace_for(layout: Layout, n_ctx: int, n_splits: int = 0, device="cuda") 
     if nbytes == 0:
         raise RQError(-1)
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def rq_probe_read_stream(buf: torch.Tensor, nontemporal: bool, sink: torch.Tensor, stream=None) -> None:
+    """Read all of buf once with 128-bit loads (include/rq_probe.h); sink is a
+    device int32/uint32 tensor whose length (a multiple of 256) sets the
+    number of workgroups."""
+    _tensor(buf, "buf", buf.dtype if isinstance(buf, torch.Tensor) else torch.uint8)
+    _tensor(sink, "sink", torch.int32)
+    if sink.numel() % 256 != 0:
+        raise ValueError("sink: length must be a multiple of 256")
+    _check(_lib.rq_probe_read_stream(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
+                                     sink.numel() // 256, _ptr(sink), _stream(stream)))

@@ -220,8 +220,10 @@ void decode_waves(int S, int bh, int32_t *wide, int32_t *waves8) {
   }
 }
 
-// Workspace: the split records f32 [S][kMaxSlots][BH][2D+2], at least one
-// split's worth (a single split writes records when a BF16 tail follows).
+// Workspace: the split records f32 [S][kMaxSlots][BH][2D+2].  A call with
+// one workgroup per (b, h) (one split, or the wide form of two) writes no
+// records; one split's worth is still asked for, so that a workspace sized
+// for any split count is never empty.
 size_t workspace_for(const rq_layout *L, int n_splits) {
   const size_t s = n_splits > 1 ? (size_t)n_splits : 1;
   return s * rq::kMaxSlots * (size_t)L->batch * L->n_heads * (size_t)(2 * L->head_dim + 2) *

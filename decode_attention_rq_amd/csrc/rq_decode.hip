@@ -189,33 +189,42 @@ hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slot
   return hipGetLastError();
 }
 
-template <int D>
-static int blocks_per_cu_d() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0, 0>, 64 * kWaves, 0) != hipSuccess)
-    return -1;
-  return n;
-}
+// Instantiated in rq_decode_inst.hip, one object file per combination.
+#define RQ_DECODE_EXTERN(D, AQ, CHAIN) \
+  extern template hipError_t launch_decode_d<D, AQ, CHAIN>(const DecodeArgs &, int, bool, hipStream_t);
+#define RQ_DECODE_EXTERN_D(AQ, CHAIN) \
+  RQ_DECODE_EXTERN(64, AQ, CHAIN) RQ_DECODE_EXTERN(128, AQ, CHAIN) RQ_DECODE_EXTERN(256, AQ, CHAIN)
+RQ_DECODE_EXTERN_D(0, 0)
+RQ_DECODE_EXTERN_D(2, 0)
+RQ_DECODE_EXTERN_D(4, 0)
+RQ_DECODE_EXTERN_D(0, 1)
+RQ_DECODE_EXTERN_D(4, 1)
+RQ_DECODE_EXTERN_D(0, 2)
+RQ_DECODE_EXTERN_D(4, 2)
+extern template int decode_blocks_per_cu_d<64>();
+extern template int decode_blocks_per_cu_d<128>();
+extern template int decode_blocks_per_cu_d<256>();
 
 int decode_blocks_per_cu(int head_dim) {
   switch (head_dim) {
-    case 64: return blocks_per_cu_d<64>();
-    case 128: return blocks_per_cu_d<128>();
-    case 256: return blocks_per_cu_d<256>();
+    case 64: return decode_blocks_per_cu_d<64>();
+    case 128: return decode_blocks_per_cu_d<128>();
+    case 256: return decode_blocks_per_cu_d<256>();
     default: return -1;
   }
 }
 
-template hipError_t launch_decode_aq<0, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
-// instantiated in rq_decode_anchor{2,4}.hip, rq_decode_chain{0,4}.hip and
-// rq_decode_chain{0,4}_one.hip
-extern template hipError_t launch_decode_aq<2, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<4, 0>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<0, 1>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<4, 1>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<0, 2>(const DecodeArgs &, int, int, bool, hipStream_t);
-extern template hipError_t launch_decode_aq<4, 2>(const DecodeArgs &, int, int, bool, hipStream_t);
+// One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits),
+// chained references or not.
+template <int AQ, int CHAIN>
+static hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_decode_d<64, AQ, CHAIN>(a, n_res, ref, st);
+    case 128: return launch_decode_d<128, AQ, CHAIN>(a, n_res, ref, st);
+    case 256: return launch_decode_d<256, AQ, CHAIN>(a, n_res, ref, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
                          int chain, hipStream_t st) {

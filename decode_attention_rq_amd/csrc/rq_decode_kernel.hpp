@@ -826,8 +826,11 @@ static hipError_t launch_bits(const DecodeArgs &a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// One decode pass at head_dim D with reference kind AQ (0: BF16 rows; 2, 4:
+// anchor bits), chained references or not.  Each (D, AQ, CHAIN) is
+// instantiated in an object file of its own (rq_decode_inst.hip).
 template <int D, int AQ, int CHAIN>
-static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
+hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t st) {
   if constexpr (CHAIN == 2) {       // slot 0 alone: never the reference slot
     switch (ref ? -1 : n_res) {
       case 1: return launch_bits<D, 1, false, AQ, CHAIN>(a, st);
@@ -853,16 +856,16 @@ static hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipS
   return hipErrorInvalidValue;
 }
 
-// One decode pass with reference kind AQ (0: BF16 rows; 2, 4: anchor bits),
-// chained references or not.
-template <int AQ, int CHAIN>
-hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t st) {
-  switch (head_dim) {
-    case 64: return launch_decode_d<64, AQ, CHAIN>(a, n_res, ref, st);
-    case 128: return launch_decode_d<128, AQ, CHAIN>(a, n_res, ref, st);
-    case 256: return launch_decode_d<256, AQ, CHAIN>(a, n_res, ref, st);
-    default: return hipErrorInvalidValue;
-  }
+// Resident workgroups per compute unit of the main decode kernel at head_dim
+// D (4-wave workgroups, a full pass over a BF16 reference), or -1 on a HIP
+// error.
+template <int D>
+int decode_blocks_per_cu_d() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, decode_kernel<D, kMaxRes, true, 0, kTilesPerIter, kWaves, 0, 0>, 64 * kWaves, 0) != hipSuccess)
+    return -1;
+  return n;
 }
 
 }  // namespace rq

@@ -101,12 +101,14 @@ hipError_t launch_reconstruct(const ReconArgs &a, int head_dim, hipStream_t s);
 // Launches the merge kernel too when a.records is set.
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, int n_res, bool ref, int anchor_bits,
                          int chain, hipStream_t s);
-template <int AQ, int CHAIN>
-hipError_t launch_decode_aq(const DecodeArgs &a, int head_dim, int n_res, bool ref, hipStream_t s);
+template <int D, int AQ, int CHAIN>
+hipError_t launch_decode_d(const DecodeArgs &a, int n_res, bool ref, hipStream_t s);
 // The split/tail merge for n_slots loop slots, the first n_res of them residual.
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, int n_res, int n_slots, hipStream_t s);
 // Decode workgroups of this head_dim resident per compute unit at once (the
 // occupancy of the main decode kernel), or <= 0 on a HIP error.
 int decode_blocks_per_cu(int head_dim);
+template <int D>
+int decode_blocks_per_cu_d();
 
 }  // namespace rq

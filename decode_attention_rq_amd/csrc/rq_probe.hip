@@ -1,0 +1,55 @@
+// rq_probe.hip -- a plain 128-bit HBM read stream (gfx950): the attainable
+// read bandwidth that the decode kernel's achieved rate is compared with.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rq.h"
+#include "rq_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(const u32x4_t *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+__device__ __forceinline__ uint32_t fold(u32x4_t v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// Every lane reads elements i, i + stride, ... of the buffer (stride = all
+// lanes of the grid), four independent loads per iteration, and writes the
+// XOR of everything it read.
+template <bool NT>
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t *p, uint64_t n16, uint32_t *sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = load16<NT>(p + i), b = load16<NT>(p + i + stride);
+    const u32x4_t c = load16<NT>(p + i + 2 * stride), d = load16<NT>(p + i + 3 * stride);
+    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+  }
+  for (; i < n16; i += stride) acc ^= fold(load16<NT>(p + i));
+  sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" rq_status rq_probe_read_stream(const void *buf, size_t bytes, int32_t nontemporal, int32_t n_blocks,
+                                          uint32_t *sink, void *hip_stream) {
+  if (!aligned16(buf) || !aligned16(sink) || bytes < 16 || bytes % 16 != 0) return RQ_ERR_INVALID_ARG;
+  if (n_blocks < 1 || n_blocks > 65535 || (nontemporal != 0 && nontemporal != 1)) return RQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const u32x4_t *p = static_cast<const u32x4_t *>(buf);
+  if (nontemporal)
+    hipLaunchKernelGGL(read_stream_kernel<true>, dim3(n_blocks), dim3(256), 0, st, p, (uint64_t)(bytes / 16), sink);
+  else
+    hipLaunchKernelGGL(read_stream_kernel<false>, dim3(n_blocks), dim3(256), 0, st, p, (uint64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_DEVICE;
+}

@@ -9,7 +9,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("rq.h", "rq_baseline.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["rq_encode", "rq_decode_workspace_bytes", "rq_decode_splits",
                             "rq_decode_attn", "rq_decode_attn_tail", "rq_reconstruct",
-                            "rq_status_string", "rq_bf16_decode_attn"])
+                            "rq_status_string", "rq_bf16_decode_attn", "rq_probe_read_stream"])
 
 
 def test_library_exports_every_declared_symbol(rq):
@@ -354,3 +355,16 @@ def test_chain_decode_checks_every_link(rq):
     k = _cache(rq, bad=("alpha", 1, 0))
     assert _decode(rq, lay, k=k, mask=0b0001) == INVALID
     assert _decode(rq, lay, k=k, mask=0b0100, ws_bytes=1) == WORKSPACE   # loop 2 needs only itself
+
+
+def test_read_stream_probe_rejects_bad_arguments(rq):
+    f = rq._lib.rq_probe_read_stream
+    INVALID = -1
+    assert f(None, 1024, 0, 4, FAKE, None) == INVALID            # null buffer
+    assert f(FAKE + 8, 1024, 0, 4, FAKE, None) == INVALID        # misaligned buffer
+    assert f(FAKE, 1000, 0, 4, FAKE, None) == INVALID            # not a multiple of 16 bytes
+    assert f(FAKE, 0, 0, 4, FAKE, None) == INVALID               # empty
+    assert f(FAKE, 1024, 2, 4, FAKE, None) == INVALID            # bad policy flag
+    assert f(FAKE, 1024, 0, 0, FAKE, None) == INVALID            # no workgroups
+    assert f(FAKE, 1024, 0, 65536, FAKE, None) == INVALID        # too many
+    assert f(FAKE, 1024, 0, 4, None, None) == INVALID            # null sink
