@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=256, help="(batch, head) pairs the oracle decodes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-baseline", action="store_true")
-    p.add_argument("--sdpa", action="store_true",
-                   help="int2-8k: also time torch's SDPA (flash / memory-efficient backends) on the BF16 "
+    p.add_argument("--no-sdpa", action="store_true",
+                   help="int2-8k: skip timing torch's SDPA (flash / memory-efficient backends) on the BF16 "
                         "baseline's shapes")
     p.add_argument("--graphs", action="store_true",
                    help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
@@ -275,9 +275,9 @@ def copy_probe():
 
 def stream_probe(args):
     """The attainable HBM read rate: rq_probe_read_stream over a 4 GiB buffer
-    (16x the 256 MB Infinity Cache), default and non-temporal loads, 4 / 8 /
-    16 workgroups of 256 lanes per compute unit.  One JSON line per point,
-    then a summary line."""
+    (16x the 256 MB Infinity Cache), grid-stride and chunked patterns,
+    default and non-temporal loads, 4 / 8 / 16 workgroups of 256 lanes per
+    compute unit.  One JSON line per point, then a summary line."""
     import torch
     import decode_attention_rq_amd as rq
     nbytes = 4 << 30
@@ -285,17 +285,19 @@ def stream_probe(args):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     steps = args.steps if args.steps_given else 20
     best = {}
-    for nt in (0, 1):
-        for per_cu in (4, 8, 16):
-            sink = torch.empty(cus * per_cu * 256, dtype=torch.int32, device="cuda")
-            ms = timed(lambda i: rq.rq_probe_read_stream(buf, nt, sink), steps, 2)
-            gbs = nbytes / (ms / 1e3) / 1e9
-            row = {"mode": "stream", "nontemporal": nt, "workgroups_per_cu": per_cu, "ms_per_read": round(ms, 4),
-                   "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-            print(json.dumps(row), flush=True)
-            key = "nontemporal" if nt else "default"
-            if gbs > best.get(key, {}).get("gbs", 0):
-                best[key] = row
+    for pattern in (0, 1):
+        for nt in (0, 1):
+            for per_cu in (4, 8, 16):
+                sink = torch.empty(cus * per_cu * 256, dtype=torch.int32, device="cuda")
+                ms = timed(lambda i: rq.rq_probe_read_stream(buf, nt, sink, pattern), steps, 2)
+                gbs = nbytes / (ms / 1e3) / 1e9
+                row = {"mode": "stream", "pattern": ["grid-stride", "chunked"][pattern], "nontemporal": nt,
+                       "workgroups_per_cu": per_cu, "ms_per_read": round(ms, 4), "gbs": round(gbs, 1),
+                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                print(json.dumps(row), flush=True)
+                key = "nontemporal" if nt else "default"
+                if gbs > best.get(key, {}).get("gbs", 0):
+                    best[key] = row
     print(json.dumps({"mode": "stream", "bytes_per_read": nbytes, "best": best, "system": system_info()}), flush=True)
 
 
@@ -1200,7 +1202,7 @@ def main():
         res["batch_gain_at_equal_kv_memory"] = round(2 * w.n_loops * w.d * 2 / per_tok, 3)
         if bf.get("trials") and trials:
             res["speedup_vs_bf16_trials_mean"] = round(bf["trials"]["ms_mean"] / float(np.mean(trials)), 3)
-    if args.sdpa:
+    if not args.no_sdpa and not args.no_bf16_baseline:
         lay_b = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, n, w.rotate, w.bits)
         ws_b = rq.workspace_for(lay_b, n, splits, dev)
 

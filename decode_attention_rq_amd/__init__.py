@@ -70,7 +70,8 @@ _lib.rq_bf16_decode_attn.argtypes = [_P(rq_layout), _P(C.c_void_p), _P(C.c_void_
                                      C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.rq_probe_read_stream.restype = C.c_int
-_lib.rq_probe_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+_lib.rq_probe_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                      C.c_void_p]
 _lib.rq_reconstruct.restype = C.c_int
 _lib.rq_reconstruct.argtypes = [_P(rq_layout), _P(rq_cache), C.c_int32, C.c_int32, C.c_int32,
                                 C.c_void_p, C.c_void_p]
@@ -400,13 +401,14 @@ def workspace_for(layout: Layout, n_ctx: int, n_splits: int = 0, device="cuda") 
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def rq_probe_read_stream(buf: torch.Tensor, nontemporal: bool, sink: torch.Tensor, stream=None) -> None:
-    """Read all of buf once with 128-bit loads (include/rq_probe.h); sink is a
-    device int32/uint32 tensor whose length (a multiple of 256) sets the
-    number of workgroups."""
+def rq_probe_read_stream(buf: torch.Tensor, nontemporal: bool, sink: torch.Tensor, pattern: int = 0,
+                         stream=None) -> None:
+    """Read all of buf once with 128-bit loads (include/rq_probe.h): pattern 0
+    grid stride, 1 one contiguous chunk per workgroup; sink is a device int32
+    tensor whose length (a multiple of 256) sets the number of workgroups."""
     _tensor(buf, "buf", buf.dtype if isinstance(buf, torch.Tensor) else torch.uint8)
     _tensor(sink, "sink", torch.int32)
     if sink.numel() % 256 != 0:
         raise ValueError("sink: length must be a multiple of 256")
     _check(_lib.rq_probe_read_stream(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
-                                     sink.numel() // 256, _ptr(sink), _stream(stream)))
+                                     int(pattern), sink.numel() // 256, _ptr(sink), _stream(stream)))

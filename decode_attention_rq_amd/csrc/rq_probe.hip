@@ -19,9 +19,9 @@ __device__ __forceinline__ u32x4_t load16(const u32x4_t *p) {
 
 __device__ __forceinline__ uint32_t fold(u32x4_t v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
-// Every lane reads elements i, i + stride, ... of the buffer (stride = all
-// lanes of the grid), four independent loads per iteration, and writes the
-// XOR of everything it read.
+// Grid-stride pattern: every lane reads elements i, i + stride, ... of the
+// buffer (stride = all lanes of the grid), four independent loads per
+// iteration, and writes the XOR of everything it read.
 template <bool NT>
 __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t *p, uint64_t n16, uint32_t *sink) {
   const uint64_t stride = (uint64_t)gridDim.x * 256;
@@ -36,20 +36,46 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t *p, uint
   sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Chunked pattern: workgroup b reads the b-th of gridDim.x contiguous
+// chunks of the buffer, 16 KiB per iteration (four consecutive 4 KiB
+// segments, one 128-bit load per lane each), the way a decode workgroup
+// walks one (batch, head)'s token rows.
+template <bool NT>
+__global__ __launch_bounds__(256) void read_chunk_kernel(const u32x4_t *p, uint64_t n16, uint32_t *sink) {
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t begin = (uint64_t)blockIdx.x * per;
+  const uint64_t end = begin + per < n16 ? begin + per : n16;
+  uint64_t i = begin + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * 256 < end; i += 4 * 256) {
+    const u32x4_t a = load16<NT>(p + i), b = load16<NT>(p + i + 256);
+    const u32x4_t c = load16<NT>(p + i + 512), d = load16<NT>(p + i + 768);
+    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+  }
+  for (; i < end; i += 256) acc ^= fold(load16<NT>(p + i));
+  sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
-extern "C" rq_status rq_probe_read_stream(const void *buf, size_t bytes, int32_t nontemporal, int32_t n_blocks,
-                                          uint32_t *sink, void *hip_stream) {
+extern "C" rq_status rq_probe_read_stream(const void *buf, size_t bytes, int32_t nontemporal, int32_t pattern,
+                                          int32_t n_blocks, uint32_t *sink, void *hip_stream) {
   if (!aligned16(buf) || !aligned16(sink) || bytes < 16 || bytes % 16 != 0) return RQ_ERR_INVALID_ARG;
   if (n_blocks < 1 || n_blocks > 65535 || (nontemporal != 0 && nontemporal != 1)) return RQ_ERR_INVALID_ARG;
+  if (pattern != 0 && pattern != 1) return RQ_ERR_INVALID_ARG;
   (void)hipGetLastError();
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const u32x4_t *p = static_cast<const u32x4_t *>(buf);
-  if (nontemporal)
-    hipLaunchKernelGGL(read_stream_kernel<true>, dim3(n_blocks), dim3(256), 0, st, p, (uint64_t)(bytes / 16), sink);
-  else
-    hipLaunchKernelGGL(read_stream_kernel<false>, dim3(n_blocks), dim3(256), 0, st, p, (uint64_t)(bytes / 16), sink);
+  const uint64_t n16 = bytes / 16;
+  const dim3 grid(n_blocks), block(256);
+  if (pattern == 0) {
+    if (nontemporal) hipLaunchKernelGGL(read_stream_kernel<true>, grid, block, 0, st, p, n16, sink);
+    else hipLaunchKernelGGL(read_stream_kernel<false>, grid, block, 0, st, p, n16, sink);
+  } else {
+    if (nontemporal) hipLaunchKernelGGL(read_chunk_kernel<true>, grid, block, 0, st, p, n16, sink);
+    else hipLaunchKernelGGL(read_chunk_kernel<false>, grid, block, 0, st, p, n16, sink);
+  }
   return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_DEVICE;
 }

@@ -19,19 +19,21 @@ extern "C" {
 
 /*
  * rq_probe_read_stream -- read `bytes` bytes of `buf` once with 128-bit
- * loads (each of n_blocks workgroups of 256 lanes walks the buffer with a
- * grid stride, four loads in flight per lane) and write one 32-bit XOR of
- * what each lane read to sink[n_blocks * 256], so that no load is dead.
+ * loads, four loads in flight per lane, and write one 32-bit XOR of what
+ * each lane read to sink[n_blocks * 256], so that no load is dead.
  *   buf          device buffer, 16-byte aligned; bytes a multiple of 16, >= 16
  *   nontemporal  0: default cache policy; 1: loads with the non-temporal hint
  *                (the policy the decode kernel uses for its streamed planes)
- *   n_blocks     1 .. 65535 workgroups
+ *   pattern      0: grid stride (consecutive lanes of the whole grid read
+ *                consecutive 16 bytes); 1: chunked (workgroup b reads the
+ *                b-th of n_blocks contiguous chunks, 16 KiB per iteration)
+ *   n_blocks     1 .. 65535 workgroups of 256 lanes
  *   sink         device uint32 [n_blocks * 256], 16-byte aligned; written
  * Returns RQ_ERR_INVALID_ARG for a null, misaligned or mis-sized argument,
  * RQ_ERR_DEVICE if the launch fails.
  */
-rq_status rq_probe_read_stream(const void *buf, size_t bytes, int32_t nontemporal, int32_t n_blocks,
-                               uint32_t *sink, void *hip_stream);
+rq_status rq_probe_read_stream(const void *buf, size_t bytes, int32_t nontemporal, int32_t pattern,
+                               int32_t n_blocks, uint32_t *sink, void *hip_stream);
 
 #ifdef __cplusplus
 }

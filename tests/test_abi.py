@@ -360,11 +360,12 @@ def test_chain_decode_checks_every_link(rq):
 def test_read_stream_probe_rejects_bad_arguments(rq):
     f = rq._lib.rq_probe_read_stream
     INVALID = -1
-    assert f(None, 1024, 0, 4, FAKE, None) == INVALID            # null buffer
-    assert f(FAKE + 8, 1024, 0, 4, FAKE, None) == INVALID        # misaligned buffer
-    assert f(FAKE, 1000, 0, 4, FAKE, None) == INVALID            # not a multiple of 16 bytes
-    assert f(FAKE, 0, 0, 4, FAKE, None) == INVALID               # empty
-    assert f(FAKE, 1024, 2, 4, FAKE, None) == INVALID            # bad policy flag
-    assert f(FAKE, 1024, 0, 0, FAKE, None) == INVALID            # no workgroups
-    assert f(FAKE, 1024, 0, 65536, FAKE, None) == INVALID        # too many
-    assert f(FAKE, 1024, 0, 4, None, None) == INVALID            # null sink
+    assert f(None, 1024, 0, 0, 4, FAKE, None) == INVALID            # null buffer
+    assert f(FAKE + 8, 1024, 0, 0, 4, FAKE, None) == INVALID        # misaligned buffer
+    assert f(FAKE, 1000, 0, 0, 4, FAKE, None) == INVALID            # not a multiple of 16 bytes
+    assert f(FAKE, 0, 0, 0, 4, FAKE, None) == INVALID               # empty
+    assert f(FAKE, 1024, 2, 0, 4, FAKE, None) == INVALID            # bad policy flag
+    assert f(FAKE, 1024, 0, 2, 4, FAKE, None) == INVALID            # bad pattern
+    assert f(FAKE, 1024, 0, 0, 0, FAKE, None) == INVALID            # no workgroups
+    assert f(FAKE, 1024, 0, 1, 65536, FAKE, None) == INVALID        # too many
+    assert f(FAKE, 1024, 0, 1, 4, None, None) == INVALID            # null sink
