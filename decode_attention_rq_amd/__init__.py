@@ -65,6 +65,10 @@ _lib.rq_decode_attn_tail.restype = C.c_int
 _lib.rq_decode_attn_tail.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), _P(rq_tail), C.c_void_p,
                                      C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.rq_decode_attn_tail_noalloc.restype = C.c_int
+_lib.rq_decode_attn_tail_noalloc.argtypes = [_P(rq_layout), _P(rq_cache), _P(rq_cache), _P(rq_tail), C.c_void_p,
+                                             C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
+                                             C.c_void_p]
 _lib.rq_bf16_decode_attn.restype = C.c_int
 _lib.rq_bf16_decode_attn.argtypes = [_P(rq_layout), _P(C.c_void_p), _P(C.c_void_p), C.c_void_p,
                                      C.c_uint32, C.c_int32, C.c_float, C.c_int32, C.c_void_p,
@@ -360,6 +364,29 @@ def rq_decode_attn_tail(layout: Layout, k: Cache, v: Cache, tail: Optional[Tail]
                                     int(loop_mask), int(n_ctx), float(sm_scale), int(n_splits),
                                     _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # RQ_NOALLOC_SCRATCH_BYTES
+
+
+def rq_decode_attn_tail_noalloc(layout: Layout, k: Cache, v: Cache, tail: Optional[Tail], q: torch.Tensor,
+                                loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
+                                n_splits: int = 0, stream=None) -> None:
+    """rq_decode_attn_tail with the split records in the library's per-GPU
+    scratch instead of a caller workspace: nothing is allocated.  Calls that
+    may overlap on one GPU race on that scratch."""
+    _check_cache(layout, k, "k")
+    _check_cache(layout, v, "v")
+    _check_rows(layout, q, "q", torch.bfloat16)
+    _check_rows(layout, out, "out", torch.float32)
+    if tail is not None:
+        tail.check(layout)
+    lay, kc, vc = layout.c(), k.c(), v.c()
+    tc = tail.c() if tail is not None else None
+    _check(_lib.rq_decode_attn_tail_noalloc(C.byref(lay), C.byref(kc), C.byref(vc),
+                                            C.byref(tc) if tc is not None else None, _ptr(q),
+                                            int(loop_mask), int(n_ctx), float(sm_scale), int(n_splits),
+                                            _ptr(out), _stream(stream)))
 
 
 def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops: Sequence[torch.Tensor],

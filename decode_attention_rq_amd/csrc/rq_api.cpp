@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -341,16 +342,41 @@ size_t rq_decode_workspace_bytes(const rq_layout *L, int32_t n_ctx, int32_t n_sp
 
 }  // extern "C"
 
+// Split-record scratch of rq_decode_attn_tail_noalloc: one copy per GPU,
+// part of the library's code object.  On the host its name stands for the
+// symbol only; its device address (per device) comes from
+// hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[RQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call with that device current; nullptr on a HIP error.
+void *scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// workspace == nullptr with `noalloc`: the split records go to this
+// device's scratch (workspace_bytes is then its size).
 rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, const rq_tail *tail,
                       const void *q, uint32_t loop_mask, int32_t n_ctx, float sm_scale,
                       int32_t n_splits, float *out, void *workspace, size_t workspace_bytes,
-                      void *hip_stream) {
+                      void *hip_stream, bool noalloc = false) {
   rq_status st = check_layout(L);
   if (st != RQ_OK) return st;
   if (k == nullptr || v == nullptr) return RQ_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return RQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (!noalloc && !aligned16(workspace))) return RQ_ERR_INVALID_ARG;
   if (loop_mask == 0) return RQ_ERR_INVALID_ARG;
   if (L->n_loops < 32 && (loop_mask >> L->n_loops) != 0) return RQ_ERR_INVALID_ARG;
   const int n_tail = tail ? tail->n : 0;
@@ -428,6 +454,10 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int G = group_len(L);
   if (launch_fault_injected()) return RQ_ERR_DEVICE;
+  if (noalloc) {
+    a.ws = static_cast<float *>(scratch_on_current_device());
+    if (a.ws == nullptr) return RQ_ERR_DEVICE;
+  }
   (void)hipGetLastError();
   for (int g0 = 0; g0 < L->n_loops; g0 += G) {
     const int ref_loop = anchor_of(L, g0);    // this group's reference / anchor
@@ -520,6 +550,14 @@ rq_status rq_decode_attn_tail(const rq_layout *L, const rq_cache *k, const rq_ca
                               void *workspace, size_t workspace_bytes, void *hip_stream) {
   return decode_impl(L, k, v, tail, q, loop_mask, n_ctx, sm_scale, n_splits, out, workspace,
                      workspace_bytes, hip_stream);
+}
+
+rq_status rq_decode_attn_tail_noalloc(const rq_layout *L, const rq_cache *k, const rq_cache *v,
+                                      const rq_tail *tail, const void *q, uint32_t loop_mask,
+                                      int32_t n_ctx, float sm_scale, int32_t n_splits, float *out,
+                                      void *hip_stream) {
+  return decode_impl(L, k, v, tail, q, loop_mask, n_ctx, sm_scale, n_splits, out, nullptr,
+                     RQ_NOALLOC_SCRATCH_BYTES, hip_stream, true);
 }
 
 rq_status rq_bf16_decode_attn(const rq_layout *L, void *const *k_loops, void *const *v_loops,

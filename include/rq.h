@@ -252,6 +252,30 @@ rq_status rq_decode_attn_tail(const rq_layout *layout, const rq_cache *k, const 
                               int32_t n_ctx, float sm_scale, int32_t n_splits, float *out,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Device scratch of rq_decode_attn_tail_noalloc, per GPU. */
+#define RQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * rq_decode_attn_tail_noalloc -- rq_decode_attn_tail without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The split records live in a scratch array of RQ_NOALLOC_SCRATCH_BYTES
+ * compiled into the library: one copy per GPU, held until the process ends,
+ * located on the first call on each device.  Nothing is allocated or freed.
+ * Arguments and results are those of rq_decode_attn_tail (same kernels,
+ * same split choice); the scratch needs no initialisation.
+ *   Returns RQ_ERR_WORKSPACE when the call would need more scratch than
+ *   RQ_NOALLOC_SCRATCH_BYTES (rq_decode_workspace_bytes(layout, n_ctx,
+ *   n_splits) above it), RQ_ERR_DEVICE when the scratch cannot be located.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one device (different streams, different host threads) race and must be
+ * serialised by the caller.
+ */
+rq_status rq_decode_attn_tail_noalloc(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
+                                      const rq_tail *tail, const void *q, uint32_t loop_mask,
+                                      int32_t n_ctx, float sm_scale, int32_t n_splits, float *out,
+                                      void *hip_stream);
+
 /*
  * rq_reconstruct -- dequantize loop `loop` (< L-1) for tokens [t0, t0+n):
  *   out[b][h][t - t0] = alpha*y + H_n (z + s*code)          (FP32)

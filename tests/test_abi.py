@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["rq_encode", "rq_decode_workspace_bytes", "rq_decode_splits",
-                            "rq_decode_attn", "rq_decode_attn_tail", "rq_reconstruct",
+                            "rq_decode_attn", "rq_decode_attn_tail", "rq_decode_attn_tail_noalloc", "rq_reconstruct",
                             "rq_status_string", "rq_bf16_decode_attn", "rq_probe_read_stream"])
 
 
@@ -369,3 +369,26 @@ def test_read_stream_probe_rejects_bad_arguments(rq):
     assert f(FAKE, 1024, 0, 0, 0, FAKE, None) == INVALID            # no workgroups
     assert f(FAKE, 1024, 0, 1, 65536, FAKE, None) == INVALID        # too many
     assert f(FAKE, 1024, 0, 1, 4, None, None) == INVALID            # null sink
+
+
+def _noalloc(rq, lay, mask=0b1111, n_ctx=32, splits=2, tail=None):
+    L = lay.c()
+    k, v = _cache(rq, lay.n_loops), _cache(rq, lay.n_loops)
+    return rq._lib.rq_decode_attn_tail_noalloc(C.byref(L), C.byref(k), C.byref(v), tail, FAKE, mask, n_ctx, 0.1,
+                                               splits, FAKE, None)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(rq):
+    # 1024 (batch, head) pairs at head_dim 128: 4 splits need 16.9 MB of
+    # records (within the 32 MiB scratch), 8 splits 33.8 MB (beyond it)
+    lay = _layout(rq, batch=64, n_heads=16, capacity=4096)
+    assert rq.rq_decode_workspace_bytes(lay, 4096, 8) > rq.NOALLOC_SCRATCH_BYTES
+    assert rq.rq_decode_workspace_bytes(lay, 4096, 4) <= rq.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(rq, lay, n_ctx=4096, splits=8) == -3
+    assert _noalloc(rq, lay, n_ctx=4096, splits=4, mask=0) == -1           # still validated
+    assert _noalloc(rq, lay, n_ctx=0, splits=1) == -1                      # nothing to attend
+
+
+def test_noalloc_device_error_path(rq, monkeypatch):
+    monkeypatch.setenv("RQ_FAULT_INJECT", "launch")
+    assert _noalloc(rq, _layout(rq), n_ctx=32, splits=2) == -4
