@@ -54,10 +54,11 @@ def parse():
                         "baseline's shapes")
     p.add_argument("--graphs", action="store_true",
                    help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
-    p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep", "stream"],
+    p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep", "stream", "encode"],
                    help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling; "
                         "split-sweep: every token-split count against the automatic one; "
-                        "stream: the attainable HBM read rate (128-bit read-stream kernel)")
+                        "stream: the attainable HBM read rate (128-bit read-stream kernel); "
+                        "encode: the prefill rq_encode of the workload's layer alone")
     a = p.parse_args()
     global SETTLE_MS
     SETTLE_MS = a.settle_ms
@@ -341,6 +342,53 @@ def sdpa_baseline(w, n, steps, warmup, ours):
     del d, ks, vs, q
     torch.cuda.empty_cache()
     return res
+
+
+def encode_bytes_per_token(w) -> int:
+    """Bytes one rq_encode of a token moves per (batch, head): every loop's
+    BF16 K and V read once (the reference included), and every encoded
+    plane written (codes, FP16 scale and zero per group, FP16 LS
+    coefficient; a quantized anchor's codes and its scale and zero)."""
+    read = 2 * w.n_loops * w.d * 2
+    write = 2 * sum(w.d * b // 8 + 4 * (w.d // w.g) + 2 for b in w.bits[:w.n_loops - 1])
+    if w.ref_bits:
+        write += 2 * (w.d * w.ref_bits // 8 + 4 * (w.d // (w.ref_group or w.g)))
+    return read + write
+
+
+def encode_bench(args):
+    """The prefill write path alone: rq_encode of all n_ctx tokens of the
+    workload's layer (every loop, K and V) from inputs already in HBM,
+    after the settling work, mean over --steps calls.  Each call rewrites
+    the same slots with the same bytes."""
+    import torch
+    import decode_attention_rq_amd as rq
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    n = w.n_ctx
+    lay = rq.Layout(w.n_loops, w.batch, w.heads, w.d, w.g, n, w.rotate, w.bits, ref_bits=w.ref_bits,
+                    ref_group=w.ref_group, group_loops=w.group_loops, ref_first=w.ref_first,
+                    alpha_mode=w.alpha_mode, ref_chain=w.ref_chain)
+    d = synth.draw_layer(w, device="cuda")
+    k, v = rq.Cache(lay, "cuda", zero=False), rq.Cache(lay, "cuda", zero=False)
+    if w.ref_bits:
+        kin = torch.cat([d["k_loops"], d["k_ref"][None]]).contiguous()
+        vin = torch.cat([d["v_loops"], d["v_ref"][None]]).contiguous()
+    else:
+        k.ref.copy_(d["k_ref"])
+        v.ref.copy_(d["v_ref"])
+        kin, vin = d["k_loops"], d["v_loops"]
+    del d
+    torch.cuda.empty_cache()
+    steps = args.steps if args.steps_given else 10
+    ms = timed(lambda i: rq.rq_encode(lay, k, v, kin, vin, 0, n), steps, 2)
+    nbytes = w.batch * w.heads * n * encode_bytes_per_token(w)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({"mode": "encode", "workload": w.name, "tokens": w.batch * w.heads * n,
+                      "bits": w.bits, "ref_bits": w.ref_bits, "group": w.g, "ms_per_call": round(ms, 4),
+                      "algorithmic_bytes": nbytes, "bytes_per_token": encode_bytes_per_token(w),
+                      "hbm_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                      "system": system_info()}), flush=True)
 
 
 def system_info():
@@ -1079,6 +1127,9 @@ def main():
         return
     if args.mode == "stream":
         stream_probe(args)
+        return
+    if args.mode == "encode":
+        encode_bench(args)
         return
     if args.mode == "split-sweep":
         split_sweep()

@@ -39,8 +39,9 @@ def units():
     return out
 
 
-def _newest_dependency() -> float:
-    paths = [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
+def _newest_header() -> float:
+    """Newest of every header (csrc/*.hpp, include/*.h) and this script."""
+    paths = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
     inc = os.path.join(ROOT, "include")
     paths += [os.path.join(inc, f) for f in os.listdir(inc)]
     paths.append(os.path.abspath(__file__))
@@ -49,7 +50,7 @@ def _newest_dependency() -> float:
 
 def build(verbose: bool = False, jobs: int = 0, force: bool = True) -> str:
     """Compile every object and link librq.so.  force=False skips objects
-    newer than every source, header and this script (for development
+    newer than their source, every header and this script (for development
     rebuilds); the default compiles everything."""
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -58,12 +59,13 @@ def build(verbose: bool = False, jobs: int = 0, force: bool = True) -> str:
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-fno-gpu-rdc", "-munsafe-fp-atomics"]
     jobs = jobs or min(16, os.cpu_count() or 4)
-    newest = 0.0 if force else _newest_dependency()
+    headers = 0.0 if force else _newest_header()
     todo, objs = [], []
     for src, name, extra in units():
         obj = os.path.join(objdir, name)
         objs.append(obj)
-        if not force and os.path.exists(obj) and os.path.getmtime(obj) > newest:
+        if (not force and os.path.exists(obj)
+                and os.path.getmtime(obj) > max(headers, os.path.getmtime(os.path.join(CSRC, src)))):
             continue
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         todo.append((name, [hipcc()] + common + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
