@@ -540,11 +540,10 @@ def append_bench(args, w):
     step_in = [(kin[:, :, :, t:t + 1].contiguous(), vin[:, :, :, t:t + 1].contiguous()) for t in range(n0, cap)]
     del data, kin, vin
     torch.cuda.empty_cache()
-    # prefill: three untimed encodes of all n0 tokens (~12 ms: from idle the
-    # GPU's clocks take ~10 ms of work to settle), then the mean of three
-    # timed ones (each writes the same slots with the same values)
-    for _ in range(3):
-        rq.rq_encode(lay, k, v, pre_k, pre_v, 0, n0)
+    # prefill: untimed encodes of all n0 tokens until the clocks have
+    # settled, then the mean of three timed ones (each writes the same slots
+    # with the same values)
+    settle(lambda i: rq.rq_encode(lay, k, v, pre_k, pre_v, 0, n0))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
