@@ -55,6 +55,53 @@ __device__ __forceinline__ float quad_bcast(float x, int s) {
   }
 }
 
+// Lane j of a row owns loop slot j mod NP, NP = the pass's slot count
+// rounded up to 1, 2 or 4 (so the four lanes of a quad own slots 0..3).
+template <int NSC>
+constexpr int own_slots() { return NSC <= 1 ? 1 : NSC <= 2 ? 2 : 4; }
+
+// The row total of the partial scores of every slot, returned on each lane
+// for its own slot only: a reduce-scatter over the row's LANES lanes.  Lanes
+// j and j^1 swap half of the slots and add the half each keeps, lanes j and
+// j^2 the same with what is left; then the lanes that own the same slot
+// (j, j^4, j^8, ...) add theirs.  For four slots over 16 lanes that is 11
+// VALU instructions, where four all-lane butterflies (every lane receiving
+// every total) take 16.  All lanes that own a slot receive the same bits
+// (each addition pairs the same two values, IEEE addition commutes).
+template <int LANES, int NSC>
+__device__ __forceinline__ float own_slot_total(const float (&part)[NSC], int j) {
+  constexpr int NP = own_slots<NSC>();
+  if constexpr (NP == 1) {
+    return group_sum_dpp<LANES>(part[0]);
+  } else {
+    const bool b0 = (j & 1) != 0;
+    float x;
+    if constexpr (NP == 2) {
+      const float keep = b0 ? part[1] : part[0], send = b0 ? part[0] : part[1];
+      x = keep + dpp<kDppQuadXor1>(send);
+      x += dpp<kDppQuadXor2>(x);
+    } else {
+      float p3 = 0.0f;
+      if constexpr (NSC > 3) p3 = part[3];
+      const float ka = b0 ? part[1] : part[0], sa = b0 ? part[0] : part[1];
+      const float kb = b0 ? p3 : part[2], sb = b0 ? part[2] : p3;
+      const float A = ka + dpp<kDppQuadXor1>(sa);
+      const float B = kb + dpp<kDppQuadXor1>(sb);
+      const bool b1 = (j & 2) != 0;
+      const float keep = b1 ? B : A, send = b1 ? A : B;
+      x = keep + dpp<kDppQuadXor2>(send);
+    }
+    if constexpr (LANES == 8) {
+      x += xor_lane<4>(x);
+    } else {
+      x += dpp<kDppRowRor4>(x);
+      x += dpp<kDppRowRor8>(x);
+      if constexpr (LANES == 32) x += xor_lane<16>(x);
+    }
+    return x;
+  }
+}
+
 // First product of a dot chain: the three-operand v_dot2_f32_bf16 with an
 // inline zero accumulator (the builtin would zero a register first).
 __device__ __forceinline__ float dot2bf0(uint32_t a, uint32_t b) {
@@ -432,7 +479,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // loop slot own = j % 4 only, kept by the lanes that compute that slot's
   // exponentials (lane j of a quad computes slot j's weight; the quad shares
   // the four weights through DPP).
-  const int own = j & 3;
+  const int own = j & (own_slots<NSC>() - 1);
   // With a quantized anchor the residual slots fold the anchor's values into
   // their residual accumulator (both are code sums in the same domain), so
   // only the anchor's own slot keeps a reference accumulator (with offset
@@ -451,6 +498,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) ores[i][p] = 0.0f;
   }
+
+  // The running max of the lane's own slot.  The tail section below keeps
+  // the max of every slot (m); the token tiles keep only the own slot's, and
+  // every lane reads another slot's max from the lane of its quad that owns
+  // it (a slot's max is the same on all lanes of a row that own it).
+  float m_own = -FLT_MAX;
 
   // ---- the tail rows.  Scores use the BF16 query; values go to the
   // accumulator the output is finished from: the reference sums (original
@@ -474,6 +527,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
           dp = dot2bf(qw.w, kw.w, dp);
           const float tot = group_sum_dpp<LANES>(dp) * a.qscale;
           const float sc = valid ? tot : -INFINITY;
+          if (own == s) m_own = fmaxf(m_own, sc);
           if (sc > m[s]) {
             const float f = fexp2(m[s] - sc);
             m[s] = sc;
@@ -519,8 +573,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 
   auto process = [&](const Tile<TR, NRA, AQ> &T, int base, auto full_tile) {
     constexpr bool FULL = decltype(full_tile)::value;
-    // scores (log2 units)
-    float sc[TR][NSC];
+    // scores (log2 units) of the lane's own slot
+    float sc[TR];
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
       // Partial scores of this lane's 8 dims, in units of 1/qscale: the
@@ -567,47 +621,40 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         }
         part[i] = acc;
       }
-      const bool valid = FULL || base + u * ROWS + r < t_end;
-#pragma unroll
-      for (int s = 0; s < NSC; ++s) {
-        const float tot = group_sum_dpp<LANES>(part[s]) * a.qscale;
-        sc[u][s] = FULL ? tot : (valid ? tot : -INFINITY);
-      }
+      const bool valid = (FULL || base + u * ROWS + r < t_end) && own < NSC;
+      const float tot = own_slot_total<LANES, NSC>(part, j) * a.qscale;
+      sc[u] = (FULL && own_slots<NSC>() == NSC) ? tot : (valid ? tot : -INFINITY);
     }
 
     // online softmax; rescale only when the max grows by more than the slack.
-    // One test over all slots guards the (rarely taken) rescale code, so
-    // every score sum is complete before the branch and each sum's last lane
-    // move fuses into its add.
-    float mts[NSC];
-    bool grow = false;
+    // Each lane tests its own slot; the rescale (rarely taken) runs on the
+    // whole wave when any lane's slot grew, every lane taking each slot's
+    // new max from the lane of its quad that owns the slot (the slot's max
+    // is the same on every such lane of the row).
+    float mt = sc[0];
 #pragma unroll
-    for (int s = 0; s < NSC; ++s) {
-      mts[s] = sc[0][s];
+    for (int u = 1; u < TR; ++u) mt = fmaxf(mt, sc[u]);
+    if (__builtin_amdgcn_ballot_w64(mt > m_own + kRescaleSlack) != 0) {
 #pragma unroll
-      for (int u = 1; u < TR; ++u) mts[s] = fmaxf(mts[s], sc[u][s]);
-      grow |= mts[s] > m[s] + kRescaleSlack;
-    }
-    if (grow) {
+      for (int s = 0; s < NSC; ++s) {
+        const float mts = own_slots<NSC>() == 1 ? mt : quad_bcast(mt, s);
+        const float mos = own_slots<NSC>() == 1 ? m_own : quad_bcast(m_own, s);
+        if (mts > mos + kRescaleSlack) {
+          const float f = fexp2(mos - mts);
+          if (own == s) l_own *= f;
+          if (s >= OREF_FROM) {
 #pragma unroll
-    for (int s = 0; s < NSC; ++s) {
-      const float mt = mts[s];
-      if (mt > m[s] + kRescaleSlack) {
-        const float f = fexp2(m[s] - mt);
-        m[s] = mt;
-        if (own == s) l_own *= f;
-        if (s >= OREF_FROM) {
+            for (int p = 0; p < 8; ++p) oref[s][p] *= f;
+            if (AQ) zref *= f;
+          }
+          if (s < NRS) {
+            zacc[s] *= f;
 #pragma unroll
-          for (int p = 0; p < 8; ++p) oref[s][p] *= f;
-          if (AQ) zref *= f;
-        }
-        if (s < NRS) {
-          zacc[s] *= f;
-#pragma unroll
-          for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+            for (int p = 0; p < 8; ++p) ores[s][p] *= f;
+          }
         }
       }
-    }
+      m_own = mt > m_own + kRescaleSlack ? mt : m_own;
     }
 
     // values
@@ -624,13 +671,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
         code_halves<AINT4>(T.av[u], hv, sel2);
       }
       // one exponential per lane (slot own), shared across the quad
-      float x = sc[u][0] - m[0];
-#pragma unroll
-      for (int s = 1; s < NSC; ++s) {
-        const float xs = sc[u][s] - m[s];
-        x = own == s ? xs : x;
-      }
-      const float p_own = fexp2(x);
+      const float p_own = fexp2(sc[u] - m_own);
       l_own += p_own;
       float pq[NSC];
 #pragma unroll
@@ -706,6 +747,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) oref[NRS][p] = __builtin_fmaf(oref[NRS][p], (float)(1 << (24 - code_pos(p))), zref);
   }
+
+  // every slot's running max on every lane, for the merges
+#pragma unroll
+  for (int s = 0; s < NSC; ++s) m[s] = own_slots<NSC>() == 1 ? m_own : quad_bcast(m_own, s);
 
   // ---- merge rows, then waves -----------------------------------------------
   if constexpr (ROWS >= 2) merge_rows<LANES, NSC, NRS, OREF_FROM>(m, l_own, own, oref, ores);

@@ -46,6 +46,8 @@ constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
 
 constexpr int kDppQuadReverse = 0x1B;    // quad_perm [3,2,1,0]
+constexpr int kDppRowRor4 = 0x124;       // lane i <- lane (i - 4) mod 16 within each 16 lanes
+constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i - 8) mod 16
 
 // Value of `x` in lane (lane ^ mask).  Masks 1 and 2 are one DPP quad
 // permutation; 4 is the half-row mirror (i -> 7-i) after a quad reversal
