@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
-SETTLE_MS = 25.0        # untimed work before every timed measurement (see parse)
+SETTLE_MS = 250.0       # untimed work before every timed measurement (see parse)
 
 
 def parse():
@@ -33,11 +33,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=5)
-    # From idle the GPU's clocks take ~10 ms of back-to-back work to settle
-    # (kernel traces show the first ~30 int2-8k steps up to 30% slower), so
-    # after the warm-up steps every timed measurement first runs untimed
-    # steps until this much work is done, whatever --warmup says.
-    p.add_argument("--settle-ms", type=float, default=25.0)
+    # From idle the GPU's clocks take ~200 ms of back-to-back work to reach
+    # their steady state: interleaved rounds of 90 int2-8k steps (~25 ms
+    # each) run ~9 % slower in the first round and ~3 % slower in rounds
+    # 2-4 than from round 5 on.  So after the warm-up steps every timed
+    # measurement first runs untimed steps until this much work is done,
+    # whatever --warmup says.
+    p.add_argument("--settle-ms", type=float, default=250.0)
     p.add_argument("--trials", type=int, default=3,
                    help="trials of --trial-steps steps after the timed steps (the pages' protocol: "
                         "one warm-up, three trials, averaged)")
@@ -478,13 +480,14 @@ def trials_summary(ms, batch, nbytes):
             "frac_of_peak_mean": round(float(np.mean(nbytes / (a / 1e3) / 1e9)) / HBM_PEAK_GBS, 4)}
 
 
-def timed_graph(fn, steps, warmup, settle_ms=20.0):
+def timed_graph(fn, steps, warmup, settle_ms=None):
     """Mean ms per step of fn, captured once into a HIP graph (torch's
     CUDAGraph on the current stream) and replayed `steps` times after
     `warmup` replays, and after as many more as make ~settle_ms of work (the
-    GPU's clocks take ~10 ms of work to settle after the idle of a capture;
+    clocks settle only after a stretch of back-to-back work, see parse;
     short steps would otherwise be timed on the ramp); HIP events bracket the
     replays."""
+    settle_ms = SETTLE_MS if settle_ms is None else settle_ms
     import torch
     fn(0)
     torch.cuda.synchronize()
@@ -504,7 +507,7 @@ def timed_graph(fn, steps, warmup, settle_ms=20.0):
     e1.record()
     torch.cuda.synchronize()
     per = max(e0.elapsed_time(e1) / max(warmup, 1), 1e-3)
-    for i in range(min(500, int(settle_ms / per))):
+    for i in range(min(5000, int(settle_ms / per))):
         g.replay()
     torch.cuda.synchronize()
     e0.record()

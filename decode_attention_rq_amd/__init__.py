@@ -99,6 +99,16 @@ def _check(status: int) -> None:
         raise RQError(status)
 
 
+_GPU = None        # whether a GPU is present (looked up once)
+
+
+def _gpu_present() -> bool:
+    global _GPU
+    if _GPU is None:
+        _GPU = torch.cuda.is_available()
+    return _GPU
+
+
 def _tensor(t, name: str, dtype, shape=None, allow_none: bool = False) -> None:
     """ValueError unless t is a contiguous tensor of `dtype` and exactly
     `shape` (None: any shape), on the GPU when one is present."""
@@ -114,12 +124,23 @@ def _tensor(t, name: str, dtype, shape=None, allow_none: bool = False) -> None:
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if not t.is_cuda and torch.cuda.is_available():
+    if not t.is_cuda and _gpu_present():
         raise ValueError(f"{name}: must be a GPU tensor (device {t.device})")
 
 
 def _check_cache(layout: "Layout", c: "Cache", name: str) -> None:
-    """Every plane of c present has the dtype and shape `layout` gives it."""
+    """Every plane of c present has the dtype and shape `layout` gives it.
+    Checked once per (layout, planes) pair: the result is kept on the cache
+    object, keyed by the layout's fields and the identity and data pointer of
+    every plane (a plane replaced by another tensor is checked again)."""
+    key = (layout._key(), c._fingerprint())
+    if getattr(c, "_checked", None) == key:
+        return
+    _check_cache_planes(layout, c, name)
+    c._checked = key
+
+
+def _check_cache_planes(layout: "Layout", c: "Cache", name: str) -> None:
     B, H, d, cap = layout.batch, layout.n_heads, layout.head_dim, layout.capacity
     if len(c.codes) != layout.n_loops or len(c.meta) != layout.n_loops or len(c.alpha) != layout.n_loops:
         raise ValueError(f"{name}: planes for {len(c.codes)} loops, layout has {layout.n_loops}")
@@ -176,7 +197,17 @@ class Layout:
         G = self.group_loops or self.n_loops
         return l % G == (0 if self.ref_first else G - 1)
 
+    def _key(self) -> tuple:
+        return (self.n_loops, self.batch, self.n_heads, self.head_dim, self.group, self.capacity, self.rotate,
+                tuple(self.bits), self.ref_bits, self.ref_group, self.group_loops, self.ref_first,
+                self.alpha_mode, self.ref_chain)
+
     def c(self) -> rq_layout:
+        """The C struct (built once per set of field values)."""
+        key = self._key()
+        memo = self.__dict__.get("_c_memo")
+        if memo is not None and memo[0] == key:
+            return memo[1]
         s = rq_layout(self.n_loops, self.batch, self.n_heads, self.head_dim, self.group,
                       self.capacity, self.rotate)
         for i, b in enumerate(list(self.bits)[:RQ_MAX_LOOPS]):
@@ -187,6 +218,7 @@ class Layout:
         s.ref_first = int(self.ref_first)
         s.alpha_mode = int(self.alpha_mode)
         s.ref_chain = int(self.ref_chain)
+        self.__dict__["_c_memo"] = (key, s)
         return s
 
 
@@ -233,7 +265,17 @@ class Cache:
                     self.meta.append(new(B, H, cap, d // g, 2, dtype=torch.float16, device=device))
                     self.alpha.append(new(B, H, cap, dtype=torch.float16, device=device))
 
+    def _fingerprint(self) -> tuple:
+        """Identity and data pointer of every plane (absent planes: None)."""
+        return tuple(None if t is None else (id(t), t.data_ptr())
+                     for t in [self.ref, *self.codes, *self.meta, *self.alpha])
+
     def c(self) -> rq_cache:
+        """The C struct (rebuilt when a plane is replaced)."""
+        fp = self._fingerprint()
+        memo = self.__dict__.get("_c_memo")
+        if memo is not None and memo[0] == fp:
+            return memo[1]
         s = rq_cache()
         s.ref = _ptr(self.ref)
         for l in range(len(self.codes)):
@@ -241,6 +283,7 @@ class Cache:
             s.meta[l] = _ptr(self.meta[l])
         for l in range(len(self.alpha)):
             s.alpha[l] = _ptr(self.alpha[l])
+        self.__dict__["_c_memo"] = (fp, s)
         return s
 
     def batch_view(self, b0: int, b1: int, layout: Layout) -> "Cache":
@@ -329,13 +372,28 @@ class Tail:
         if self.n < 0 or self.n > self.capacity:
             raise ValueError(f"tail: n = {self.n} outside [0, capacity {self.capacity}]")
 
+    def _fingerprint(self) -> tuple:
+        return (self.n, self.capacity) + tuple(None if t is None else (id(t), t.data_ptr())
+                                               for t in [*self.k, *self.v])
+
     def check(self, layout: "Layout") -> None:
+        key = (layout._key(), self._fingerprint())
+        if self.__dict__.get("_checked") == key:
+            return
+        self._check_planes(layout)
+        self.__dict__["_checked"] = key
+
+    def _check_planes(self, layout: "Layout") -> None:
         for side, planes in (("k", self.k), ("v", self.v)):
             for l, t in enumerate(planes):
                 _tensor(t, f"tail.{side}[{l}]", torch.bfloat16,
                         (layout.batch, layout.n_heads, self.capacity, layout.head_dim), allow_none=True)
 
     def c(self) -> rq_tail:
+        fp = self._fingerprint()
+        memo = self.__dict__.get("_c_memo")
+        if memo is not None and memo[0] == fp:
+            return memo[1]
         s = rq_tail()
         for l, t in enumerate(self.k):
             s.k[l] = _ptr(t)
@@ -343,6 +401,7 @@ class Tail:
             s.v[l] = _ptr(t)
         s.capacity = self.capacity
         s.n = self.n
+        self.__dict__["_c_memo"] = (fp, s)
         return s
 
 

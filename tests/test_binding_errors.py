@@ -137,6 +137,6 @@ def test_tail_planes_must_share_one_capacity():
 def test_binding_rejects_host_tensors_when_a_gpu_is_present(monkeypatch):
     lay = _lay()
     k, v, q, out, ws = _decode_args(lay)
-    monkeypatch.setattr(torch.cuda, "is_available", lambda: True)
+    monkeypatch.setattr(rq, "_GPU", True)
     with pytest.raises(ValueError, match="GPU tensor"):
         rq.rq_decode_attn(lay, k, v, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)

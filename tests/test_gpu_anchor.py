@@ -242,14 +242,14 @@ def test_anchor_perloop_full_size(oracle, wname):
     """The per-loop workloads at full size (batch 16, 16 heads, 8192 cached
     tokens + 64 BF16 tail tokens, INT4 anchor g=32, INT2 residuals g=16; Last-
     loop references, or Next-loop chains), in the launch configuration the
-    benchmark uses, on sampled (batch, head) pairs: bytes of the sampled
-    pairs, then every loop's row, one loop per call."""
+    benchmark uses, on one whole batch row of heads and two corner pairs:
+    bytes of those pairs, then every loop's row, one loop per call."""
     import decode_attention_rq_amd as rq
     w = synth.WORKLOADS[wname]
     T = w.extra["tail"]
     n = w.n_ctx
     case = Case(w, n, gen_device="cuda")
-    pairs = [(0, 0), (9, 13), (15, 15)]
+    pairs = [(9, h) for h in range(w.heads)] + [(0, 0), (15, 15)]
     lay, kp, vp, qb = case.oracle_planes(oracle, pairs)
     for side, planes in (("k", kp), ("v", vp)):
         gc = getattr(case, side)
