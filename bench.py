@@ -854,6 +854,7 @@ def anchor_bench(args, w):
     steps = args.steps
     for i in range(args.warmup):
         step(i)
+    settled = settle(step, args.warmup)
     # The step rate: two events around the steps (an event marker between two
     # kernels idles the GPU for ~5 us, so the calls are not timed one by one
     # here).
@@ -871,8 +872,7 @@ def anchor_bench(args, w):
     # the anchor loop's call.
     call_ms = np.zeros((1, L))
     for l in range(L):
-        for i in range(3):
-            call(i, l)
+        settle(lambda i: call(i, l), settle_ms=SETTLE_MS / 4)
         e0.record()
         for i in range(steps):
             call(i, l)
@@ -907,7 +907,8 @@ def anchor_bench(args, w):
                                   f"{n} cached tokens + {T} BF16 tail tokens, one call per loop",
                       "splits": splits, "replicas": args.replicas},
            "bytes_per_step": step_bytes, "hbm_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
-           "frac_of_peak": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof}
+           "frac_of_peak": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof,
+           "settle": {"steps": settled, "target_ms": SETTLE_MS}}
     # all four loops in one call (when every loop's query is known at once)
     def fstep(i):
         k, v, tail, q = reps[i % len(reps)]
