@@ -614,8 +614,10 @@ def append_bench(args, w):
         ks = [d2["k_loops"][l] for l in range(w.n_loops - 1)] + [d2["k_ref"]]
         vs = [d2["v_loops"][l] for l in range(w.n_loops - 1)] + [d2["v_ref"]]
         lay_b = layout_of(w, w.batch, cap)
-        ms = timed(lambda i: rq.rq_bf16_decode_attn(lay_b, ks, vs, d2["q"], mask, n0 + i + 1, scale, out, ws,
-                                                    rq.rq_decode_splits(lay_b, n0 + i + 1)), steps, 3)
+        # step i attends n0 + (i mod steps) + 1 tokens (the settling calls
+        # cycle through the same context lengths)
+        ms = timed(lambda i: rq.rq_bf16_decode_attn(lay_b, ks, vs, d2["q"], mask, n0 + i % steps + 1, scale, out,
+                                                    ws, rq.rq_decode_splits(lay_b, n0 + i % steps + 1)), steps, 3)
         res["bf16_baseline"] = {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4)}
         res["speedup_vs_bf16"] = round(res["value"] / res["bf16_baseline"]["value"], 3)
     if not args.no_cpu_baseline:
