@@ -532,7 +532,10 @@ def append_bench(args, w):
 
     dev = "cuda"
     n0, steps = w.n_ctx, w.steps
-    cap = n0 + steps
+    # capacity for the prefill and the appends, rounded up to a multiple of
+    # 256 tokens (per-(batch, head) plane strides that are not slow the
+    # decode by 5-10 %; see include/rq.h)
+    cap = -(-(n0 + steps) // 256) * 256
     lay = layout_of(w, w.batch, cap)
     data = synth.draw_layer(w, n=cap, device=dev)
     k, v = rq.Cache(lay, dev), rq.Cache(lay, dev)
@@ -540,7 +543,7 @@ def append_bench(args, w):
     v.ref.copy_(data["v_ref"])
     kin, vin, q = data["k_loops"], data["v_loops"], data["q"].contiguous()
     pre_k, pre_v = kin[:, :, :, :n0].contiguous(), vin[:, :, :, :n0].contiguous()
-    step_in = [(kin[:, :, :, t:t + 1].contiguous(), vin[:, :, :, t:t + 1].contiguous()) for t in range(n0, cap)]
+    step_in = [(kin[:, :, :, t:t + 1].contiguous(), vin[:, :, :, t:t + 1].contiguous()) for t in range(n0, n0 + steps)]
     del data, kin, vin
     torch.cuda.empty_cache()
     # prefill: untimed encodes of all n0 tokens until the clocks have
