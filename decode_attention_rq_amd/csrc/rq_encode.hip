@@ -216,21 +216,49 @@ __device__ __forceinline__ void rotate_canonical(float (&v)[EPL], int rotate, fl
   }
 }
 
+// range / L for the level count L = 2^b - 1 (3 or 15) of a group's range
+// x >= 0, bit-identical to the IEEE quotient without a divide sequence:
+// q = RN(x * RN(1/L)) is within an ulp of x / L, the residual x - q*L is exact
+// in one fma, and one fma correction rounds to the quotient.  The identity
+// holds for every float x in [0, 2^120] and both level counts (an exhaustive
+// host check in the test suite); a larger range, infinite included, is
+// clamped to 2^120 first, whose quotient saturates binary16 as the IEEE one
+// does.
+template <int L>
+__device__ __forceinline__ float div_levels(float x) {
+  constexpr float r = 1.0f / (float)L;
+  x = fminf(x, 0x1p120f);
+  const float q = x * r;
+  const float e = __builtin_fmaf(-q, (float)L, x);
+  return __builtin_fmaf(e, r, q);
+}
+
+// 1/s for a stored binary16 scale s > 0, bit-identical to the IEEE quotient:
+// v_rcp_f32 is within an ulp of 1/s, and one fma Newton step from any value
+// within 2 ulp rounds to 1/s for every positive finite binary16 s (an
+// exhaustive host check in the test suite).
+__device__ __forceinline__ float recip_f16_value(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-r0, s, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
+
 // One group of N values of the lane (rotated if the layout rotates, -0
 // already canonicalised to +0): min/max, then the FP16 scale s = (max-min)/
 // (2^b - 1) and offset z = min as stored, and the factor the codes use, 1/s
-// (0 when the stored scale is 0, which makes every code 0).
-template <int N>
-__device__ __forceinline__ void group_params(const float *u, float levels, uint32_t &sz, float &s, float &z,
-                                             float &inv) {
+// (0 when the stored scale is 0, which makes every code 0).  Both conversions
+// round to nearest even and saturate at +-65504: clamping to +-65504 first and
+// converting gives the same half as converting and replacing an infinity.
+template <int N, int L>
+__device__ __forceinline__ void group_params(const float *u, uint32_t &sz, float &s, float &z, float &inv) {
   float mn = u[0], mx = u[0];
 #pragma unroll
   for (int p = 1; p < N; ++p) { mn = fminf(mn, u[p]); mx = fmaxf(mx, u[p]); }
-  const uint32_t s16 = f32_to_f16_sat((mx - mn) / levels);
-  const uint32_t z16 = f32_to_f16_sat(mn);
+  const uint32_t s16 = __builtin_bit_cast(uint16_t, (_Float16)fminf(div_levels<L>(mx - mn), 65504.0f));
+  const uint32_t z16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_fmed3f(mn, -65504.0f, 65504.0f));
   s = f16_to_f32(s16);
   z = f16_to_f32(z16);
-  inv = s != 0.0f ? 1.0f / s : 0.0f;
+  inv = s != 0.0f ? recip_f16_value(s) : 0.0f;
   sz = s16 | (z16 << 16);
 }
 
@@ -241,41 +269,49 @@ __device__ __forceinline__ void group_params(const float *u, float levels, uint3
 // DEQ, u becomes the dequantized values fma(code, s, z) (for a reference
 // that a later step rebuilds).
 //
-// Codes are not kept: each code (a small integer in FP32) is added into a
-// 16-bit field of its packed word, held as an exact FP32 integer (sum of
-// code * 2^(b*i) < 2^16), so packing costs one FMA per code plus two
-// conversions and a shift-or per 32-bit word.  cr / mr address the code and
-// meta planes from the wave's first token; tok is the lane's token relative
-// to it.
+// Clamping before rounding gives the same code as rounding first, as both
+// bounds are integers.  v_cvt_pk_u8_f32 rounds to nearest even (the default
+// mode) and writes the code into a chosen byte of a word, so one instruction
+// per code rounds and places it: byte i of plane word m collects the codes
+// that land in byte i of an output word, and shifted ORs of the planes
+// interleave them into 2- or 4-bit fields.  cr / mr address the code and meta
+// planes from the wave's first token; tok is the lane's token relative to it.
 template <int D, int BITS, bool DEQ>
 __device__ __forceinline__ void quantize_pack(float (&u)[EPL], int group, __amdgpu_buffer_rsrc_t cr,
                                               __amdgpu_buffer_rsrc_t mr, uint32_t tok, int j, bool valid) {
-  constexpr float levels = (float)((1 << BITS) - 1);
-  constexpr int PER_HALF = 16 / BITS;                 // codes per 16-bit field
-  constexpr int NH = EPL / PER_HALF;                  // 16-bit fields per lane
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int PER_BYTE = 8 / BITS;                  // codes per output byte
+  constexpr int NW = EPL * BITS / 32;                 // output words per lane
   uint32_t sz[2];
   float sc[2], z[2], inv[2];
   if (group == 32) {
-    group_params<32>(u, levels, sz[0], sc[0], z[0], inv[0]);
+    group_params<32, L>(u, sz[0], sc[0], z[0], inv[0]);
     sz[1] = sz[0]; sc[1] = sc[0]; z[1] = z[0]; inv[1] = inv[0];
   } else {
-    group_params<16>(u, levels, sz[0], sc[0], z[0], inv[0]);
-    group_params<16>(u + 16, levels, sz[1], sc[1], z[1], inv[1]);
+    group_params<16, L>(u, sz[0], sc[0], z[0], inv[0]);
+    group_params<16, L>(u + 16, sz[1], sc[1], z[1], inv[1]);
   }
-  float h[NH];
-#pragma unroll
-  for (int f = 0; f < NH; ++f) h[f] = 0.0f;
+  // plane[k][m], byte i = code 32*k/BITS + PER_BYTE*i + m of the lane
+  uint32_t plane_w[NW][PER_BYTE];
 #pragma unroll
   for (int p = 0; p < EPL; ++p) {
     const int g = p / 16;
-    const float c = __builtin_amdgcn_fmed3f(__builtin_rintf((u[p] - z[g]) * inv[g]), 0.0f, levels);
-    h[p / PER_HALF] = __builtin_fmaf(c, (float)(1 << (BITS * (p % PER_HALF))), h[p / PER_HALF]);
-    if constexpr (DEQ) u[p] = __builtin_fmaf(c, sc[g], z[g]);
+    const int k = p / (32 / BITS), i = (p % (32 / BITS)) / PER_BYTE, m = p % PER_BYTE;
+    float c = __builtin_amdgcn_fmed3f((u[p] - z[g]) * inv[g], 0.0f, (float)L);
+    if constexpr (DEQ) {
+      c = __builtin_rintf(c);
+      u[p] = __builtin_fmaf(c, sc[g], z[g]);
+    }
+    plane_w[k][m] = __builtin_amdgcn_cvt_pk_u8_f32(c, i, i == 0 ? 0u : plane_w[k][m]);
   }
   if (!valid) return;
-  uint32_t w[NH / 2];
+  uint32_t w[NW];
 #pragma unroll
-  for (int k = 0; k < NH / 2; ++k) w[k] = (uint32_t)h[2 * k] | ((uint32_t)h[2 * k + 1] << 16);
+  for (int k = 0; k < NW; ++k) {
+    w[k] = plane_w[k][0];
+#pragma unroll
+    for (int m = 1; m < PER_BYTE; ++m) w[k] = (plane_w[k][m] << (BITS * m)) | w[k];
+  }
   if constexpr (BITS == 2) {
     const u32x2_t v = {w[0], w[1]};
     __builtin_amdgcn_raw_buffer_store_b64(v, cr, tok * (D / 4) + 8 * j, 0, 0);
