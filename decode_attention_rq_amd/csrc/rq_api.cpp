@@ -146,9 +146,9 @@ int decode_slots(int head_dim) {
 //    slots, but no more than about sqrt(n_ctx / 32): every workgroup runs at
 //    once, and the step is one workgroup's chain of tiles plus a merge that
 //    grows with the split count (8 splits at 2k, 16 from 8k on; never under
-//    256 tokens per split).  If those workgroups would not fit one per
-//    compute unit but 8 or more splits would, the most that fit are taken
-//    (they then run 8 waves each).
+//    256 tokens per split).  When 8 or more splits fit one workgroup per
+//    compute unit, the most that fit are taken instead (they then run 8
+//    waves each).
 //  * Large batch: a decode step is bound by HBM, and a partial last round of
 //    workgroups still streams at full rate once it holds half the slots.  So
 //    among 1..4 splits take the fewest rounds-equivalent of work, counting a
@@ -169,9 +169,11 @@ int auto_splits(const rq_layout *L, int n_ctx, int slots, int cus) {
     if (lat > 16) lat = 16;
     best = fill < lat ? fill : lat;
     // Workgroups that fit one per compute unit run with 8 waves (see
-    // decode_waves); when `best` does not fit but 8 or more splits would,
-    // take the most that fit: as many waves per unit, half the records.
-    if (cus > 0 && best * bh > cus && cus / bh >= 8) best = cus / bh;
+    // decode_waves); when 8 or more splits fit, take the most that fit, so
+    // each 8-wave workgroup has the fewest tiles to chain (batch 1 at 4k,
+    // per-loop calls with a tail: 16 splits 7% faster than 11; at 2k the
+    // 256-token floor keeps 8, as fast as 16 there).
+    if (cus > 0 && cus / bh >= 8) best = cus / bh;
   } else {
     double best_cost = -1.0;
     for (int64_t sp = 1; sp <= 4; ++sp) {
@@ -437,14 +439,14 @@ rq_status decode_impl(const rq_layout *L, const rq_cache *k, const rq_cache *v, 
   a.tcap = tail ? tail->capacity : 0;
   a.out_mask = loop_mask;
   decode_waves(S, a.bh, &a.wide, &a.waves8);
-  // The BF16 tail: with one workgroup per (b,h) (one split, or the wide
-  // form of two) the decode kernel attends it and finishes the rows.  With
-  // 8-wave splits (small batch) the first split attends it as more tokens of
-  // its own, and the merge kernel has no tail to walk (batch 1-2: 2-8%
-  // faster per call).  With 4-wave splits the first split's extra rows
-  // lengthened the step (batch 4-8: 1-3% slower), so the merge kernel walks
-  // the tail.  (A call over the tail alone runs the merge kernel only.)
-  a.tail_in = (n_tail > 0 && S > 0 && (S == 1 || a.wide || a.waves8)) ? 1 : 0;
+  // The BF16 tail is attended by the decode kernel: with one workgroup per
+  // (b,h) (one split, or the wide form of two) by that workgroup, which
+  // finishes the rows; with several splits each split takes an equal share
+  // of the tail rows as more tokens of its own, so the merge kernel has no
+  // tail to walk.  (Against the first split taking the whole tail, per-loop
+  // calls with a 64-row tail: 6-9% faster at batch 1-2, 2k; 4-6% at batch 4,
+  // 2k and 8k.)  A call over the tail alone runs the merge kernel only.
+  a.tail_in = (n_tail > 0 && S > 0) ? 1 : 0;
   a.records = (S > 1 && !a.wide) ? 1 : 0;
   a.group = L->group;
   a.rotate = L->rotate;

@@ -20,12 +20,12 @@
 // lane, ROWS = 64/(D/8) tokens side by side, so one 128-bit load per lane
 // reads ROWS consecutive reference rows, and every loop of the pass shares
 // that load.  Online softmax per (row, loop) in the exp2 domain; rows, then
-// waves (through LDS), are merged by log-sum-exp.  The first split may also
-// attend the BF16 tail rows.  With one split the workgroup finishes the
-// output itself (un-rotation of the residual accumulator, normalisation);
-// with several it writes one record per (split, loop, batch*head) to the
-// workspace and kernel M merges the records (and the tail, if the first
-// split did not take it).
+// waves (through LDS), are merged by log-sum-exp.  The splits also attend
+// the BF16 tail rows, an equal share each.  With one split the workgroup
+// finishes the output itself (un-rotation of the residual accumulator,
+// normalisation); with several it writes one record per (split, loop,
+// batch*head) to the workspace and kernel M merges the records.  (Kernel M
+// alone attends a tail with no cache tokens before it.)
 
 #pragma once
 
@@ -418,16 +418,19 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   Tile<TR, NRA, AQ> ta, tb;
   load(ta, base);
 
-  // BF16 tail rows (the first split's workgroup attends them, as more tokens
-  // of its split): each wave takes every W-th group of ROWS rows, TG groups
-  // per chunk, every loop slot's rows at once.  Slots whose loop is not asked
-  // for (chain links) have no tail.
+  // BF16 tail rows: split s attends rows [tail0, tail1), an equal share of the
+  // tail per split (as more tokens of its own), so that no split's chain of
+  // work is longer than the others'.  Each wave takes every W-th group of
+  // ROWS rows of the share, TG groups per chunk, every loop slot's rows at
+  // once.  Slots whose loop is not asked for (chain links) have no tail.
   constexpr int TG = 2;
+  const int tshare = a.tail_in ? (a.n_tail + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int tail0 = split * tshare, tail1 = min(tail0 + tshare, a.n_tail);
   uint4 tkw[TG][NSC], tvw[TG][NSC];
   auto load_tail = [&](int t0) {
 #pragma unroll
     for (int g = 0; g < TG; ++g) {
-      const uint32_t t = (uint32_t)min(t0 + g * W * ROWS + r, a.n_tail - 1);
+      const uint32_t t = (uint32_t)min(t0 + g * W * ROWS + r, tail1 - 1);
 #pragma unroll
       for (int s = 0; s < NSC; ++s) {
         if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;
@@ -437,8 +440,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
       }
     }
   };
-  const bool tail_here = a.tail_in && split == 0;
-  if (tail_here) load_tail(wave * ROWS);
+  const bool tail_here = a.tail_in && tail0 < tail1;
+  if (tail_here) load_tail(tail0 + wave * ROWS);
 
   // BF16 reference: its dots use the BF16 query pairs as stored (qb).
   // Code dots (residual loops, and with a quantized anchor the anchor too)
@@ -512,11 +515,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const DecodeArgs a) {
   // so those rows enter as c H v times those factors (finish_row un-rotates
   // them back).
   if (tail_here) {
-    for (int t0 = wave * ROWS; t0 < a.n_tail; t0 += TG * W * ROWS) {
-      if (t0 != wave * ROWS) load_tail(t0);
+    for (int t0 = tail0 + wave * ROWS; t0 < tail1; t0 += TG * W * ROWS) {
+      if (t0 != tail0 + wave * ROWS) load_tail(t0);
 #pragma unroll
       for (int g = 0; g < TG; ++g) {
-        const bool valid = t0 + g * W * ROWS + r < a.n_tail;
+        const bool valid = t0 + g * W * ROWS + r < tail1;
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
           if (!((a.out_mask >> a.qloop[s]) & 1u)) continue;   // a chain link not asked for
@@ -859,7 +862,7 @@ static hipError_t launch_kernel(const DecodeArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.records) return e;
   DecodeArgs m = a;
-  if (a.tail_in) m.n_tail = 0;        // already in the first split's records
+  if (a.tail_in) m.n_tail = 0;        // already in the splits' records
   if constexpr (CHAIN == 2) return launch_merge(m, D, 1, 1, st);
   return launch_merge(m, D, NR, NR + (REF ? 1 : 0), st);
 }

@@ -84,7 +84,7 @@ struct DecodeArgs {
   int32_t wide;                      // run the two splits as one 8-wave workgroup per batch*head,
                                      // no records (two splits, no tail)
   int32_t waves8;                    // 8-wave workgroups per split (else 4)
-  int32_t tail_in;                   // the first split's workgroup attends the BF16 tail
+  int32_t tail_in;                   // the splits attend the BF16 tail, an equal share each
   uint32_t out_mask;                 // loops whose rows are written (a chain pass also
                                      // computes the links between them and the root)
   int32_t bh, cap, n_ctx, n_splits, tps;

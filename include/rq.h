@@ -243,11 +243,10 @@ typedef struct {
  *   tail       NULL or a tail; tail->n == 0 makes this call rq_decode_attn
  *   n_ctx      0 <= n_ctx <= capacity, n_ctx + tail->n >= 1 (n_ctx = 0: the
  *              tail alone; no cache plane is read)
- * The tail is meant for tens of tokens: it is attended by one workgroup per
- * (b, h), not spread over the splits -- the one workgroup of the (b, h) when
- * a call has one per (b, h) (one split, or two run as one 8-wave workgroup);
- * the first split's workgroup when splits run 8 waves each; otherwise the
- * merge step's four waves per (b, h, loop).
+ * The tail is meant for tens of tokens: the decode kernel attends it, the one
+ * workgroup of the (b, h) when a call has one per (b, h) (one split, or two
+ * run as one workgroup), otherwise every split an equal share of the tail
+ * rows.  With n_ctx = 0 the merge step attends it alone.
  */
 rq_status rq_decode_attn_tail(const rq_layout *layout, const rq_cache *k, const rq_cache *v,
                               const rq_tail *tail, const void *q, uint32_t loop_mask,
