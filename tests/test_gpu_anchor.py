@@ -221,6 +221,23 @@ def test_bf16_reference_with_tail(oracle, waves, T, mask):
         _check(oracle, case, got, mask, 500, tk, tv)
 
 
+@pytest.mark.parametrize("anchored", [False, True])
+def test_tail_shared_over_many_splits(oracle, waves, anchored):
+    """Each split attends an equal share of the tail rows: tails shorter than
+    the split count (the last splits have none), one row per split, and a
+    ragged last share; fused and per loop, under every workgroup shape."""
+    w = _w() if anchored else synth.Workload("b", n_loops=4, batch=2, heads=3, d=128, g=32, n_ctx=0,
+                                             bits=[2, 4, 2], c=[0.8, 0.85, 0.9],
+                                             sigma=[0.15, 0.12, 0.1], rotate=1, seed=45)
+    n = 900
+    case = Case(w, n, cap=n + 4)
+    for T, s in ((1, 7), (5, 13), (13, 13), (70, 24)):
+        tk, tv = _tail(w, case.B, T, seed=T)
+        for mask in (0b1111, 0b0010):
+            got = _run(case, mask, n, tk, tv, T, splits=s)
+            _check(oracle, case, got, mask, n, tk, tv)
+
+
 def test_tail_of_zero_tokens_is_plain_decode():
     import decode_attention_rq_amd as rq
     w = _w()
