@@ -898,8 +898,9 @@ def anchor_bench(args, w):
             "unit": "GB/s", "frac": round(res_call / (res_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
             "kernel": "a residual loop's call (mean over the three): decode_kernel against the INT4 anchor"
                       + (" along the reference chain" if w.ref_chain else "")
-                      + " and the BF16 tail (one 8-wave workgroup per (b,h) attends both when the call has two"
-                        " splits; otherwise decode_merge_kernel merges the split records with the tail)",
+                      + " and the BF16 tail (with two splits over these 256 batch*heads the call runs as one"
+                        " workgroup per (b,h) over all tokens and the tail; with more, each split takes a share"
+                        " of the tail and decode_merge_kernel merges the split records)",
             "algorithmic_bytes_per_launch": res_call, "launch_us_mean": round(res_us, 2),
             "anchor_loop_call_us_mean": round(float(call_ms[:, L - 1].mean()) * 1e3, 2)}
     res = {"metric": "per-loop decode tokens/s, [2,2,2,4] INT4 anchor + INT2 residuals g=16, 8k ctx + 64 BF16 tail"
