@@ -56,6 +56,11 @@ def parse():
                         "baseline's shapes")
     p.add_argument("--graphs", action="store_true",
                    help="grid workloads: time each step as a replayed HIP graph (both RQ and BF16)")
+    p.add_argument("--contexts", default="",
+                   help="grid workloads: comma-separated context lengths to run (default: the workload's)")
+    p.add_argument("--batches", default="",
+                   help="grid workloads: comma-separated batches to run at each context (default: powers of "
+                        "two up to the largest that fits, and that largest)")
     p.add_argument("--mode", default="decode", choices=["decode", "copy", "split-sweep", "stream", "encode"],
                    help="copy: a plain 1 GiB device copy, the reference for HBM counter scaling; "
                         "split-sweep: every token-split count against the automatic one; "
@@ -969,11 +974,18 @@ def grid_bench(args, w, budget=250e9):
     steps = args.steps if args.steps_given else 8
     per_tok_rq = layout_bytes_per_token(L, w.bits, w.g, d, w.ref_bits, w.ref_group)
     rows = []
-    for n in w.extra["contexts"]:
+    contexts = [int(x) for x in args.contexts.split(",")] if args.contexts else w.extra["contexts"]
+    only = [int(x) for x in args.batches.split(",")] if args.batches else None
+    for n in contexts:
         rq_per_b = NL * H * (n * per_tok_rq + T * L * 2 * d * 2)
         bf_per_b = NL * H * (n + T) * L * 2 * d * 2
-        bmax_rq, bmax_bf = int(budget // rq_per_b), int(budget // bf_per_b)
-        sweep = lambda bm: [b for b in (1, 2, 4, 8, 16, 32, 64, 128, 256) if b < bm] + [bm]
+        fit_rq, fit_bf = int(budget // rq_per_b), int(budget // bf_per_b)
+        bmax_rq, bmax_bf = fit_rq, fit_bf
+        if only:           # allocate and run only the batches asked for
+            bmax_rq, bmax_bf = min(bmax_rq, max(only)), min(bmax_bf, max(only))
+            sweep = lambda bm: [b for b in only if b <= bm]
+        else:
+            sweep = lambda bm: [b for b in (1, 2, 4, 8, 16, 32, 64, 128, 256) if b < bm] + [bm]
         lay_max = rq.Layout(L, bmax_rq, H, d, w.g, n, w.rotate, w.bits, ref_bits=w.ref_bits,
                             ref_group=w.ref_group)
         layers = [(rq.Cache(lay_max, dev, zero=False), rq.Cache(lay_max, dev, zero=False)) for _ in range(NL)]
@@ -1039,8 +1051,8 @@ def grid_bench(args, w, budget=250e9):
                 bf_rows.append({"batch": B, "ms_per_step": round(ms, 3), "tokens_per_s": round(B / (ms / 1e3), 1)})
             del bl, views
             torch.cuda.empty_cache()
-        row = {"n_ctx": n, "max_batch": {"residualquant": bmax_rq, "bf16": bmax_bf},
-               "max_pow2_batch": {"residualquant": 2 ** int(np.log2(bmax_rq)), "bf16": 2 ** int(np.log2(bmax_bf))},
+        row = {"n_ctx": n, "max_batch": {"residualquant": fit_rq, "bf16": fit_bf},
+               "max_pow2_batch": {"residualquant": 2 ** int(np.log2(fit_rq)), "bf16": 2 ** int(np.log2(fit_bf))},
                "residualquant": rq_rows}
         if bf_rows:
             pr, pb = max(r["tokens_per_s"] for r in rq_rows), max(r["tokens_per_s"] for r in bf_rows)
@@ -1059,7 +1071,8 @@ def grid_bench(args, w, budget=250e9):
             "data": "synthetic",
             "config": {"workload": f"{w.name}: {NL} layers x ({H} heads, head_dim {d}, {L} loops, INT{w.ref_bits} "
                                    f"anchor g={w.ref_group}, residual bits {w.bits} g={w.g}, {T} BF16 tail tokens), "
-                                   f"contexts {w.extra['contexts']}",
+                                   f"contexts {contexts}"
+                                   + (f", batches {only} only" if only else ""),
                        "timing": "HIP graph replay" if args.graphs else "eager launches"},
             "grid": rows}
 
