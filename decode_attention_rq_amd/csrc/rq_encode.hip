@@ -348,12 +348,13 @@ __device__ __forceinline__ void quantize_loop(float (&u)[EPL], int bits, int gro
 // reconstruction becomes the next loop's reference.
 //
 // Everything that depends only on the wave is wave-uniform, so every plane
-// is a buffer at the wave's first token addressed by 32-bit lane offsets;
-// the next loop's input is loaded while the current loop is quantized.
-// About 140 VGPRs: three waves per SIMD (forcing four spills y and runs
-// slower).  CHAIN (chained references) is a template parameter: without it
-// y is fixed over the loops, and the loop carries no copies of it around
-// its back edge.
+// is a buffer at the wave's first token addressed by 32-bit lane offsets.
+// Each loop's input is loaded when the loop starts, with no prefetch of the
+// next loop's rows: that buffer cost 16 VGPRs, and without it the kernel
+// fits 128 (four waves per SIMD), whose other waves cover the load latency
+// (anchored prefill 4% faster, [4,2,2] prefill unchanged).  CHAIN (chained
+// references) is a template parameter: without it y is fixed over the
+// loops, and the loop carries no copies of it around its back edge.
 template <int D, bool CHAIN>
 __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   constexpr int LANES = D / EPL;
@@ -378,12 +379,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   const uint32_t rows = (uint32_t)nw * (2 * D);
   auto input = [&](int i) { return plane(S.xin[i] + xrow0 * D, rows); };
 
-  u32x4_t raw[EPL / 8];
   float y[EPL];
   {
     u32x4_t yr[EPL / 8];
     load_raw32(a.abits == 0 ? plane(S.ref + row0 * D, rows) : input(a.n_res), xoff, yr);
-    if (a.n_res > 0) load_raw32(input(0), xoff, raw);
     unpack_raw32(yr, y);
   }
   if (a.abits != 0) {
@@ -395,12 +394,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
 
   for (int l = 0; l < a.n_res; ++l) {
     float x[EPL];
-    unpack_raw32(raw, x);
-    // the next loop's rows; after the last loop a zero-length buffer (the
-    // loads return zeros and touch no memory), so that the prefetch buffer is
-    // written on every iteration and needs no register copies across the
-    // loop's back edge
-    load_raw32(plane(S.xin[min(l + 1, a.n_res - 1)] + xrow0 * D, l + 1 < a.n_res ? rows : 0u), xoff, raw);
+    {
+      u32x4_t raw[EPL / 8];
+      load_raw32(input(l), xoff, raw);
+      unpack_raw32(raw, x);
+    }
     float alpha32;
     if (a.alpha_mode == 1) {
       alpha32 = 1.0f;
