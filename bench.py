@@ -283,9 +283,10 @@ def copy_probe():
 
 def stream_probe(args):
     """The attainable HBM read rate: rq_probe_read_stream over a 4 GiB buffer
-    (16x the 256 MB Infinity Cache), grid-stride and chunked patterns,
-    default and non-temporal loads, 4 / 8 / 16 workgroups of 256 lanes per
-    compute unit.  One JSON line per point, then a summary line."""
+    (16x the 256 MB Infinity Cache), grid-stride, chunked and 20-plane
+    patterns, default and non-temporal loads, 2 / 4 / 8 / 16 workgroups of
+    256 lanes per compute unit.  One JSON line per point, then a summary
+    line."""
     import torch
     import decode_attention_rq_amd as rq
     nbytes = 4 << 30
@@ -293,13 +294,17 @@ def stream_probe(args):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     steps = args.steps if args.steps_given else 20
     best = {}
-    for pattern in (0, 1):
+    for pattern in (0, 1, 2):
         for nt in (0, 1):
-            for per_cu in (4, 8, 16):
-                sink = torch.empty(cus * per_cu * 256, dtype=torch.int32, device="cuda")
+            for per_cu in (2, 4, 8, 16):
+                blocks = cus * per_cu
+                sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
                 ms = timed(lambda i: rq.rq_probe_read_stream(buf, nt, sink, pattern), steps, 2)
-                gbs = nbytes / (ms / 1e3) / 1e9
-                row = {"mode": "stream", "pattern": ["grid-stride", "chunked"][pattern], "nontemporal": nt,
+                read = nbytes
+                if pattern == 2:     # whole 4 KiB segments of each of the 20 planes' chunks
+                    read = 20 * 4096 * (nbytes // 20 // 16 // blocks // 256) * blocks
+                gbs = read / (ms / 1e3) / 1e9
+                row = {"mode": "stream", "pattern": ["grid-stride", "chunked", "planes-20"][pattern], "nontemporal": nt,
                        "workgroups_per_cu": per_cu, "ms_per_read": round(ms, 4), "gbs": round(gbs, 1),
                        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
                 print(json.dumps(row), flush=True)

@@ -489,9 +489,10 @@ def workspace_for(layout: Layout, n_ctx: int, n_splits: int = 0, device="cuda") 
 
 def rq_probe_read_stream(buf: torch.Tensor, nontemporal: bool, sink: torch.Tensor, pattern: int = 0,
                          stream=None) -> None:
-    """Read all of buf once with 128-bit loads (include/rq_probe.h): pattern 0
-    grid stride, 1 one contiguous chunk per workgroup; sink is a device int32
-    tensor whose length (a multiple of 256) sets the number of workgroups."""
+    """Read buf once with 128-bit loads (include/rq_probe.h): pattern 0 grid
+    stride, 1 one contiguous chunk per workgroup, 2 a chunk of each of 20
+    planes per workgroup; sink is a device int32 tensor whose length (a
+    multiple of 256) sets the number of workgroups."""
     _tensor(buf, "buf", buf.dtype if isinstance(buf, torch.Tensor) else torch.uint8)
     _tensor(sink, "sink", torch.int32)
     if sink.numel() % 256 != 0:

@@ -26,7 +26,13 @@ extern "C" {
  *                (the policy the decode kernel uses for its streamed planes)
  *   pattern      0: grid stride (consecutive lanes of the whole grid read
  *                consecutive 16 bytes); 1: chunked (workgroup b reads the
- *                b-th of n_blocks contiguous chunks, 16 KiB per iteration)
+ *                b-th of n_blocks contiguous chunks, 16 KiB per iteration);
+ *                2: planes (the buffer cut into 20 equal planes, workgroup b
+ *                walking the b-th chunk of all of them at once, as a decode
+ *                workgroup walks every plane of its (batch, head); only the
+ *                whole 4 KiB segments of each chunk are read, so the bytes
+ *                read are 20 * 4096 * floor(bytes / 20 / 16 / n_blocks / 256)
+ *                * n_blocks)
  *   n_blocks     1 .. 65535 workgroups of 256 lanes
  *   sink         device uint32 [n_blocks * 256], 16-byte aligned; written
  * Returns RQ_ERR_INVALID_ARG for a null, misaligned or mis-sized argument,

@@ -365,7 +365,8 @@ def test_read_stream_probe_rejects_bad_arguments(rq):
     assert f(FAKE, 1000, 0, 0, 4, FAKE, None) == INVALID            # not a multiple of 16 bytes
     assert f(FAKE, 0, 0, 0, 4, FAKE, None) == INVALID               # empty
     assert f(FAKE, 1024, 2, 0, 4, FAKE, None) == INVALID            # bad policy flag
-    assert f(FAKE, 1024, 0, 2, 4, FAKE, None) == INVALID            # bad pattern
+    assert f(FAKE, 1024, 0, 3, 4, FAKE, None) == INVALID            # bad pattern
+    assert f(FAKE, 1024, 0, -1, 4, FAKE, None) == INVALID           # bad pattern
     assert f(FAKE, 1024, 0, 0, 0, FAKE, None) == INVALID            # no workgroups
     assert f(FAKE, 1024, 0, 1, 65536, FAKE, None) == INVALID        # too many
     assert f(FAKE, 1024, 0, 1, 4, None, None) == INVALID            # null sink
