@@ -68,7 +68,8 @@ def test_encode_chunked_appends(oracle):
 
 def test_encode_degenerate_vectors(oracle):
     """Zero reference (alpha = 0), exact multiples (zero residual, zero scale),
-    constant vectors, huge and tiny magnitudes (saturation, subnormal FP16)."""
+    constant vectors, huge and tiny magnitudes (saturation, subnormal FP16,
+    group ranges beyond 2^120, FP32-subnormal ranges)."""
     w = _w(bits=(2, 4), B=1, H=1)
     case = Case(w, 16, cap=16)
     import decode_attention_rq_amd as rq
@@ -84,6 +85,9 @@ def test_encode_degenerate_vectors(oracle):
     kin[:, :, :, 5] *= 1e6                                 # saturating scale/zero
     kin[:, :, :, 6] *= 1e-6                                # subnormal FP16 scales
     kref[..., 7, :] *= 1e-20                               # tiny reference: huge alpha, saturated
+    kin[:, :, :, 8] *= 1e36                                # group ranges past 2^120: the scale's quotient
+                                                           # is taken on a clamped range (still finite)
+    kin[:, :, :, 9] *= 1e-39                               # BF16 subnormal inputs: FP32-subnormal ranges
     kref, kin = kref.to(torch.bfloat16), kin.to(torch.bfloat16)
     case.data["k_ref"], case.data["k_loops"] = kref, kin
     case.data["v_ref"], case.data["v_loops"] = kref.clone(), kin.clone()
