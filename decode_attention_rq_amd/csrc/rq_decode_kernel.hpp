@@ -1,6 +1,7 @@
 // rq_decode_kernel.hpp -- fused decode attention over a ResidualQuant cache
-// (gfx950): the kernel template, included by the files that instantiate it
-// for a BF16 reference (rq_decode.hip) and for quantized anchors.
+// (gfx950): the kernel template, instantiated by rq_decode_inst.hip once per
+// (head_dim, reference kind, chain mode) and dispatched from rq_decode.hip,
+// which also holds the split merge (kernel M).
 //
 // ResidualQuant page ("ResidualQuant: KV Cache Quantization for Looped
 // Transformers with 2-Bit Residuals"), Abstract: decode reads each loop's

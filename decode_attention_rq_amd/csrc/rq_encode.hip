@@ -10,10 +10,12 @@
 //
 // Mapping: one head_dim vector per D/32 consecutive lanes, 32 consecutive dims
 // per lane, 64/(D/32) tokens per wave.  A wave handles all residual loops of
-// its tokens, so each reference vector is read once.  The
-// FP32 arithmetic is the library's bit-exact contract: the same IEEE
-// operations in the same order as the sequential definition, no contraction
-// (fp contract off below), explicit fma where the contract has one.
+// its tokens, so each reference vector is read once.  The FP32 arithmetic is
+// the library's bit-exact contract: the results of the sequential
+// definition's IEEE operations in its order, no contraction (fp contract off
+// below), explicit fma where the contract has one.  Two quotients (a group's
+// scale, its code factor) are formed without a divide instruction, by fma
+// identities that give the IEEE quotient's bits for every input they see.
 
 #pragma clang fp contract(off)
 
