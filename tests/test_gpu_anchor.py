@@ -254,19 +254,26 @@ def test_tail_of_zero_tokens_is_plain_decode():
     assert np.array_equal(a, out.cpu().double().numpy())
 
 
-@pytest.mark.parametrize("wname", ["anchor-8k-perloop", "chain-8k-perloop"])
+@pytest.mark.parametrize("wname", ["anchor-8k-perloop", "chain-8k-perloop", "grid-g16-2k-batch512"])
 def test_anchor_perloop_full_size(oracle, wname):
     """The per-loop workloads at full size (batch 16, 16 heads, 8192 cached
     tokens + 64 BF16 tail tokens, INT4 anchor g=32, INT2 residuals g=16; Last-
-    loop references, or Next-loop chains), in the launch configuration the
-    benchmark uses, on one whole batch row of heads and two corner pairs:
-    bytes of those pairs, then every loop's row, one loop per call."""
+    loop references, or Next-loop chains), and the decode grid's largest
+    launch (batch 512 at 2k context: the most the 250 GB budget holds, 8192
+    batch*heads), in the launch configuration the benchmark uses, on one whole
+    batch row of heads and two corner pairs: bytes of those pairs, then every
+    loop's row, one loop per call."""
+    import dataclasses
     import decode_attention_rq_amd as rq
-    w = synth.WORKLOADS[wname]
+    if wname == "grid-g16-2k-batch512":
+        w = dataclasses.replace(synth.WORKLOADS["grid-g16"], name=wname, batch=512, n_ctx=2048)
+    else:
+        w = synth.WORKLOADS[wname]
     T = w.extra["tail"]
     n = w.n_ctx
     case = Case(w, n, gen_device="cuda")
-    pairs = [(9, h) for h in range(w.heads)] + [(0, 0), (15, 15)]
+    mid = w.batch // 2 + 1
+    pairs = [(mid, h) for h in range(w.heads)] + [(0, 0), (w.batch - 1, w.heads - 1)]
     lay, kp, vp, qb = case.oracle_planes(oracle, pairs)
     for side, planes in (("k", kp), ("v", vp)):
         gc = getattr(case, side)
