@@ -128,16 +128,25 @@ def _tensor(t, name: str, dtype, shape=None, allow_none: bool = False) -> None:
         raise ValueError(f"{name}: must be a GPU tensor (device {t.device})")
 
 
-def _check_cache(layout: "Layout", c: "Cache", name: str) -> None:
+def _plane_key(t: torch.Tensor) -> tuple:
+    """What a checked plane's validity depends on: the tensor, its data
+    pointer and its version counter (which in-place changes of its shape or
+    strides, and in-place writes through torch, advance)."""
+    return (id(t), t.data_ptr(), t._version)
+
+
+def _check_cache(layout: "Layout", c: "Cache", name: str) -> "rq_cache":
     """Every plane of c present has the dtype and shape `layout` gives it.
     Checked once per (layout, planes) pair: the result is kept on the cache
-    object, keyed by the layout's fields and the identity and data pointer of
-    every plane (a plane replaced by another tensor is checked again)."""
-    key = (layout._key(), c._fingerprint())
-    if getattr(c, "_checked", None) == key:
-        return
-    _check_cache_planes(layout, c, name)
-    c._checked = key
+    object, keyed by the layout's fields and every plane's identity, data
+    pointer and version counter (a plane replaced, or resized or restrided in
+    place, is checked again).  Returns the cache's C struct."""
+    fp = c._fingerprint()
+    key = (layout._key(), fp)
+    if getattr(c, "_checked", None) != key:
+        _check_cache_planes(layout, c, name)
+        c._checked = key
+    return c.c(fp)
 
 
 def _check_cache_planes(layout: "Layout", c: "Cache", name: str) -> None:
@@ -266,13 +275,15 @@ class Cache:
                     self.alpha.append(new(B, H, cap, dtype=torch.float16, device=device))
 
     def _fingerprint(self) -> tuple:
-        """Identity and data pointer of every plane (absent planes: None)."""
-        return tuple(None if t is None else (id(t), t.data_ptr())
+        """_plane_key of every plane (absent planes: None): a plane replaced,
+        or resized or restrided in place, changes it."""
+        return tuple(None if t is None else _plane_key(t)
                      for t in [self.ref, *self.codes, *self.meta, *self.alpha])
 
-    def c(self) -> rq_cache:
-        """The C struct (rebuilt when a plane is replaced)."""
-        fp = self._fingerprint()
+    def c(self, fp: Optional[tuple] = None) -> rq_cache:
+        """The C struct (rebuilt when a plane is replaced); fp: this cache's
+        _fingerprint() if the caller has it."""
+        fp = fp if fp is not None else self._fingerprint()
         memo = self.__dict__.get("_c_memo")
         if memo is not None and memo[0] == fp:
             return memo[1]
@@ -318,13 +329,13 @@ def rq_encode(layout: Layout, k: Cache, v: Cache, k_in: torch.Tensor, v_in: torc
     """k_in / v_in: bf16 [L-1, B, H, n, d] contiguous, the loops other than
     the BF16 reference in loop order; with quantized anchors [L, B, H, n, d]
     (every loop, anchors included, in loop order)."""
-    _check_cache(layout, k, "k")
-    _check_cache(layout, v, "v")
+    kc = _check_cache(layout, k, "k")
+    vc = _check_cache(layout, v, "v")
     loops = layout.n_loops if layout.ref_bits else layout.n_loops - 1
     shape = (loops, layout.batch, layout.n_heads, int(n), layout.head_dim) if n > 0 else None
     _tensor(k_in, "k_in", torch.bfloat16, shape)
     _tensor(v_in, "v_in", torch.bfloat16, shape)
-    lay, kc, vc = layout.c(), k.c(), v.c()
+    lay = layout.c()
     _check(_lib.rq_encode(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(k_in), _ptr(v_in),
                           int(t0), int(n), _stream(stream)))
 
@@ -346,12 +357,12 @@ def rq_decode_attn(layout: Layout, k: Cache, v: Cache, q: torch.Tensor, loop_mas
                    sm_scale: float, out: torch.Tensor, workspace: torch.Tensor, n_splits: int = 0,
                    stream=None) -> None:
     """q: bf16 [L, B, H, d]; out: f32 [L, B, H, d]; workspace: device bytes."""
-    _check_cache(layout, k, "k")
-    _check_cache(layout, v, "v")
+    kc = _check_cache(layout, k, "k")
+    vc = _check_cache(layout, v, "v")
     _check_rows(layout, q, "q", torch.bfloat16)
     _check_rows(layout, out, "out", torch.float32)
     _check_workspace(workspace)
-    lay, kc, vc = layout.c(), k.c(), v.c()
+    lay = layout.c()
     _check(_lib.rq_decode_attn(C.byref(lay), C.byref(kc), C.byref(vc), _ptr(q), int(loop_mask),
                                int(n_ctx), float(sm_scale), int(n_splits), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -373,15 +384,18 @@ class Tail:
             raise ValueError(f"tail: n = {self.n} outside [0, capacity {self.capacity}]")
 
     def _fingerprint(self) -> tuple:
-        return (self.n, self.capacity) + tuple(None if t is None else (id(t), t.data_ptr())
+        return (self.n, self.capacity) + tuple(None if t is None else _plane_key(t)
                                                for t in [*self.k, *self.v])
 
-    def check(self, layout: "Layout") -> None:
-        key = (layout._key(), self._fingerprint())
-        if self.__dict__.get("_checked") == key:
-            return
-        self._check_planes(layout)
-        self.__dict__["_checked"] = key
+    def check(self, layout: "Layout") -> "rq_tail":
+        """Check the planes against `layout` (once per layout and set of
+        planes, as for a cache); returns the C struct."""
+        fp = self._fingerprint()
+        key = (layout._key(), fp)
+        if self.__dict__.get("_checked") != key:
+            self._check_planes(layout)
+            self.__dict__["_checked"] = key
+        return self.c(fp)
 
     def _check_planes(self, layout: "Layout") -> None:
         for side, planes in (("k", self.k), ("v", self.v)):
@@ -389,8 +403,8 @@ class Tail:
                 _tensor(t, f"tail.{side}[{l}]", torch.bfloat16,
                         (layout.batch, layout.n_heads, self.capacity, layout.head_dim), allow_none=True)
 
-    def c(self) -> rq_tail:
-        fp = self._fingerprint()
+    def c(self, fp: Optional[tuple] = None) -> rq_tail:
+        fp = fp if fp is not None else self._fingerprint()
         memo = self.__dict__.get("_c_memo")
         if memo is not None and memo[0] == fp:
             return memo[1]
@@ -409,15 +423,13 @@ def rq_decode_attn_tail(layout: Layout, k: Cache, v: Cache, tail: Optional[Tail]
                         loop_mask: int, n_ctx: int, sm_scale: float, out: torch.Tensor,
                         workspace: torch.Tensor, n_splits: int = 0, stream=None) -> None:
     """rq_decode_attn over n_ctx cached tokens followed by tail.n BF16 tokens."""
-    _check_cache(layout, k, "k")
-    _check_cache(layout, v, "v")
+    kc = _check_cache(layout, k, "k")
+    vc = _check_cache(layout, v, "v")
     _check_rows(layout, q, "q", torch.bfloat16)
     _check_rows(layout, out, "out", torch.float32)
     _check_workspace(workspace)
-    if tail is not None:
-        tail.check(layout)
-    lay, kc, vc = layout.c(), k.c(), v.c()
-    tc = tail.c() if tail is not None else None
+    tc = tail.check(layout) if tail is not None else None
+    lay = layout.c()
     _check(_lib.rq_decode_attn_tail(C.byref(lay), C.byref(kc), C.byref(vc),
                                     C.byref(tc) if tc is not None else None, _ptr(q),
                                     int(loop_mask), int(n_ctx), float(sm_scale), int(n_splits),
@@ -434,14 +446,12 @@ def rq_decode_attn_tail_noalloc(layout: Layout, k: Cache, v: Cache, tail: Option
     """rq_decode_attn_tail with the split records in the library's per-GPU
     scratch instead of a caller workspace: nothing is allocated.  Calls that
     may overlap on one GPU race on that scratch."""
-    _check_cache(layout, k, "k")
-    _check_cache(layout, v, "v")
+    kc = _check_cache(layout, k, "k")
+    vc = _check_cache(layout, v, "v")
     _check_rows(layout, q, "q", torch.bfloat16)
     _check_rows(layout, out, "out", torch.float32)
-    if tail is not None:
-        tail.check(layout)
-    lay, kc, vc = layout.c(), k.c(), v.c()
-    tc = tail.c() if tail is not None else None
+    tc = tail.check(layout) if tail is not None else None
+    lay = layout.c()
     _check(_lib.rq_decode_attn_tail_noalloc(C.byref(lay), C.byref(kc), C.byref(vc),
                                             C.byref(tc) if tc is not None else None, _ptr(q),
                                             int(loop_mask), int(n_ctx), float(sm_scale), int(n_splits),
@@ -472,9 +482,9 @@ def rq_bf16_decode_attn(layout: Layout, k_loops: Sequence[torch.Tensor], v_loops
 def rq_reconstruct(layout: Layout, c: Cache, loop: int, t0: int, n: int, out: torch.Tensor,
                    stream=None) -> None:
     """out: f32 [B, H, n, d]."""
-    _check_cache(layout, c, "c")
+    cc = _check_cache(layout, c, "c")
     _tensor(out, "out", torch.float32, (layout.batch, layout.n_heads, int(n), layout.head_dim))
-    lay, cc = layout.c(), c.c()
+    lay = layout.c()
     _check(_lib.rq_reconstruct(C.byref(lay), C.byref(cc), int(loop), int(t0), int(n), _ptr(out),
                                _stream(stream)))
 

@@ -106,6 +106,27 @@ def test_binding_rejects_mismatched_tensors(bad):
         rq.rq_decode_attn(lay, k, v, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)
 
 
+def test_binding_rechecks_planes_changed_in_place(monkeypatch):
+    """The argument checks are kept per cache and tail object; a plane resized
+    or restrided in place (same tensor, same data pointer) is checked again."""
+    lay = _lay()
+    k, v, q, out, ws = _decode_args(lay)
+    monkeypatch.setenv("RQ_FAULT_INJECT", "launch")        # valid calls stop after validation
+    with pytest.raises(rq.RQError):
+        rq.rq_decode_attn(lay, k, v, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)
+    k.meta[1].resize_(k.meta[1].shape[0], k.meta[1].shape[1], 8, *k.meta[1].shape[3:])
+    with pytest.raises(ValueError):
+        rq.rq_decode_attn(lay, k, v, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)
+    kt = [torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16) for _ in range(4)]
+    tail = rq.Tail(kt, [t.clone() for t in kt], 4)
+    k2, v2, _, _, _ = _decode_args(lay)
+    with pytest.raises(rq.RQError):
+        rq.rq_decode_attn_tail(lay, k2, v2, tail, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)
+    kt[2].as_strided_((1, 2, 8, 128), (2 * 8 * 128, 8 * 128, 64, 1))   # rows overlap: not contiguous
+    with pytest.raises(ValueError):
+        rq.rq_decode_attn_tail(lay, k2, v2, tail, q, 0b1111, 32, 0.1, out, ws, n_splits=1, stream=0)
+
+
 def test_binding_rejects_encode_inputs_of_another_shape():
     lay = _lay()
     k, v, x = _inputs(lay, 4)
